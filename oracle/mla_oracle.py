@@ -1,0 +1,243 @@
+"""CPU oracle for the VideoMLA latent-KV chunk step.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  It shares no code with the HIP path: no kernels, headers, helpers,
+tables or constants.  Everything is plain NumPy in float64 with no intermediate
+rounding; inputs are the exact values of what the GPU receives.
+
+Source: the VideoMLA paper ("VideoMLA: Low-Rank Latent KV Cache for Minute-Scale
+Autoregressive Video Diffusion").  Each function names the section and equation
+it writes out.  The oracle is the *unabsorbed* training-time definition (§3,
+App. D.2-D.4): per-head keys and values are reconstructed explicitly and a
+dense softmax is taken over the whole active window.  The absorbed form of
+App. E is kept here too, as an independent route used to pin the oracle.
+
+Readings taken where the paper is silent (same numbering as the design notes):
+  * RMSNorm: u / sqrt(mean(u^2) + eps) * g, applied to c^KV and c^Q (App. D.2);
+    the cache holds the normalised latent.
+  * RoPE pair split for d_rope/2 = P pairs: y and x get floor(P/3) pairs each,
+    t gets the rest -> (6,5,5) at P=16 (App. D.3).
+  * RoPE frequencies: axis group widths of a full-d_head split, D_y = D_x =
+    2*floor(d_head/6), D_t = d_head - 2*D_y; pair k of axis a rotates by
+    theta^(-2k/D_a) per unit position, k from 0 (the highest-frequency bands,
+    §3.2 and App. D.3); theta = 10000.
+  * Pair m is channels (2m, 2m+1) = (re, im), axis order t, y, x; the same
+    rotation e^{+i*angle} for queries and keys.
+  * Position of token n of latent frame f: (t, y, x) = (f, n // grid_w,
+    n % grid_w), tokens flattened frame-major then row-major (App. C.1, S=FHW).
+  * Keys are rotated at their absolute position when written; the whole valid
+    window (the chunk's own frames included) is attended with no mask.
+  * Ring buffer: latent frame f lives in slot f mod W (FIFO eviction of whole
+    frames, App. D.4).
+"""
+import numpy as np
+
+__all__ = [
+    "rope_pair_split", "rope_omegas", "rope3d", "rmsnorm", "token_positions",
+    "ring_slot", "window_frames", "ring_rows_for_window", "cache_entries",
+    "expected_ring", "query_parts", "reconstruct_kv", "attention_unabsorbed",
+    "attention_absorbed", "output_projection", "step", "cache_scalars_per_token",
+    "dense_scalars_per_token",
+]
+
+
+# ----------------------------------------------------------------- accounting
+def cache_scalars_per_token(d_c, d_rope):
+    """Scalars cached per token per layer: the latent plus the shared RoPE key
+    (§3.1 and App. E, Eq. 13)."""
+    return d_c + d_rope
+
+
+def dense_scalars_per_token(n_heads, d_head):
+    """Scalars a dense per-head KV cache holds per token per layer (App. E, Eq. 14)."""
+    return 2 * n_heads * d_head
+
+
+# ----------------------------------------------------------------- 3D-RoPE
+def rope_pair_split(d_rope):
+    """(t, y, x) complex pairs for a RoPE subspace of d_rope channels (App. D.3)."""
+    p = d_rope // 2
+    n_sp = p // 3
+    return (p - 2 * n_sp, n_sp, n_sp)
+
+
+def rope_omegas(d_head, pairs, theta=10000.0):
+    """Per-pair angular frequency and axis index.  For axis a the pairs take the
+    first (highest-frequency) bands of that axis's group (§3.2, App. D.3)."""
+    d_sp = 2 * (d_head // 6)
+    widths = (d_head - 2 * d_sp, d_sp, d_sp)
+    omegas, axes = [], []
+    for axis in range(3):
+        for k in range(pairs[axis]):
+            omegas.append(float(theta) ** (-2.0 * k / widths[axis]))
+            axes.append(axis)
+    return np.array(omegas, dtype=np.float64), np.array(axes, dtype=np.int64)
+
+
+def rope3d(v, pos, omegas, axes):
+    """Rotate the RoPE subspace (§3.2 Eq. 5-6).  v: (..., 2P); pos: (..., 3)
+    integer (t, y, x) broadcastable against v's leading dims."""
+    v = np.asarray(v, dtype=np.float64)
+    z = v[..., 0::2] + 1j * v[..., 1::2]
+    angle = np.asarray(pos, dtype=np.float64)[..., axes] * omegas
+    z = z * np.exp(1j * angle)
+    out = np.empty_like(v)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+def rmsnorm(u, g, eps):
+    """RMSNorm applied to c^KV and c^Q before their up-projections (App. D.2)."""
+    u = np.asarray(u, dtype=np.float64)
+    return u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps) * g
+
+
+def token_positions(frames, grid_h, grid_w):
+    """(t, y, x) for every token of the given latent frames, frame-major then
+    row-major (App. C.1: S = F*H*W)."""
+    pos = []
+    for f in frames:
+        for n in range(grid_h * grid_w):
+            pos.append((f, n // grid_w, n % grid_w))
+    return np.array(pos, dtype=np.int64).reshape(-1, 3)
+
+
+# ----------------------------------------------------------------- ring bookkeeping
+def ring_slot(frame, window_frames):
+    """Ring slot of an absolute latent frame: FIFO over whole frames (App. D.4)."""
+    return frame % window_frames
+
+
+def window_frames(t0, chunk_frames, n_valid_frames):
+    """Chronological list of frames attended once the chunk [t0, t0+C) is written."""
+    last = t0 + chunk_frames - 1
+    return list(range(last - n_valid_frames + 1, last + 1))
+
+
+def ring_rows_for_window(t0, chunk_frames, n_valid_frames, window_frames_, tpf):
+    """Ring rows holding the window, in chronological token order."""
+    rows = []
+    for f in window_frames(t0, chunk_frames, n_valid_frames):
+        base = ring_slot(f, window_frames_) * tpf
+        rows.extend(range(base, base + tpf))
+    return np.array(rows, dtype=np.int64)
+
+
+# ----------------------------------------------------------------- the layer
+def _head_rows(w, h, width):
+    return w[h * width:(h + 1) * width]
+
+
+def cache_entries(s, w, x, frames):
+    """Per-token cache state (c^KV, k^R) for tokens x of the given frames.
+    c = RMSNorm(W_down^KV x) (§3.1 Eq. 1, App. D.2); k^R = W_R^K x (§3.2 Eq. 5);
+    the rotated key k^rope = RoPE3D(k^R) at the token's absolute position.
+    x: (N, d).  Returns (c (N, d_c), k_r_raw (N, d_rope), k_rope (N, d_rope))."""
+    x = np.asarray(x, dtype=np.float64)
+    c = rmsnorm(x @ w["w_kv_down"].T, w["g_kv"], s.rms_eps)
+    k_r = x @ w["w_kr"].T
+    om, ax = rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
+    pos = token_positions(frames, s.grid_h, s.grid_w)
+    return c, k_r, rope3d(k_r, pos, om, ax)
+
+
+def expected_ring(s, w, x, frames, ring=None):
+    """Ring contents after writing the tokens x of the given frames.  Row
+    (f mod W)*tpf + n holds [c^KV | RoPE3D(k^R)] (keys rotated at write)."""
+    tpf = s.tokens_per_frame
+    if ring is None:
+        ring = np.zeros((s.window_frames * tpf, s.d_c + s.d_rope))
+    c, _, k_rope = cache_entries(s, w, x, frames)
+    for i, f in enumerate(frames):
+        base = ring_slot(f, s.window_frames) * tpf
+        ring[base:base + tpf, :s.d_c] = c[i * tpf:(i + 1) * tpf]
+        ring[base:base + tpf, s.d_c:] = k_rope[i * tpf:(i + 1) * tpf]
+    return ring
+
+
+def query_parts(s, w, x, frames):
+    """Per-head queries (§3.1 Eq. 3-4, §3.2 Eq. 6): c^Q = RMSNorm(W_down^Q x),
+    q^nope_h = W_up,h^Q c^Q, q^rope_h = RoPE3D(W_R,h^Q c^Q).
+    Returns (c_q (N, d_q), q_nope (N, H, d_nope), q_rope (N, H, d_rope))."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    c_q = rmsnorm(x @ w["w_q_down"].T, w["g_q"], s.rms_eps)
+    q_nope = (c_q @ w["w_q_up"].T).reshape(n, s.n_heads, s.d_nope)
+    q_r = (c_q @ w["w_qr"].T).reshape(n, s.n_heads, s.d_rope)
+    om, ax = rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
+    pos = token_positions(frames, s.grid_h, s.grid_w)[:, None, :]
+    return c_q, q_nope, rope3d(q_r, pos, om, ax)
+
+
+def reconstruct_kv(s, w, c):
+    """Per-head content keys and values from the cached latent (§3.1 Eq. 2):
+    k^nope_{j,h} = W_up,h^K c_j, v_{j,h} = W_up,h^V c_j."""
+    n = c.shape[0]
+    k_nope = (c @ w["w_k_up"].T).reshape(n, s.n_heads, s.d_nope)
+    v = (c @ w["w_v_up"].T).reshape(n, s.n_heads, s.d_head)
+    return k_nope, v
+
+
+def attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope, block=1024):
+    """Chunk attention as defined in §3.3 Eq. 7: per head, score =
+    (q^nope.k^nope + q^rope.k^rope) / sqrt(d_nope + d_rope) over every window
+    token, softmax over the window, weighted sum of v_{j,h}; heads concatenated.
+    q_nope (N, H, d_nope), q_rope (N, H, d_rope), c (M, d_c), k_rope (M, d_rope).
+    Returns out (N, H*d_head)."""
+    k_nope, v = reconstruct_kv(s, w, c)
+    n = q_nope.shape[0]
+    scale = 1.0 / np.sqrt(s.d_nope + s.d_rope)
+    out = np.empty((n, s.n_heads, s.d_head))
+    for h in range(s.n_heads):
+        kn = k_nope[:, h, :]
+        vh = v[:, h, :]
+        for i0 in range(0, n, block):
+            i1 = min(n, i0 + block)
+            sc = (q_nope[i0:i1, h, :] @ kn.T + q_rope[i0:i1, h, :] @ k_rope.T) * scale
+            sc = sc - sc.max(axis=1, keepdims=True)
+            a = np.exp(sc)
+            a /= a.sum(axis=1, keepdims=True)
+            out[i0:i1, h, :] = a @ vh
+    return out.reshape(n, s.n_heads * s.d_head)
+
+
+def output_projection(w, out):
+    """Heads mixed by the output projection W_O (§3.3)."""
+    return out @ w["w_o"].T
+
+
+def attention_absorbed(s, w, c_q, q_rope, c, k_rope):
+    """The inference reparameterisation of App. E, written as the paper states it:
+    content score (c^Q)^T A_h c^KV with A_h = (W_up,h^Q)^T W_up,h^K (Eq. 8-9), the
+    RoPE term kept separate (Eq. 12), and the output sum_h B_h sum_j a_j c_j with
+    B_h = W_O,h W_up,h^V (Eq. 10-11).  Returns y (N, d)."""
+    n = c_q.shape[0]
+    scale = 1.0 / np.sqrt(s.d_nope + s.d_rope)
+    y = np.zeros((n, s.d_model))
+    for h in range(s.n_heads):
+        a_h = _head_rows(w["w_q_up"], h, s.d_nope).T @ _head_rows(w["w_k_up"], h, s.d_nope)
+        b_h = w["w_o"][:, h * s.d_head:(h + 1) * s.d_head] @ _head_rows(w["w_v_up"], h, s.d_head)
+        sc = (c_q @ a_h @ c.T + q_rope[:, h, :] @ k_rope.T) * scale
+        sc = sc - sc.max(axis=1, keepdims=True)
+        a = np.exp(sc)
+        a /= a.sum(axis=1, keepdims=True)
+        y += (a @ c) @ b_h.T
+    return y
+
+
+def step(s, w, x_window, window_ids, chunk_ids, query_rows=None):
+    """One chunk step for one batch element: cache entries for every window frame,
+    queries for the chunk, attention, and W_O.  x_window holds the tokens of
+    window_ids (chronological); the chunk frames are the last ones.  query_rows
+    optionally restricts the queries to a subset of chunk tokens (indices into
+    the chunk).  Returns dict(out=(Nq, H*d_h), y=(Nq, d), c, k_rope)."""
+    tpf = s.tokens_per_frame
+    c, _, k_rope = cache_entries(s, w, x_window, window_ids)
+    first = window_ids.index(chunk_ids[0])
+    x_chunk = np.asarray(x_window[first * tpf:(first + len(chunk_ids)) * tpf], dtype=np.float64)
+    _, q_nope, q_rope = query_parts(s, w, x_chunk, chunk_ids)
+    if query_rows is not None:
+        q_nope, q_rope = q_nope[query_rows], q_rope[query_rows]
+    out = attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope)
+    return {"out": out, "y": output_projection(w, out), "c": c, "k_rope": k_rope}

@@ -1,0 +1,12 @@
+"""Seeded synthetic workloads for the VideoMLA latent-KV chunk step.
+
+This module only draws random numbers and describes shapes; it holds none of
+the method's arithmetic.  Both the HIP path (through the Python binding) and
+the CPU oracle receive exactly the arrays produced here.
+"""
+from .shapes import MLAShape, SHAPES, shape_by_name
+from .gen import (draw_weights, draw_frames, round_to_bf16_bits, bf16_bits_to_f32,
+                  WEIGHT_NAMES)
+
+__all__ = ["MLAShape", "SHAPES", "shape_by_name", "draw_weights", "draw_frames",
+           "round_to_bf16_bits", "bf16_bits_to_f32", "WEIGHT_NAMES"]

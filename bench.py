@@ -1,0 +1,246 @@
+"""Benchmark of the VideoMLA latent-KV chunk step on one MI355X.
+
+A step is one mla_step call: cache write of the 3-frame chunk into the 21-frame
+ring, query preparation, latent chunk attention over the whole window, value
+up-projection and W_O, on the Wan-1.3B layer shape (bf16 storage, fp32
+accumulation), inputs resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def step_flops(s):
+    """Algorithmic FLOP of one chunk step (each projection counted once, attention
+    as one (d_c+d_rope)-wide score plus one d_c-wide latent value per (query, key,
+    head))."""
+    tq, tw, nh = s.chunk_tokens, s.window_tokens, s.n_heads
+    write = 2 * tq * s.d_model * (s.d_c + s.d_rope)
+    qprep = (2 * tq * s.d_model * s.d_q + 2 * tq * s.d_q * nh * (s.d_nope + s.d_rope)
+             + 2 * tq * nh * s.d_nope * s.d_c)
+    attn = attention_flops(s)
+    vup = 2 * tq * nh * s.d_c * s.d_head
+    out = 2 * tq * nh * s.d_head * s.d_model
+    return {"write": write, "qprep": qprep, "attention": attn, "vup": vup, "out": out,
+            "total": write + qprep + attn + vup + out}
+
+
+def attention_flops(s):
+    return 2 * s.chunk_tokens * s.n_heads * s.window_tokens * (2 * s.d_c + s.d_rope)
+
+
+def cache_write_bytes(s):
+    """Algorithmic HBM bytes of one cache write: read x and the two weights once,
+    write the new ring rows."""
+    tq = s.chunk_tokens
+    return 2 * (tq * s.d_model + (s.d_c + s.d_rope) * s.d_model + tq * (s.d_c + s.d_rope))
+
+
+class Hip:
+    """hipEvent helpers from the HIP runtime (the library records into them)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        assert self.lib.hipEventSynchronize(b) == 0
+        t = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return t.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_src, units):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on the
+    current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "latent_attention_wan1.3b_w21_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha256_16") != source_hash(kernel_src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(s, w_exact, x_window, n_tokens):
+    """The oracle (fp64 NumPy, unabsorbed) on a bounded sample: n_tokens evenly
+    spaced query tokens of the chunk, all heads, the full window (cache entries and
+    K/V reconstruction for every window token)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    rows = np.linspace(0, s.chunk_tokens - 1, n_tokens).round().astype(int)
+    t0 = time.perf_counter()
+    O.step(s, w_exact, x_window, s.window_frame_ids, s.chunk_frame_ids, query_rows=rows)
+    dt = time.perf_counter() - t0
+    flops = step_flops(s)["total"] * n_tokens / s.chunk_tokens
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_tokens} of {s.chunk_tokens} query tokens (all {s.n_heads} heads) over "
+                      f"the full {s.window_tokens}-token window, fp64 NumPy; "
+                      f"{dt:.1f} s wall; credited {flops / 1e12:.4f} TFLOP pro rata"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan1.3b-w21")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2340)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a measured run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workload as W
+    import latent_kv_attention_down_amd as mla
+    from latent_kv_attention_down_amd.layer import DeviceLayer
+
+    s = W.shape_by_name(args.workload)
+    print(f"[bench] workload {s.name}: {s.chunk_tokens} query tokens x {s.n_heads} heads over "
+          f"{s.window_tokens} keys", file=sys.stderr, flush=True)
+    stored, w_exact = W.draw_weights(s)
+    ids = s.window_frame_ids
+    xs, xe = W.draw_frames(s, ids)
+    L = DeviceLayer(s, stored)
+    tpf = s.tokens_per_frame
+    for i, f in enumerate(ids):
+        if f >= s.t0:
+            break
+        L.cache_write(L.chunk(1, f, 1), L.tokens(xs[:, i * tpf:(i + 1) * tpf]))
+    chunk = L.chunk(s.chunk_frames, s.t0, s.n_valid_frames)
+    x = L.tokens(xs[:, -s.chunk_frames * tpf:])
+    y = L.new_out(chunk, s.d_model)
+    ws = L.workspace(chunk)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+
+    def one_step():
+        mla.step(L.cfg, L.weights, chunk, x, L.cache, y, ws, stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(hip.event(), hip.event()) for _ in range(K)]
+    t_start, t_stop = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(t_start, stream)
+    for i in range(K):
+        mla.set_timing_events(ev[i][0], ev[i][1])
+        one_step()
+    hip.record(t_stop, stream)
+    mla.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    ms_total = hip.ms(t_start, t_stop)
+    ms_step = ms_total / K
+    attn_ms = [hip.ms(a, b) for a, b in ev]
+    attn_avg = sum(attn_ms) / K
+    assert torch.isfinite(y.float()).all(), "non-finite output"
+
+    # cache write on its own: back-to-back launches between one pair of events
+    wr_ch = L.chunk(s.chunk_frames, s.t0, s.n_valid_frames)
+    for _ in range(3):
+        mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
+    torch.cuda.synchronize()
+    nw = max(K, 20)
+    hip.record(t_start, stream)
+    for _ in range(nw):
+        mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
+    hip.record(t_stop, stream)
+    torch.cuda.synchronize()
+    write_ms = hip.ms(t_start, t_stop) / nw
+
+    fl = step_flops(s)
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
+    attn_tflops = fl["attention"] / (attn_avg * 1e-3) / 1e12
+    wbytes = cache_write_bytes(s)
+    write_gbs = wbytes / (write_ms * 1e-3) / 1e9
+    kernel_src = os.path.join(ROOT, "latent_kv_attention_down_amd", "csrc", "attention.hip")
+    traffic = traffic_from_profiles(kernel_src, 1)
+
+    line = {
+        "metric": "MLA chunk-attention TFLOP/s + cache GB/s, Wan-1.3B shape, 21-frame window",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights; no trained model)",
+        "config": {"workload": s.name, "batch": 1, "query_tokens": s.chunk_tokens,
+                   "window_tokens": s.window_tokens, "chunk_frames": s.chunk_frames,
+                   "window_frames": s.window_frames, "heads": s.n_heads, "d_c": s.d_c,
+                   "d_rope": s.d_rope, "d_model": s.d_model, "grid": [s.grid_h, s.grid_w],
+                   "step_tflop": round(fl["total"] / 1e12, 4)},
+        "chunk_attention_tflops": round(attn_tflops, 2),
+        "cache_write_gbs": round(write_gbs, 1),
+        "cache_write_us": round(write_ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_latent_attn (latent attention, fast path)",
+                     "kernel_ms": round(attn_avg, 4)},
+        "cache_write_roofline": {"bound": "hbm", "achieved": round(write_gbs, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(write_gbs / HBM_PEAK_GBS, 4),
+                                 "bytes_per_launch": wbytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(s, w_exact, xe[0], args.cpu_tokens)
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

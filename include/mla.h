@@ -1,0 +1,189 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) VideoMLA latent-KV chunk step.
+ *
+ * The operation is the per-layer attention of the VideoMLA paper ("VideoMLA:
+ * Low-Rank Latent KV Cache for Minute-Scale Autoregressive Video Diffusion"):
+ *   - each new token x writes a content latent c^KV = RMSNorm(W^KV_down x)
+ *     (§3.1 Eq. 1, App. D.2) and a head-shared positional key
+ *     k^R = W^K_R x rotated by 3D-RoPE (§3.2 Eq. 5) into a ring-buffer cache
+ *     of whole latent frames with FIFO eviction (App. D.4);
+ *   - the query chunk attends over the valid window with per-head scores
+ *     q^nope.k^nope + q^rope.k^rope scaled by 1/sqrt(d_nope + d_rope)
+ *     (§3.3 Eq. 7), evaluated in the absorbed latent form of App. E
+ *     (Eq. 8-9 and 12), softmax over the window, value sum accumulated in
+ *     latent space and up-projected per head through W^V_up (Eq. 2);
+ *   - heads are mixed by W_O (§3.3).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
+ *     The caller owns all memory; the library allocates nothing and keeps no
+ *     state between calls except the thread-local error string and timing
+ *     hook below.
+ *   - Element type of x, weights, gains, cache, out_heads and y is cfg->dtype:
+ *     MLA_BF16 (bfloat16 storage, fp32 accumulation) or MLA_F32.
+ *   - Matrices are row-major [out][in] (y = W x is y_i = sum_k W[i][k] x_k).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Arguments are validated on the host first: an invalid argument
+ *     returns a negative status before anything is launched.  A failed launch
+ *     returns MLA_ERR_HIP and mla_last_error() gives the HIP message.  Device
+ *     faults surface at the caller's next synchronisation.  No C++ exception
+ *     crosses this boundary.
+ *   - Two calls that write the same cache must not run concurrently.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* a null pointer, a bad dimension or window      */
+  MLA_ERR_UNSUPPORTED = -2, /* valid, but not built for this shape and dtype  */
+  MLA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned               */
+  MLA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required     */
+  MLA_ERR_HIP = -5          /* the HIP runtime refused a launch               */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* Layer shape, token grid and ring geometry (VideoMLA Table 4, App. D.1-D.3). */
+typedef struct {
+  int32_t d_model;       /* d: model width (1536)                                  */
+  int32_t n_heads;       /* n_h (12)                                               */
+  int32_t d_head;        /* d_h = d_nope + d_rope (128); value width per head      */
+  int32_t d_nope;        /* NoPE query/key width per head (96)                     */
+  int32_t d_rope;        /* RoPE width, shared key and per-head query (32), even   */
+  int32_t d_c;           /* KV latent width (192)                                  */
+  int32_t d_q;           /* query latent width (768)                               */
+  int32_t rope_pairs[3]; /* complex pairs on the t, y, x axes; sum = d_rope / 2    */
+  float rope_theta;      /* frequency base; pair k of axis a turns by              */
+                         /* theta^(-2k/D_a) per position, D_y = D_x = 2*(d_head/6),*/
+                         /* D_t = d_head - 2*D_y (highest bands first, §3.2)       */
+  int32_t grid_h;        /* latent tokens per frame = grid_h * grid_w (30 x 52)    */
+  int32_t grid_w;
+  int32_t window_frames; /* W: ring capacity in latent frames (21)                 */
+  int32_t dtype;         /* mla_dtype                                              */
+  float rms_eps;         /* RMSNorm epsilon (1e-6)                                 */
+} mla_config;
+
+/* Weights, element type cfg->dtype, row-major [out][in] (App. D.2 shapes).      */
+typedef struct {
+  const void *w_kv_down; /* W^KV_down  d_c x d              (Eq. 1)                */
+  const void *w_kr;      /* W^K_R      d_rope x d           (Eq. 5)                */
+  const void *g_kv;      /* RMSNorm gain of c^KV, d_c; NULL = ones                 */
+  const void *w_q_down;  /* W^Q_down   d_q x d              (Eq. 3)                */
+  const void *g_q;       /* RMSNorm gain of c^Q, d_q; NULL = ones                  */
+  const void *w_q_up;    /* W^Q_up     (n_h*d_nope) x d_q, head h = rows h*d_nope..*/
+  const void *w_qr;      /* W^Q_R      (n_h*d_rope) x d_q   (Eq. 6)                */
+  const void *w_k_up;    /* W^K_up     (n_h*d_nope) x d_c   (Eq. 2)                */
+  const void *w_v_up;    /* W^V_up     (n_h*d_head) x d_c   (Eq. 2)                */
+  const void *w_o;       /* W_O        d x (n_h*d_head)                            */
+} mla_weights;
+
+/* The chunk being generated and the window it sees.                             */
+typedef struct {
+  int32_t batch;          /* B >= 1 independent requests (separate caches)        */
+  int32_t chunk_frames;   /* C: latent frames in the query chunk (3)              */
+  int64_t t0;             /* absolute index of the chunk's first latent frame     */
+  int32_t n_valid_frames; /* frames attended after the chunk is written: the      */
+                          /* frames t0+C-n_valid .. t0+C-1, C <= n_valid <= W     */
+} mla_chunk;
+
+/*
+ * Cache layout (every entry point that takes `cache`): a ring of W latent-frame
+ * slots per request, contiguous, shape (B, W * grid_h * grid_w, d_c + d_rope),
+ * element type cfg->dtype.  Latent frame f occupies slot f mod W; token n of
+ * the frame (row-major over the grid) is row (f mod W) * grid_h * grid_w + n,
+ * holding [ c^KV (d_c) | RoPE3D(k^R) (d_rope) ] with k^R rotated at the
+ * token's absolute position (t, y, x) = (f, n / grid_w, n % grid_w).
+ * Only the d_c + d_rope scalars per token are stored (App. E, Eq. 13).
+ */
+
+/* Host-only checks of cfg and chunk (no HIP call).  MLA_OK, INVALID_ARG or
+ * UNSUPPORTED.  UNSUPPORTED: the bf16 path needs d_model, d_q, d_c, d_nope and
+ * n_heads*d_head divisible by 32, d_rope divisible by 16 and (d_c, d_rope) one
+ * of (128,32), (192,32), (256,32), (192,64); the fp32 path has no such limits. */
+int mla_validate(const mla_config *cfg, const mla_chunk *chunk);
+
+/* Bytes of device workspace mla_chunk_attention / mla_step need for this
+ * problem; 0 if cfg/chunk are invalid.  Host-only. */
+size_t mla_workspace_bytes(const mla_config *cfg, const mla_chunk *chunk);
+
+/* Bytes of the ring cache for `batch` requests: batch * W * tokens_per_frame *
+ * (d_c + d_rope) * element size.  0 if cfg is invalid.  Host-only. */
+size_t mla_cache_bytes(const mla_config *cfg, int32_t batch);
+
+/*
+ * Cache write (§3.1 Eq. 1, App. D.2 RMSNorm, §3.2 Eq. 5, App. D.4 FIFO).
+ *   x     (B, C * grid_h * grid_w, d) tokens of frames t0 .. t0+C-1, in order.
+ *   cache ring described above; rows of slots (t0 .. t0+C-1) mod W are
+ *         overwritten, evicting the frames that held them; nothing else is
+ *         touched.
+ * One fused kernel: [W^KV_down; W^K_R] x, RMSNorm of the latent, rotation of
+ * k^R, rounding to cfg->dtype and the ring store.
+ */
+int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+                    const void *x, void *cache, void *stream);
+
+/*
+ * Chunk attention (§3.3 Eq. 7 in the absorbed form of App. E Eq. 8-12).
+ *   x         (B, C * tpf, d) the chunk's tokens (queries); frames t0 ..
+ *   cache     ring holding the n_valid_frames window, the chunk's own frames
+ *             included (write them first with mla_cache_write); read only.
+ *   out_heads (B, C * tpf, n_h * d_head): head outputs o_h = W^V_up,h sum_j a_j c_j,
+ *             concatenated over heads (before W_O).
+ *   workspace device scratch of at least mla_workspace_bytes(cfg, chunk).
+ * Every query attends to every valid cached token (no mask inside the window).
+ */
+int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+                        const void *x, const void *cache, void *out_heads,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One layer's chunk step: mla_cache_write, then mla_chunk_attention, then the
+ * output projection y = W_O out_heads (§3.3).
+ *   y  (B, C * tpf, d).
+ */
+int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+             const void *x, void *cache, void *y, void *workspace, size_t ws_bytes,
+             void *stream);
+
+/*
+ * The latent attention loop on its own (App. E Eq. 8, 12 and 16): the inner call
+ * of mla_chunk_attention, exposed so it can be timed and checked in isolation.
+ *   q_lat  (B, C*tpf*n_h, d_c + d_rope) cfg->dtype; row (token*n_h + h) holds
+ *          [ (W^K_up,h)^T q^nope_h | RoPE3D(q^R_h) ] multiplied by
+ *          log2(e) / sqrt(d_nope + d_rope).
+ *   cache  the ring, as above (read only).
+ *   o_lat  (B, C*tpf*n_h, d_c) cfg->dtype: sum_j a_j c_j with a the softmax over
+ *          the window of the scores q_lat . [c_j | k_rope_j] (base-2 logits).
+ *   workspace  at least mla_workspace_bytes(cfg, chunk) bytes.
+ */
+int mla_latent_attention(const mla_config *cfg, const mla_chunk *chunk, const void *q_lat,
+                         const void *cache, void *o_lat, void *workspace, size_t ws_bytes,
+                         void *stream);
+
+/* Measurement hook: when both are non-NULL, later calls on this thread record
+ * the hipEvent_t `ev_start` just before and `ev_stop` just after the launch of
+ * the latent-attention kernel (not its split merge), on the call's stream.
+ * Pass NULLs to clear. */
+void mla_set_timing_events(void *ev_start, void *ev_stop);
+
+/* Number of workgroups the latent-attention kernel launches for this problem
+ * (one persistent workgroup per compute unit, capped by the work); host-only
+ * apart from one device-attribute query. */
+int mla_attention_grid(const mla_config *cfg, const mla_chunk *chunk);
+
+const char *mla_status_string(int status);
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char *mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

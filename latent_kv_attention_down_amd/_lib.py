@@ -1,0 +1,178 @@
+"""ctypes binding of libmla.so (include/mla.h): argument marshalling only.
+
+Every entry point of the C ABI has a Python function of the same name (without
+the ``mla_`` prefix).  Tensors are torch device tensors; their data pointers and
+torch's current HIP stream are handed to the library, which does all the work.
+Loading fails loudly when the library has not been built.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED = 0, -1, -2
+MLA_ERR_ALIGNMENT, MLA_ERR_WORKSPACE, MLA_ERR_HIP = -3, -4, -5
+MLA_BF16, MLA_F32 = 0, 1
+
+# Every function include/mla.h declares, with (restype, argtypes).
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("d_model", _i32), ("n_heads", _i32), ("d_head", _i32), ("d_nope", _i32),
+                ("d_rope", _i32), ("d_c", _i32), ("d_q", _i32), ("rope_pairs", _i32 * 3),
+                ("rope_theta", ctypes.c_float), ("grid_h", _i32), ("grid_w", _i32),
+                ("window_frames", _i32), ("dtype", _i32), ("rms_eps", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_kv_down", "w_kr", "g_kv", "w_q_down", "g_q", "w_q_up",
+                                   "w_qr", "w_k_up", "w_v_up", "w_o")]
+
+
+class Chunk(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("chunk_frames", _i32), ("t0", _i64), ("n_valid_frames", _i32)]
+
+
+_P = ctypes.POINTER
+SIGNATURES = {
+    "mla_validate": (ctypes.c_int, [_P(Config), _P(Chunk)]),
+    "mla_workspace_bytes": (_sz, [_P(Config), _P(Chunk)]),
+    "mla_cache_bytes": (_sz, [_P(Config), _i32]),
+    "mla_cache_write": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _vp, _vp]),
+    "mla_chunk_attention": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _vp, _vp,
+                                           _vp, _sz, _vp]),
+    "mla_step": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_latent_attention": (ctypes.c_int, [_P(Config), _P(Chunk), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_set_timing_events": (None, [_vp, _vp]),
+    "mla_attention_grid": (ctypes.c_int, [_P(Config), _P(Chunk)]),
+    "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load libmla.so once; raise if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m latent_kv_attention_down_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status, where):
+        lib = load()
+        super().__init__(f"{where}: {lib.mla_status_string(status).decode()} "
+                         f"({lib.mla_last_error().decode()})")
+        self.status = status
+
+
+def _check(status, where):
+    if status != MLA_OK:
+        raise MLAError(status, where)
+
+
+def make_config(shape, dtype=None):
+    """Build an mla_config from any object with the shape fields (d_model, n_heads,
+    d_head, d_nope, d_rope, d_c, d_q, rope_pairs, rope_theta, grid_h, grid_w,
+    window_frames, dtype ('bf16'/'f32'), rms_eps)."""
+    dt = shape.dtype if dtype is None else dtype
+    c = Config()
+    for f in ("d_model", "n_heads", "d_head", "d_nope", "d_rope", "d_c", "d_q", "grid_h",
+              "grid_w", "window_frames"):
+        setattr(c, f, int(getattr(shape, f)))
+    for i, v in enumerate(shape.rope_pairs):
+        c.rope_pairs[i] = int(v)
+    c.rope_theta = float(shape.rope_theta)
+    c.rms_eps = float(shape.rms_eps)
+    c.dtype = MLA_BF16 if dt == "bf16" else MLA_F32
+    return c
+
+
+def make_chunk(batch, chunk_frames, t0, n_valid_frames):
+    return Chunk(int(batch), int(chunk_frames), int(t0), int(n_valid_frames))
+
+
+def make_weights(tensors):
+    """tensors: dict name -> device tensor (or None) for the mla_weights fields."""
+    w = Weights()
+    for name, _ in Weights._fields_:
+        t = tensors.get(name)
+        setattr(w, name, None if t is None else t.data_ptr())
+    return w
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def validate(cfg, chunk):
+    return load().mla_validate(ctypes.byref(cfg), ctypes.byref(chunk))
+
+
+def workspace_bytes(cfg, chunk):
+    return load().mla_workspace_bytes(ctypes.byref(cfg), ctypes.byref(chunk))
+
+
+def cache_bytes(cfg, batch):
+    return load().mla_cache_bytes(ctypes.byref(cfg), int(batch))
+
+
+def cache_write(cfg, weights, chunk, x, cache, stream=None):
+    _check(load().mla_cache_write(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(chunk),
+                                  _ptr(x), _ptr(cache), _stream(stream)), "mla_cache_write")
+
+
+def chunk_attention(cfg, weights, chunk, x, cache, out_heads, workspace, stream=None):
+    _check(load().mla_chunk_attention(ctypes.byref(cfg), ctypes.byref(weights),
+                                      ctypes.byref(chunk), _ptr(x), _ptr(cache), _ptr(out_heads),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "mla_chunk_attention")
+
+
+def step(cfg, weights, chunk, x, cache, y, workspace, stream=None):
+    _check(load().mla_step(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(chunk), _ptr(x),
+                           _ptr(cache), _ptr(y), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)),
+           "mla_step")
+
+
+def latent_attention(cfg, chunk, q_lat, cache, o_lat, workspace, stream=None):
+    _check(load().mla_latent_attention(ctypes.byref(cfg), ctypes.byref(chunk), _ptr(q_lat),
+                                       _ptr(cache), _ptr(o_lat), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "mla_latent_attention")
+
+
+def set_timing_events(ev_start, ev_stop):
+    load().mla_set_timing_events(ev_start, ev_stop)
+
+
+def attention_grid(cfg, chunk):
+    return load().mla_attention_grid(ctypes.byref(cfg), ctypes.byref(chunk))
+
+
+def status_string(status):
+    return load().mla_status_string(int(status)).decode()
+
+
+def last_error():
+    return load().mla_last_error().decode()

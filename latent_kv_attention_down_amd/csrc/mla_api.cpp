@@ -1,0 +1,489 @@
+// Host side of the C ABI declared in include/mla.h: argument validation, ring and
+// window index arithmetic, workspace carving and the launch sequence of the MLA
+// chunk step on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "../../include/mla.h"
+#include "mla_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+constexpr int kMaxAttnGrid = 512;  // persistent attention workgroups, upper bound
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int fail(int status, const std::string &msg) {
+  g_last_error = msg;
+  return status;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shapes derived from the config and chunk.
+struct Dims {
+  int64_t tpf;       // tokens per latent frame
+  int64_t T_q;       // chunk tokens per request
+  int64_t M;         // B * T_q
+  int64_t R;         // rows per request = T_q * n_h
+  int64_t DK;        // d_c + d_rope
+  int64_t ring;      // W * tpf rows per request
+  int64_t nk;        // valid keys
+  int64_t start0;    // first contiguous ring range of the window
+  int64_t len0;
+  size_t esz;
+};
+
+Dims dims(const mla_config &c, const mla_chunk &k) {
+  Dims d;
+  d.tpf = (int64_t)c.grid_h * c.grid_w;
+  d.T_q = (int64_t)k.chunk_frames * d.tpf;
+  d.M = (int64_t)k.batch * d.T_q;
+  d.R = d.T_q * c.n_heads;
+  d.DK = (int64_t)c.d_c + c.d_rope;
+  d.ring = (int64_t)c.window_frames * d.tpf;
+  d.nk = (int64_t)k.n_valid_frames * d.tpf;
+  const int64_t last = k.t0 + k.chunk_frames - 1;
+  const int64_t first = last - k.n_valid_frames + 1;
+  const int64_t slot0 = first % c.window_frames;
+  const int64_t run = std::min<int64_t>(k.n_valid_frames, c.window_frames - slot0);
+  d.start0 = slot0 * d.tpf;
+  d.len0 = run * d.tpf;
+  d.esz = c.dtype == MLA_BF16 ? 2 : 4;
+  return d;
+}
+
+int validate_config(const mla_config *c) {
+  if (!c) return fail(MLA_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->d_model <= 0 || c->n_heads <= 0 || c->d_head <= 0 || c->d_nope <= 0 || c->d_rope <= 0 ||
+      c->d_c <= 0 || c->d_q <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "dimensions must be positive");
+  if (c->d_nope + c->d_rope != c->d_head)
+    return fail(MLA_ERR_INVALID_ARG, "d_nope + d_rope must equal d_head");
+  if (c->d_rope % 2 != 0) return fail(MLA_ERR_INVALID_ARG, "d_rope must be even");
+  if (c->d_rope / 2 > 64) return fail(MLA_ERR_INVALID_ARG, "at most 64 RoPE pairs");
+  for (int a = 0; a < 3; ++a)
+    if (c->rope_pairs[a] < 0) return fail(MLA_ERR_INVALID_ARG, "negative rope_pairs");
+  if (c->rope_pairs[0] + c->rope_pairs[1] + c->rope_pairs[2] != c->d_rope / 2)
+    return fail(MLA_ERR_INVALID_ARG, "rope_pairs must sum to d_rope / 2");
+  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta))
+    return fail(MLA_ERR_INVALID_ARG, "rope_theta must be positive and finite");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(MLA_ERR_INVALID_ARG, "rms_eps must be >= 0 and finite");
+  if (c->grid_h <= 0 || c->grid_w <= 0) return fail(MLA_ERR_INVALID_ARG, "grid must be positive");
+  if (c->window_frames <= 0) return fail(MLA_ERR_INVALID_ARG, "window_frames must be positive");
+  if (c->dtype != MLA_BF16 && c->dtype != MLA_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype");
+  const int64_t ring = (int64_t)c->window_frames * c->grid_h * c->grid_w;
+  if (ring >= (int64_t)1 << 30) return fail(MLA_ERR_INVALID_ARG, "ring too large");
+  if (c->dtype == MLA_BF16) {
+    if (c->d_model % 32 || c->d_q % 32 || c->d_c % 32 || c->d_nope % 32 ||
+        (c->n_heads * c->d_head) % 32 || c->d_rope % 16)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "bf16 path needs d_model, d_q, d_c, d_nope, n_heads*d_head % 32 == 0 and "
+                  "d_rope % 16 == 0");
+    if (!mla::latent_attention_bf16_supported(c->d_c, c->d_rope))
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "bf16 path is built for (d_c, d_rope) in {(128,32), (192,32), (256,32), (192,64)}");
+  } else {
+    if (c->d_c + c->d_rope > 512) return fail(MLA_ERR_UNSUPPORTED, "fp32 path needs d_c + d_rope <= 512");
+  }
+  return MLA_OK;
+}
+
+int validate_chunk(const mla_config *c, const mla_chunk *k) {
+  if (!k) return fail(MLA_ERR_INVALID_ARG, "chunk is NULL");
+  if (k->batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
+  if (k->chunk_frames <= 0) return fail(MLA_ERR_INVALID_ARG, "chunk_frames must be >= 1");
+  if (k->chunk_frames > c->window_frames)
+    return fail(MLA_ERR_INVALID_ARG, "chunk_frames must be <= window_frames");
+  if (k->t0 < 0) return fail(MLA_ERR_INVALID_ARG, "t0 must be >= 0");
+  if (k->n_valid_frames < k->chunk_frames || k->n_valid_frames > c->window_frames)
+    return fail(MLA_ERR_INVALID_ARG, "need chunk_frames <= n_valid_frames <= window_frames");
+  if (k->n_valid_frames > k->t0 + k->chunk_frames)
+    return fail(MLA_ERR_INVALID_ARG, "window reaches before frame 0");
+  const int64_t rows = (int64_t)k->batch * k->chunk_frames * c->grid_h * c->grid_w * c->n_heads;
+  if (rows >= (int64_t)1 << 30) return fail(MLA_ERR_INVALID_ARG, "chunk too large");
+  return MLA_OK;
+}
+
+int validate(const mla_config *c, const mla_chunk *k) {
+  int s = validate_config(c);
+  if (s != MLA_OK) return s;
+  return validate_chunk(c, k);
+}
+
+int validate_weights(const mla_config &c, const mla_weights *w, bool write, bool attend,
+                     bool project) {
+  if (!w) return fail(MLA_ERR_INVALID_ARG, "weights is NULL");
+  if (write && (!w->w_kv_down || !w->w_kr)) return fail(MLA_ERR_INVALID_ARG, "w_kv_down/w_kr NULL");
+  if (attend && (!w->w_q_down || !w->w_q_up || !w->w_qr || !w->w_k_up || !w->w_v_up))
+    return fail(MLA_ERR_INVALID_ARG, "a query/up-projection weight is NULL");
+  if (project && !w->w_o) return fail(MLA_ERR_INVALID_ARG, "w_o is NULL");
+  const void *ptrs[] = {w->w_kv_down, w->w_kr, w->w_q_down, w->w_q_up, w->w_qr,
+                        w->w_k_up,    w->w_v_up, w->w_o};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "weights must be 16-byte aligned");
+  (void)c;
+  return MLA_OK;
+}
+
+// RoPE table: pair k of axis a turns by theta^(-2k / D_a) per unit position with
+// D_y = D_x = 2 * floor(d_head / 6) and D_t = d_head - 2 * D_y; the pairs of each
+// axis take its highest-frequency bands (k = 0, 1, ...).
+mla::RopeTable rope_table(const mla_config &c) {
+  mla::RopeTable t;
+  std::memset(&t, 0, sizeof(t));
+  const int d_sp = 2 * (c.d_head / 6);
+  const int width[3] = {c.d_head - 2 * d_sp, d_sp, d_sp};
+  int p = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int k = 0; k < c.rope_pairs[a]; ++k, ++p) {
+      t.axis[p] = a;
+      t.omega[p] = (float)std::pow((double)c.rope_theta, -2.0 * k / (double)width[a]);
+    }
+  t.n_pairs = p;
+  return t;
+}
+
+int attn_grid(const Dims &d, const mla_config &c, const mla_chunk &k) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  int g = cus < kMaxAttnGrid ? cus : kMaxAttnGrid;
+  (void)d;
+  (void)c;
+  (void)k;
+  return g;
+}
+
+// Workspace carving (offsets in bytes, each 256-aligned).
+struct Workspace {
+  size_t u_q, c_q, q_nope, q_r, w_t, q_lat, o_lat, part, flags, out_heads, total;
+};
+
+Workspace carve(const mla_config &c, const mla_chunk &k) {
+  const Dims d = dims(c, k);
+  Workspace w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  w.u_q = take((size_t)d.M * c.d_q * 4);
+  w.c_q = take((size_t)d.M * c.d_q * d.esz);
+  w.q_nope = take((size_t)d.M * c.n_heads * c.d_nope * d.esz);
+  w.q_r = take((size_t)d.M * c.n_heads * c.d_rope * 4);
+  w.w_t = take((size_t)c.n_heads * c.d_c * c.d_nope * d.esz);
+  w.q_lat = take((size_t)k.batch * d.R * d.DK * d.esz);
+  w.o_lat = take((size_t)k.batch * d.R * c.d_c * d.esz);
+  size_t part = 0, flags = 0;
+  if (c.dtype == MLA_BF16) {
+    const int64_t rw = mla::latent_attention_rows_per_wg(c.d_c, c.d_rope);
+    const int64_t rt = (int64_t)k.batch * ((d.R + rw - 1) / rw);
+    part = (size_t)(kMaxAttnGrid + rt) * mla::latent_attention_record_bytes(c.d_c, c.d_rope);
+    flags = (size_t)rt * sizeof(int);
+  }
+  w.part = take(part);
+  w.flags = take(flags);
+  w.out_heads = take((size_t)d.M * c.n_heads * c.d_head * d.esz);
+  w.total = off;
+  return w;
+}
+
+int hip_fail(hipError_t e, const char *stage) {
+  return fail(MLA_ERR_HIP, std::string(stage) + ": " + hipGetErrorString(e));
+}
+
+#define MLA_HIP(call, stage)                      \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, stage); \
+  } while (0)
+
+int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
+                    void *cache, hipStream_t st) {
+  const Dims d = dims(c, k);
+  mla::CacheWriteArgs a;
+  a.x = x;
+  a.w_kv = w.w_kv_down;
+  a.w_kr = w.w_kr;
+  a.g_kv = w.g_kv;
+  a.cache = cache;
+  a.M = (int)d.M;
+  a.T_q = (int)d.T_q;
+  a.d = c.d_model;
+  a.d_c = c.d_c;
+  a.d_rope = c.d_rope;
+  a.tpf = (int)d.tpf;
+  a.grid_w = c.grid_w;
+  a.W = c.window_frames;
+  a.t0 = k.t0;
+  a.cache_batch_rows = d.ring;
+  a.eps = c.rms_eps;
+  a.rope = rope_table(c);
+  if (c.dtype == MLA_BF16)
+    MLA_HIP(mla::cache_write_bf16(a, st), "cache write");
+  else
+    MLA_HIP(mla::cache_write_f32(a, st), "cache write");
+  return MLA_OK;
+}
+
+int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_lat,
+                         const void *cache, void *o_lat, unsigned char *ws, hipStream_t st) {
+  const Dims d = dims(c, k);
+  const Workspace L = carve(c, k);
+  mla::AttnArgs a;
+  a.q = q_lat;
+  a.cache = cache;
+  a.o = o_lat;
+  a.part = ws + L.part;
+  a.flags = (int *)(ws + L.flags);
+  a.B = k.batch;
+  a.R = (int)d.R;
+  a.DC = c.d_c;
+  a.DR = c.d_rope;
+  a.cache_rows = d.ring;
+  a.nk = (int)d.nk;
+  a.start0 = (int)d.start0;
+  a.len0 = (int)d.len0;
+  a.grid = attn_grid(d, c, k);
+  if (c.dtype == MLA_BF16)
+    MLA_HIP(mla::latent_attention_bf16(a, g_ev_start, g_ev_stop, st), "latent attention");
+  else
+    MLA_HIP(mla::latent_attention_f32(a, g_ev_start, g_ev_stop, st), "latent attention");
+  return MLA_OK;
+}
+
+mla::GemmArgs gemm(const void *A, int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB,
+                   void *C, int64_t ldc, int64_t sC, int64_t M, int N, int K, int batch, float alpha) {
+  mla::GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.sA = sA;
+  g.B = B;
+  g.ldb = ldb;
+  g.sB = sB;
+  g.C = C;
+  g.ldc = ldc;
+  g.sC = sC;
+  g.M = (int)M;
+  g.N = N;
+  g.K = K;
+  g.batch = batch;
+  g.alpha = alpha;
+  return g;
+}
+
+int run_gemm(const mla_config &c, const mla::GemmArgs &g, bool out_f32, hipStream_t st,
+             const char *stage) {
+  if (c.dtype == MLA_BF16)
+    MLA_HIP(mla::gemm_bf16_nt(g, out_f32, st), stage);
+  else
+    MLA_HIP(mla::gemm_f32_nt(g, st), stage);
+  return MLA_OK;
+}
+
+#define MLA_TRY(expr)           \
+  do {                          \
+    int s_ = (expr);            \
+    if (s_ != MLA_OK) return s_; \
+  } while (0)
+
+// Query preparation, latent attention and per-head value up-projection.
+int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chunk &k,
+                        const void *x, const void *cache, void *out_heads, unsigned char *ws,
+                        hipStream_t st) {
+  const Dims d = dims(c, k);
+  const Workspace L = carve(c, k);
+  const bool bf = c.dtype == MLA_BF16;
+  const int nh = c.n_heads;
+  const float scale = (float)(1.4426950408889634 / std::sqrt((double)(c.d_nope + c.d_rope)));
+  float *u_q = (float *)(ws + L.u_q);
+  void *c_q = ws + L.c_q, *q_nope = ws + L.q_nope, *w_t = ws + L.w_t;
+  float *q_r = (float *)(ws + L.q_r);
+  unsigned char *q_lat = ws + L.q_lat, *o_lat = ws + L.o_lat;
+
+  // c^Q = RMSNorm(W^Q_down x)  (Eq. 3, App. D.2)
+  MLA_TRY(run_gemm(c, gemm(x, c.d_model, 0, w.w_q_down, c.d_model, 0, u_q, c.d_q, 0, d.M, c.d_q,
+                           c.d_model, 1, 1.f),
+                   true, st, "query down-projection"));
+  MLA_HIP(mla::rmsnorm_rows(u_q, w.g_q, c_q, (int)d.M, c.d_q, c.rms_eps, bf, st), "query rmsnorm");
+  // q^nope = W^Q_up c^Q (Eq. 4), q^R = W^Q_R c^Q (Eq. 6)
+  MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_q_up, c.d_q, 0, q_nope, (int64_t)nh * c.d_nope, 0,
+                           d.M, nh * c.d_nope, c.d_q, 1, 1.f),
+                   false, st, "query up-projection"));
+  MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qr, c.d_q, 0, q_r, (int64_t)nh * c.d_rope, 0, d.M,
+                           nh * c.d_rope, c.d_q, 1, 1.f),
+                   true, st, "positional query projection"));
+  // q~_h = (W^K_up,h)^T q^nope_h, scaled (App. E Eq. 8-9 applied to the query)
+  MLA_HIP(mla::transpose_heads(w.w_k_up, w_t, nh, c.d_nope, c.d_c, (int)d.esz, st), "key up transpose");
+  MLA_TRY(run_gemm(c, gemm(q_nope, (int64_t)nh * c.d_nope, c.d_nope, w_t, c.d_nope,
+                           (int64_t)c.d_c * c.d_nope, q_lat, (int64_t)nh * d.DK, d.DK, d.M, c.d_c,
+                           c.d_nope, nh, scale),
+                   false, st, "key absorption"));
+  // RoPE3D(q^R_h) into the last d_rope columns, same scale (Eq. 6, 12)
+  mla::RopeQArgs rq;
+  rq.q_r = q_r;
+  rq.q_lat = q_lat;
+  rq.M = (int)d.M;
+  rq.T_q = (int)d.T_q;
+  rq.n_h = nh;
+  rq.d_rope = c.d_rope;
+  rq.d_c = c.d_c;
+  rq.tpf = (int)d.tpf;
+  rq.grid_w = c.grid_w;
+  rq.t0 = k.t0;
+  rq.scale = scale;
+  rq.rope = rope_table(c);
+  MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
+  // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16)
+  MLA_TRY(run_latent_attention(c, k, q_lat, cache, o_lat, ws, st));
+  // o_h = W^V_up,h O_lat,h  (Eq. 2)
+  MLA_TRY(run_gemm(c, gemm(o_lat, (int64_t)nh * c.d_c, c.d_c, w.w_v_up, c.d_c,
+                           (int64_t)c.d_head * c.d_c, out_heads, (int64_t)nh * c.d_head, c.d_head,
+                           d.M, c.d_head, c.d_c, nh, 1.f),
+                   false, st, "value up-projection"));
+  return MLA_OK;
+}
+
+int check_ws(const mla_config &c, const mla_chunk &k, void *ws, size_t ws_bytes) {
+  const size_t need = carve(c, k).total;
+  if (!ws || ws_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(MLA_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_validate(const mla_config *cfg, const mla_chunk *chunk) {
+  g_last_error.clear();
+  return validate(cfg, chunk);
+}
+
+size_t mla_workspace_bytes(const mla_config *cfg, const mla_chunk *chunk) {
+  if (validate(cfg, chunk) != MLA_OK) return 0;
+  return carve(*cfg, *chunk).total;
+}
+
+size_t mla_cache_bytes(const mla_config *cfg, int32_t batch) {
+  if (validate_config(cfg) != MLA_OK || batch <= 0) return 0;
+  const size_t esz = cfg->dtype == MLA_BF16 ? 2 : 4;
+  return (size_t)batch * cfg->window_frames * cfg->grid_h * cfg->grid_w *
+         (size_t)(cfg->d_c + cfg->d_rope) * esz;
+}
+
+int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+                    const void *x, void *cache, void *stream) {
+  g_last_error.clear();
+  MLA_TRY(validate(cfg, chunk));
+  MLA_TRY(validate_weights(*cfg, w, true, false, false));
+  if (!x || !cache) return fail(MLA_ERR_INVALID_ARG, "x or cache is NULL");
+  if (!aligned16(x) || !aligned16(cache)) return fail(MLA_ERR_ALIGNMENT, "x and cache must be 16-byte aligned");
+  return run_cache_write(*cfg, *w, *chunk, x, cache, (hipStream_t)stream);
+}
+
+int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+                        const void *x, const void *cache, void *out_heads, void *workspace,
+                        size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  MLA_TRY(validate(cfg, chunk));
+  MLA_TRY(validate_weights(*cfg, w, false, true, false));
+  if (!x || !cache || !out_heads) return fail(MLA_ERR_INVALID_ARG, "x, cache or out_heads is NULL");
+  if (!aligned16(x) || !aligned16(cache) || !aligned16(out_heads))
+    return fail(MLA_ERR_ALIGNMENT, "x, cache and out_heads must be 16-byte aligned");
+  MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
+  return run_chunk_attention(*cfg, *w, *chunk, x, cache, out_heads, (unsigned char *)workspace,
+                             (hipStream_t)stream);
+}
+
+int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk, const void *x,
+             void *cache, void *y, void *workspace, size_t ws_bytes, void *stream) {
+  g_last_error.clear();
+  MLA_TRY(validate(cfg, chunk));
+  MLA_TRY(validate_weights(*cfg, w, true, true, true));
+  if (!x || !cache || !y) return fail(MLA_ERR_INVALID_ARG, "x, cache or y is NULL");
+  if (!aligned16(x) || !aligned16(cache) || !aligned16(y))
+    return fail(MLA_ERR_ALIGNMENT, "x, cache and y must be 16-byte aligned");
+  MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
+  const mla_config &c = *cfg;
+  const mla_chunk &k = *chunk;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char *ws = (unsigned char *)workspace;
+  const Workspace L = carve(c, k);
+  const Dims d = dims(c, k);
+  MLA_TRY(run_cache_write(c, *w, k, x, cache, st));
+  MLA_TRY(run_chunk_attention(c, *w, k, x, cache, ws + L.out_heads, ws, st));
+  // y = W_O out  (§3.3)
+  MLA_TRY(run_gemm(c, gemm(ws + L.out_heads, (int64_t)c.n_heads * c.d_head, 0, w->w_o,
+                           (int64_t)c.n_heads * c.d_head, 0, y, c.d_model, 0, d.M, c.d_model,
+                           c.n_heads * c.d_head, 1, 1.f),
+                   false, st, "output projection"));
+  return MLA_OK;
+}
+
+int mla_latent_attention(const mla_config *cfg, const mla_chunk *chunk, const void *q_lat,
+                         const void *cache, void *o_lat, void *workspace, size_t ws_bytes,
+                         void *stream) {
+  g_last_error.clear();
+  MLA_TRY(validate(cfg, chunk));
+  if (!q_lat || !cache || !o_lat) return fail(MLA_ERR_INVALID_ARG, "q_lat, cache or o_lat is NULL");
+  if (!aligned16(q_lat) || !aligned16(cache) || !aligned16(o_lat))
+    return fail(MLA_ERR_ALIGNMENT, "q_lat, cache and o_lat must be 16-byte aligned");
+  MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
+  return run_latent_attention(*cfg, *chunk, q_lat, cache, o_lat, (unsigned char *)workspace,
+                              (hipStream_t)stream);
+}
+
+void mla_set_timing_events(void *ev_start, void *ev_stop) {
+  if (ev_start && ev_stop) {
+    g_ev_start = (hipEvent_t)ev_start;
+    g_ev_stop = (hipEvent_t)ev_stop;
+  } else {
+    g_ev_start = nullptr;
+    g_ev_stop = nullptr;
+  }
+}
+
+int mla_attention_grid(const mla_config *cfg, const mla_chunk *chunk) {
+  if (validate(cfg, chunk) != MLA_OK) return 0;
+  const Dims d = dims(*cfg, *chunk);
+  if (cfg->dtype != MLA_BF16) return (int)((d.M * cfg->n_heads + 3) / 4);
+  const int64_t rw = mla::latent_attention_rows_per_wg(cfg->d_c, cfg->d_rope);
+  const int64_t t = (int64_t)chunk->batch * ((d.R + rw - 1) / rw) *
+                    ((d.nk + mla::kAttnKeyTile - 1) / mla::kAttnKeyTile);
+  const int64_t g = attn_grid(d, *cfg, *chunk);
+  return (int)(g < t ? g : t);
+}
+
+const char *mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_UNKNOWN_STATUS";
+  }
+}
+
+const char *mla_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

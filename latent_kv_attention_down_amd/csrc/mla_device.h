@@ -1,0 +1,59 @@
+// Device-side types and helpers shared by the gfx950 kernels of the MLA chunk step.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_types.h"
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+namespace mla {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// 32x32x16 bf16 MFMA, D = A(32x16) * B(16x32) + C.  Lane l supplies A row l%32 and
+// B column l%32, eight consecutive k of the 16 (group l/32).  Lane l receives
+// column l%32 of D, rows 8*i + 4*(l/32) + j in acc[4*i + j].
+__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16 MFMA.  Lane l supplies A row l%16 / B column l%16 with eight
+// consecutive k (group l/16).  Lane l receives column l%16, rows 4*(l/16)+j in acc[j].
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Rotate pair (re, im) by angle pos * omega (counter-clockwise).
+__device__ __forceinline__ void rope_rotate(float &re, float &im, float pos, float omega) {
+  float s, c;
+  sincosf(pos * omega, &s, &c);
+  float r = re * c - im * s;
+  float i = re * s + im * c;
+  re = r;
+  im = i;
+}
+
+}  // namespace mla

@@ -1,0 +1,83 @@
+// Internal host-side launchers of the gfx950 kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_types.h"
+
+namespace mla {
+
+// C[b] = alpha * A[b] (M x K, row stride lda) * B[b]^T (B is N x K, row stride ldb);
+// batch b offsets each operand by its batch stride (elements).
+struct GemmArgs {
+  const void *A;
+  int64_t lda, sA;
+  const void *B;
+  int64_t ldb, sB;
+  void *C;
+  int64_t ldc, sC;
+  int M, N, K, batch;
+  float alpha;
+};
+hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st);
+hipError_t gemm_f32_nt(const GemmArgs &g, hipStream_t st);
+
+// Fused cache write: [W_kv_down; W_kr] x -> RMSNorm(latent) * g, RoPE(k^R) -> ring rows.
+struct CacheWriteArgs {
+  const void *x, *w_kv, *w_kr, *g_kv;
+  void *cache;
+  int M;          // B * tokens in the chunk
+  int T_q;        // tokens in the chunk per request
+  int d, d_c, d_rope, tpf, grid_w, W;
+  int64_t t0;
+  int64_t cache_batch_rows;  // W * tpf
+  float eps;
+  RopeTable rope;
+};
+hipError_t cache_write_bf16(const CacheWriteArgs &a, hipStream_t st);
+hipError_t cache_write_f32(const CacheWriteArgs &a, hipStream_t st);
+
+// out[r] = in[r] / sqrt(mean(in[r]^2) + eps) * g  (in fp32, out bf16 or fp32).
+hipError_t rmsnorm_rows(const float *in, const void *g, void *out, int rows, int cols, float eps,
+                        bool out_bf16, hipStream_t st);
+
+// q_lat[(m*n_h + h), d_c + i] = scale * RoPE(q_r[m, h*d_rope + i]) at token m's position.
+struct RopeQArgs {
+  const float *q_r;
+  void *q_lat;
+  int M, T_q, n_h, d_rope, d_c, tpf, grid_w;
+  int64_t t0;
+  float scale;
+  RopeTable rope;
+};
+hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st);
+
+// w_t[h][c][n] = w_k_up[h*d_nope + n][c]  (per-head transpose, element size esz).
+hipError_t transpose_heads(const void *w, void *w_t, int n_h, int d_nope, int d_c, int esz,
+                           hipStream_t st);
+
+// Latent attention over the ring window.
+struct AttnArgs {
+  const void *q;       // (B, R, DK)
+  const void *cache;   // (B, cache_rows, DK)
+  void *o;             // (B, R, DC)
+  void *part;          // split records (bf16 path)
+  int *flags;          // one int per fast row tile (bf16 path)
+  int B, R, DC, DR;
+  int64_t cache_rows;  // rows per request in the ring
+  int nk;              // valid keys
+  int start0, len0;    // first contiguous row range of the window; the rest starts at row 0
+  int grid;            // persistent workgroups
+};
+hipError_t latent_attention_bf16(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1,
+                                 hipStream_t st);
+hipError_t latent_attention_f32(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1,
+                                hipStream_t st);
+bool latent_attention_bf16_supported(int dc, int dr);
+// Rows of queries per workgroup and key tile length of the bf16 kernel.
+int latent_attention_rows_per_wg(int dc, int dr);
+constexpr int kAttnKeyTile = 64;
+// Bytes of one split record (rows_per_wg rows of DC bf16 plus m and l in fp32).
+size_t latent_attention_record_bytes(int dc, int dr);
+
+}  // namespace mla

@@ -1,0 +1,14 @@
+// Plain data types shared by the host launchers and the kernels.
+#pragma once
+
+namespace mla {
+
+// 3D-RoPE rotation table, passed to kernels by value: per complex pair, its axis
+// (0 = t, 1 = y, 2 = x) and its angular frequency (radians per position).
+struct RopeTable {
+  int n_pairs;
+  int axis[64];
+  float omega[64];
+};
+
+}  // namespace mla

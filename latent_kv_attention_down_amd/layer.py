@@ -1,0 +1,84 @@
+"""Device memory for one MLA layer: weights, ring cache and workspace as torch
+tensors, with the ctypes structs the C ABI takes.  PyTorch is used only to own
+device memory and to name the stream."""
+import numpy as np
+import torch
+
+from . import _lib
+
+WEIGHT_FIELDS = ("w_kv_down", "w_kr", "g_kv", "w_q_down", "g_q", "w_q_up", "w_qr", "w_k_up",
+                 "w_v_up", "w_o")
+
+
+def to_device(arr, dtype, device="cuda"):
+    """Host array -> device tensor.  bf16 arrays are given as uint16 bit patterns."""
+    a = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 arrays are passed as uint16 bit patterns")
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a.astype(np.float32)).to(device)
+
+
+def to_host(t):
+    """Device tensor -> float64 numpy (exact for bf16 and fp32)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class DeviceLayer:
+    def __init__(self, shape, stored_weights, batch=1, device="cuda"):
+        self.shape = shape
+        self.dtype = shape.dtype
+        self.tdtype = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        self.device = device
+        self.cfg = _lib.make_config(shape)
+        self.tensors = {k: to_device(stored_weights[k], self.dtype, device)
+                        for k in WEIGHT_FIELDS if stored_weights.get(k) is not None}
+        self.weights = _lib.make_weights(self.tensors)
+        self.batch = batch
+        tpf = shape.grid_h * shape.grid_w
+        self.cache = torch.zeros((batch, shape.window_frames * tpf, shape.d_c + shape.d_rope),
+                                 dtype=self.tdtype, device=device)
+        assert self.cache.numel() * self.cache.element_size() == _lib.cache_bytes(self.cfg, batch)
+        self._ws = None
+
+    def chunk(self, chunk_frames, t0, n_valid_frames):
+        return _lib.make_chunk(self.batch, chunk_frames, t0, n_valid_frames)
+
+    def workspace(self, chunk):
+        n = _lib.workspace_bytes(self.cfg, chunk)
+        if n == 0:
+            raise _lib.MLAError(_lib.validate(self.cfg, chunk), "mla_workspace_bytes")
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n + 256, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def tokens(self, x_host):
+        return to_device(x_host, self.dtype, self.device)
+
+    def new_out(self, chunk, width):
+        tpf = self.shape.grid_h * self.shape.grid_w
+        return torch.empty((self.batch, chunk.chunk_frames * tpf, width), dtype=self.tdtype,
+                           device=self.device)
+
+    def cache_write(self, chunk, x):
+        _lib.cache_write(self.cfg, self.weights, chunk, x, self.cache)
+
+    def chunk_attention(self, chunk, x):
+        s = self.shape
+        out = self.new_out(chunk, s.n_heads * s.d_head)
+        _lib.chunk_attention(self.cfg, self.weights, chunk, x, self.cache, out,
+                             self.workspace(chunk))
+        return out
+
+    def step(self, chunk, x):
+        y = self.new_out(chunk, self.shape.d_model)
+        _lib.step(self.cfg, self.weights, chunk, x, self.cache, y, self.workspace(chunk))
+        return y
+
+    def latent_attention(self, chunk, q_lat):
+        s = self.shape
+        o = torch.empty((q_lat.shape[0], q_lat.shape[1], s.d_c), dtype=self.tdtype,
+                        device=self.device)
+        _lib.latent_attention(self.cfg, chunk, q_lat, self.cache, o, self.workspace(chunk))
+        return o

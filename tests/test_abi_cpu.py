@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mla.h declares, and its host-only calls (validation, workspace and cache
+sizing, status strings) behave as documented.  No compute entry point is called
+with valid arguments here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import latent_kv_attention_down_amd as mla
+import workload as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mla.load()
+
+
+def test_header_declares_the_three_entry_points():
+    fns = header_functions()
+    for name in ("mla_cache_write", "mla_chunk_attention", "mla_step"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    fns = header_functions()
+    assert fns, "no declarations parsed"
+    for name in fns:
+        assert hasattr(lib, name), name
+    assert set(fns) == set(mla.SIGNATURES), "binding and header disagree"
+
+
+def cfg_of(name, **kw):
+    return mla.make_config(W.shape_by_name(name).with_(**kw))
+
+
+def chunk_of(s, **kw):
+    d = dict(batch=1, chunk_frames=s.chunk_frames, t0=s.t0, n_valid_frames=s.n_valid_frames)
+    d.update(kw)
+    return mla.make_chunk(**d)
+
+
+@pytest.mark.parametrize("name", ["tiny-f32", "wan1.3b-w21", "wan1.3b-w42-t240",
+                                  "wan1.3b-w21-t240-q1", "wan1.3b-w21-dc128-dr32",
+                                  "wan1.3b-w21-dc256-dr32", "wan1.3b-w21-dc192-dr64"])
+def test_workload_shapes_validate(name):
+    s = W.shape_by_name(name)
+    assert mla.validate(mla.make_config(s), chunk_of(s)) == mla.MLA_OK, mla.last_error()
+
+
+def test_cache_bytes_is_224_scalars_per_token():
+    """Only d_c + d_rope scalars per token are cached (VideoMLA App. E, Eq. 13)."""
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    assert mla.cache_bytes(cfg, 1) == 21 * 1560 * 224 * 2
+    assert mla.cache_bytes(cfg, 3) == 3 * 21 * 1560 * 224 * 2
+    assert mla.cache_bytes(mla.make_config(s, dtype="f32"), 1) == 21 * 1560 * 224 * 4
+    assert mla.cache_bytes(cfg, 0) == 0
+
+
+def test_workspace_bytes_positive_and_monotone():
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    w1 = mla.workspace_bytes(cfg, chunk_of(s))
+    w2 = mla.workspace_bytes(cfg, chunk_of(s, batch=2))
+    assert 0 < w1 < w2
+    assert w1 % 256 == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_model", 0, mla.MLA_ERR_INVALID_ARG),
+    ("d_nope", 95, mla.MLA_ERR_INVALID_ARG),          # d_nope + d_rope != d_head
+    ("d_rope", 31, mla.MLA_ERR_INVALID_ARG),
+    ("window_frames", 0, mla.MLA_ERR_INVALID_ARG),
+    ("grid_w", -1, mla.MLA_ERR_INVALID_ARG),
+    ("dtype", 7, mla.MLA_ERR_INVALID_ARG),
+    ("rope_theta", 0.0, mla.MLA_ERR_INVALID_ARG),
+    ("d_c", 160, mla.MLA_ERR_UNSUPPORTED),            # bf16 kernel not built for 160
+    ("d_q", 100, mla.MLA_ERR_UNSUPPORTED),            # bf16 needs multiples of 32
+])
+def test_validate_rejects(field, value, code):
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    setattr(cfg, field, value)
+    if field == "d_rope":
+        cfg.d_nope = cfg.d_head - value
+    assert mla.validate(cfg, chunk_of(s)) == code
+    assert mla.last_error() != ""
+
+
+def test_validate_rope_pairs_sum():
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    cfg.rope_pairs[0] = 7
+    assert mla.validate(cfg, chunk_of(s)) == mla.MLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(chunk_frames=0), dict(chunk_frames=22),
+                                dict(n_valid_frames=2), dict(n_valid_frames=22), dict(t0=-1),
+                                dict(t0=0, n_valid_frames=21)])
+def test_validate_rejects_bad_chunk(kw):
+    s = W.shape_by_name("wan1.3b-w21")
+    assert mla.validate(mla.make_config(s), chunk_of(s, **kw)) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_fp32_path_accepts_odd_dims():
+    s = W.shape_by_name("tiny-f32").with_(d_c=17, d_q=33)
+    assert mla.validate(mla.make_config(s), chunk_of(s)) == mla.MLA_OK
+
+
+def test_null_arguments_fail_before_any_launch(lib):
+    """Invalid calls return a status on the host; nothing is launched (no GPU here)."""
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    ch = chunk_of(s)
+    w = mla.Weights()
+    assert lib.mla_cache_write(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ch), None, None,
+                               None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_step(None, None, None, None, None, None, None, 0, None) == mla.MLA_ERR_INVALID_ARG
+    # misaligned pointers are refused before any HIP call
+    fake = {n: 4096 for n, _ in mla.Weights._fields_}
+    wt = mla.Weights(**fake)
+    assert lib.mla_cache_write(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4097, 4096,
+                               None) == mla.MLA_ERR_ALIGNMENT
+    # a workspace that is too small is refused before any HIP call
+    assert lib.mla_latent_attention(ctypes.byref(cfg), ctypes.byref(ch), 4096, 4096, 4096, 4096, 16,
+                                    None) == mla.MLA_ERR_WORKSPACE
+
+
+def test_status_strings(lib):
+    for code, name in ((0, "MLA_OK"), (-1, "MLA_ERR_INVALID_ARG"), (-2, "MLA_ERR_UNSUPPORTED"),
+                       (-3, "MLA_ERR_ALIGNMENT"), (-4, "MLA_ERR_WORKSPACE"), (-5, "MLA_ERR_HIP")):
+        assert mla.status_string(code) == name
+    assert mla.status_string(42) == "MLA_UNKNOWN_STATUS"

@@ -8,13 +8,15 @@
 // O = sum_j a_j c_j over the d_c latent columns (V is the first d_c columns of K).
 //
 // gfx950 mapping (bf16):
-//  * a workgroup is 4 waves; each wave owns QT tiles of 32 query rows and keeps
+//  * a workgroup is NW waves; each wave owns QT tiles of 32 query rows and keeps
 //    their q_lat in registers as MFMA B operands for the whole window;
 //  * key tiles of 64 ring rows are staged once per workgroup in LDS twice: key-
 //    major (A operand of S^T = K Q^T, contraction over features) and, for the d_c
 //    latent columns, feature-major (A operand of O^T = V^T P^T, contraction over
 //    keys).  The transposed copy is written from the registers that carry the
-//    global loads, so HBM/L2 is read once per tile;
+//    global loads, so HBM/L2 is read once per tile.  With DB the stage is double
+//    buffered: the next tile's global loads fly during this tile's MFMAs and one
+//    barrier per tile remains;
 //  * S^T comes out of v_mfma_f32_32x32x16_bf16 with one query per lane column, so
 //    the row max needs one cross-lane step (lane l and l^32) and the bf16
 //    probabilities feed the next MFMA as its B operand without a shuffle;
@@ -36,10 +38,9 @@
 namespace mla {
 namespace {
 
-constexpr int BN = kAttnKeyTile;      // keys per tile
+constexpr int BN = kAttnKeyTile;       // keys per tile
 constexpr float kFastHeadroom = 64.f;  // log2 units above the fixed reference
 constexpr float kSafeThreshold = 8.f;  // lazy rescale threshold of the safe kernel
-constexpr int kSafeQT = 1;
 
 struct Sched {
   int B, R, RTb, RT;
@@ -54,86 +55,96 @@ __host__ __device__ __forceinline__ int wg_of(const Sched &s, int64_t flat) {
   return (int)(((flat + 1) * s.G - 1) / s.T);
 }
 
-template <int DC, int DR, int QT>
+// DC/DR: latent and RoPE widths; QT: 32-row query tiles per wave; NW: waves per
+// workgroup; DB: double-buffered LDS stage; WPC: workgroups resident per CU.
+template <int DC_, int DR_, int QT_, int NW_, bool DB_, int WPC_>
 struct Cfg {
+  static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_, WPC = WPC_;
+  static constexpr bool DB = DB_;
+  static constexpr int NT = NW * 64;
   static constexpr int DK = DC + DR;
   static constexpr int KB = DK / 16;
   static constexpr int FT = DC / 32;
-  static constexpr int RW = 4 * QT * 32;
-  static constexpr int KS = DK + 8;
-  static constexpr int VS = BN + 8;
-  static constexpr int LAT_PER_T = (BN / 2) * (DC / 8) / 256;
-  static constexpr int ROPE_CH = BN * (DR / 8);
-  static constexpr int ROPE_PER_T = (ROPE_CH + 255) / 256;
-  static constexpr size_t LDS = (size_t)(BN * KS + DC * VS) * 2;
+  static constexpr int RW = NW * QT * 32;
+  static constexpr int KS = DK + 8;           // LDS row stride (elements) of the key tile
+  static constexpr int CPR = DK / 8;          // 16-byte chunks per ring row
+  static constexpr int CHUNKS = BN * CPR;     // chunks per key tile
+  static constexpr int CH_PER_T = (CHUNKS + NT - 1) / NT;
+  static constexpr int STAGE = BN * KS;       // elements per LDS stage
+  static constexpr size_t LDS = (size_t)STAGE * 2 * (DB ? 2 : 1);
   static constexpr size_t REC = (size_t)RW * DC * 2 + (size_t)RW * 8;
-  static_assert((BN / 2) * (DC / 8) % 256 == 0, "latent cells must split evenly");
+  static constexpr int WAVES_PER_SIMD = (NW / 4) * WPC;
+  static_assert(NW % 4 == 0, "whole waves per SIMD");
   static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
 };
 
-// One workgroup's view of the ring: global -> registers -> LDS (key-major K and
-// feature-major V^T), and the two MFMA contractions of a key tile.
-template <int DC, int DR, int QT>
+// Production configuration per (d_c, d_rope), and the safe-path configuration.
+template <int DC, int DR>
+struct Choice {
+  using Fast = Cfg<DC, DR, 1, 8, false, 1>;
+  using Safe = Cfg<DC, DR, 1, 4, false, 1>;
+};
+
+// One workgroup's view of the ring: global -> registers -> LDS (one key-major tile
+// of BN ring rows), and the two MFMA contractions of a key tile.  The score
+// contraction reads 16-byte K fragments (lane: key l32, features 8g..8g+7); the
+// value contraction reads V^T fragments from the same tile with the gfx950 LDS
+// transpose load ds_read_b64_tr_b16, which hands each lane one feature of four
+// consecutive keys, so no transposed copy of the latent is ever written.
+template <class C>
 struct Tile {
-  using C = Cfg<DC, DR, QT>;
-  static constexpr int DK = C::DK, KB = C::KB, FT = C::FT, KS = C::KS, VS = C::VS;
-  bf16 *Ks, *Vt;
+  static constexpr int DC = C::DC, DR = C::DR, QT = C::QT, NT = C::NT;
+  static constexpr int DK = C::DK, KB = C::KB, FT = C::FT, KS = C::KS, CPR = C::CPR;
+  bf16 *base;      // LDS stage(s)
   const bf16 *cb;  // this request's ring
   int nk, start0, len0;
-  uint4 lat0[C::LAT_PER_T], lat1[C::LAT_PER_T], rop[C::ROPE_PER_T];
+  uint4 reg[C::CH_PER_T];
+
+  __device__ __forceinline__ bf16 *Ks(int buf) const { return base + buf * C::STAGE; }
 
   __device__ __forceinline__ int64_t key_row(int kk) const {
     return kk < len0 ? (int64_t)(start0 + kk) : (int64_t)(kk - len0);
   }
 
+  // Global loads of tile kt into registers: chunk c = tid + NT*i is 16 bytes of
+  // key c / CPR at feature 8 * (c % CPR); consecutive lanes read consecutive bytes.
   __device__ __forceinline__ void load(int kt, int tid) {
+    const int k0 = kt * BN;
+    const bool contiguous = (k0 + BN <= nk) && (k0 + BN <= len0 || k0 >= len0);
+    if (contiguous) {
+      const bf16 *tb = cb + key_row(k0) * DK;
 #pragma unroll
-    for (int c = 0; c < C::LAT_PER_T; ++c) {
-      const int cell = tid + 256 * c, p = cell / (DC / 8), ch = cell % (DC / 8);
-      const int kk = kt * BN + 2 * p;
-      lat0[c] = kk < nk ? *(const uint4 *)(cb + key_row(kk) * DK + ch * 8) : make_uint4(0, 0, 0, 0);
-      lat1[c] = kk + 1 < nk ? *(const uint4 *)(cb + key_row(kk + 1) * DK + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
+      for (int i = 0; i < C::CH_PER_T; ++i) {
+        const int c = tid + NT * i;
+        if (C::CHUNKS % NT == 0 || c < C::CHUNKS) reg[i] = *(const uint4 *)(tb + c * 8);
+      }
+    } else {
 #pragma unroll
-    for (int c = 0; c < C::ROPE_PER_T; ++c) {
-      const int id = tid + 256 * c;
-      if (id < C::ROPE_CH) {
-        const int key = id / (DR / 8), ch = id % (DR / 8), kk = kt * BN + key;
-        rop[c] = kk < nk ? *(const uint4 *)(cb + key_row(kk) * DK + DC + ch * 8)
-                         : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < C::CH_PER_T; ++i) {
+        const int c = tid + NT * i;
+        if (C::CHUNKS % NT == 0 || c < C::CHUNKS) {
+          const int kk = k0 + c / CPR;
+          reg[i] = kk < nk ? *(const uint4 *)(cb + key_row(kk) * DK + (c % CPR) * 8)
+                           : make_uint4(0, 0, 0, 0);
+        }
       }
     }
   }
 
-  __device__ __forceinline__ void store(int tid) {
+  __device__ __forceinline__ void store(int tid, int buf) {
+    bf16 *ks = Ks(buf);
 #pragma unroll
-    for (int c = 0; c < C::LAT_PER_T; ++c) {
-      const int cell = tid + 256 * c, p = cell / (DC / 8), ch = cell % (DC / 8);
-      *(uint4 *)(Ks + (2 * p) * KS + ch * 8) = lat0[c];
-      *(uint4 *)(Ks + (2 * p + 1) * KS + ch * 8) = lat1[c];
-      const uint32_t *a0 = (const uint32_t *)&lat0[c], *a1 = (const uint32_t *)&lat1[c];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = (a0[d] & 0xffffu) | (a1[d] << 16);
-        const uint32_t hi = (a0[d] >> 16) | (a1[d] & 0xffff0000u);
-        *(uint32_t *)(Vt + (ch * 8 + 2 * d) * VS + 2 * p) = lo;
-        *(uint32_t *)(Vt + (ch * 8 + 2 * d + 1) * VS + 2 * p) = hi;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < C::ROPE_PER_T; ++c) {
-      const int id = tid + 256 * c;
-      if (id < C::ROPE_CH) {
-        const int key = id / (DR / 8), ch = id % (DR / 8);
-        *(uint4 *)(Ks + key * KS + DC + ch * 8) = rop[c];
-      }
+    for (int i = 0; i < C::CH_PER_T; ++i) {
+      const int c = tid + NT * i;
+      if (C::CHUNKS % NT == 0 || c < C::CHUNKS)
+        *(uint4 *)(ks + (c / CPR) * KS + (c % CPR) * 8) = reg[i];
     }
   }
 
   // S^T (keys x queries) for the 64 keys of tile kt; masked keys get -inf.
   __device__ __forceinline__ void scores(f32x16 (&S)[2][QT], const bf16x8 (&Qr)[QT][KB], int kt,
-                                         int l32, int g) const {
+                                         int buf, int l32, int g) const {
+    const bf16 *ks = Ks(buf);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -144,10 +155,13 @@ struct Tile {
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = *(const bf16x8 *)(Ks + (t * 32 + l32) * KS + kb * 16 + g * 8);
+        const bf16x8 a = *(const bf16x8 *)(ks + (t * 32 + l32) * KS + kb * 16 + g * 8);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) S[t][qt] = mfma32(a, Qr[qt][kb], S[t][qt]);
       }
+      // keep one k-block of fragments in flight: 2 LDS reads, then their MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * QT, 0);
     }
     if ((kt + 1) * BN > nk) {
 #pragma unroll
@@ -162,19 +176,35 @@ struct Tile {
     }
   }
 
-  // O^T (features x queries) += V^T P^T over the tile's four 16-key blocks.
+  // O^T (features x queries) += V^T P^T over the tile's four 16-key blocks.  For
+  // block kb the A operand of lane l (16-lane group G = l/16, r = l%16) must hold
+  // feature ft*32 + l%32 of keys kb*16 + 4g + j (slots 0-3) and kb*16 + 8 + 4g + j
+  // (slots 4-7).  ds_read_b64_tr_b16 gives lane r of a 16-lane group element r%4 of
+  // the 8-byte chunks addressed by lanes r/4 + 4j, so lane r addresses key
+  // kb*16 + 8h + 4g + r/4 at feature ft*32 + 16*(G%2) + 4*(r%4).
   __device__ __forceinline__ void values(f32x16 (&O)[FT][QT], const bf16x8 (&P)[BN / 16][QT],
-                                         int l32, int g) const {
+                                         int buf, int lane) const {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int G = lane >> 4, r = lane & 15, g = lane >> 5;
+    const bf16 *vt = Ks(buf) + (4 * g + (r >> 2)) * KS + 16 * (G & 1) + 4 * (r & 3);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
 #pragma unroll
       for (int kb = 0; kb < BN / 16; ++kb) {
-        const bf16 *vr = Vt + (ft * 32 + l32) * VS + kb * 16 + g * 4;
-        const uint2 lo = *(const uint2 *)vr, hi = *(const uint2 *)(vr + 8);
-        uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const bf16x8 a = *(const bf16x8 *)&u;
+        const bf16 *p0 = vt + (kb * 16) * KS + ft * 32;
+        const bf16 *p1 = p0 + 8 * KS;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)p0);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)p1);
+        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+        const s16x8 u = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) O[ft][qt] = mfma32(a, P[kb][qt], O[ft][qt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
       }
     }
   }
@@ -241,8 +271,8 @@ __device__ __forceinline__ void load_queries(bf16x8 (&Qr)[QT][KB], const bf16 *q
 
 // Normalise and store 32 rows x DC: lane holds row l32, features ft*32 + 8i + 4g + j.
 template <int FT, int QT>
-__device__ __forceinline__ void store_rows(bf16 *dst, int64_t ld, const f32x16 (&O)[FT][QT], int qt,
-                                           float inv, int g) {
+__device__ __forceinline__ void store_rows(bf16 *dst, const f32x16 (&O)[FT][QT], int qt, float inv,
+                                           int g) {
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
@@ -252,20 +282,18 @@ __device__ __forceinline__ void store_rows(bf16 *dst, int64_t ld, const f32x16 (
       for (int j = 0; j < 4; ++j) v4[j] = (bf16)(O[ft][qt][4 * i + j] * inv);
       *(uint2 *)(dst + ft * 32 + i * 8 + g * 4) = *(const uint2 *)v4;
     }
-  (void)ld;
 }
 
-template <int DC, int DR, int QT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class C>
+__global__ __launch_bounds__(C::NT)
+__attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD)))
 void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
                    bf16 *__restrict__ o, unsigned char *__restrict__ part, int *__restrict__ flags,
                    Sched s) {
-  using C = Cfg<DC, DR, QT>;
-  constexpr int KB = C::KB, FT = C::FT, RW = C::RW;
+  constexpr int DC = C::DC, QT = C::QT, KB = C::KB, FT = C::FT, RW = C::RW;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  Tile<DC, DR, QT> tl;
-  tl.Ks = (bf16 *)lds;
-  tl.Vt = tl.Ks + BN * C::KS;
+  Tile<C> tl;
+  tl.base = (bf16 *)lds;
   tl.nk = s.nk;
   tl.start0 = s.start0;
   tl.len0 = s.len0;
@@ -300,15 +328,9 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
     }
     bool over = false;
 
-    tl.load(kt0, tid);
-    for (int kt = kt0; kt < kt1; ++kt) {
-      __syncthreads();
-      tl.store(tid);
-      __syncthreads();
-      if (kt + 1 < kt1) tl.load(kt + 1, tid);
-
+    auto compute = [&](int kt, int buf) {
       f32x16 S[2][QT];
-      tl.scores(S, Qr, kt, l32, g);
+      tl.scores(S, Qr, kt, buf, l32, g);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const float mx = tile_max<QT>(S, qt);
@@ -316,7 +338,28 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
         over |= mx > m[qt] + kFastHeadroom;
         l[qt] += exp_and_pack<QT>(S, P, qt, m[qt]);
       }
-      tl.values(O, P, l32, g);
+      tl.values(O, P, buf, lane);
+    };
+
+    tl.load(kt0, tid);
+    if (C::DB) {
+      tl.store(tid, 0);
+      __syncthreads();
+      for (int kt = kt0; kt < kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        if (kt + 1 < kt1) tl.load(kt + 1, tid);
+        compute(kt, cur);
+        if (kt + 1 < kt1) tl.store(tid, cur ^ 1);
+        __syncthreads();
+      }
+    } else {
+      for (int kt = kt0; kt < kt1; ++kt) {
+        __syncthreads();
+        tl.store(tid, 0);
+        __syncthreads();
+        if (kt + 1 < kt1) tl.load(kt + 1, tid);
+        compute(kt, 0);
+      }
     }
 
     if (over) flags[rt] = 1;
@@ -331,7 +374,7 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
       const int row = row0 + lrow;
       if (row < s.R) {
         bf16 *dst = whole ? o + ((int64_t)b * s.R + row) * DC : (bf16 *)rec + (int64_t)lrow * DC;
-        store_rows<FT, QT>(dst, DC, O, qt, 1.0f / lt, g);
+        store_rows<FT, QT>(dst, O, qt, 1.0f / lt, g);
         if (!whole && g == 0) {
           rec_m[lrow] = m[qt];
           rec_l[lrow] = lt;
@@ -342,69 +385,60 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
   }
 }
 
-// Merge the pieces of every row tile that more than one workgroup worked on.
-template <int DC, int DR, int QT>
+// Merge the pieces of every row tile that more than one workgroup worked on.  One
+// thread per (row, 8 latent columns): it weighs each piece's normalised partial by
+// l_p * 2^(m_p - max m) and renormalises.  Workgroups of unsplit tiles exit at once.
+template <class C>
 __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
-                                                    const unsigned char *__restrict__ part, Sched s) {
-  using C = Cfg<DC, DR, QT>;
-  constexpr int RW = C::RW;
-  constexpr int PER = (DC + 63) / 64;
-  const int rt = blockIdx.x;
+                                                    const unsigned char *__restrict__ part, Sched s,
+                                                    int blocks_per_tile) {
+  constexpr int DC = C::DC, RW = C::RW, C8 = DC / 8;
+  const int rt = blockIdx.x / blocks_per_tile;
   const int g0 = wg_of(s, (int64_t)rt * s.KT), g1 = wg_of(s, (int64_t)rt * s.KT + s.KT - 1);
   if (g0 == g1) return;
-  const int b = rt / s.RTb, row0 = (rt % s.RTb) * RW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int lrow = wave; lrow < RW; lrow += 4) {
-    const int row = row0 + lrow;
-    if (row >= s.R) break;
-    float mmax = -INFINITY;
-    for (int gg = g0; gg <= g1; ++gg) {
-      const float *rm = (const float *)(part + (size_t)(gg + rt) * C::REC + (size_t)RW * DC * 2);
-      mmax = fmaxf(mmax, rm[lrow]);
-    }
-    float wsum = 0.f;
-    float acc[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    for (int gg = g0; gg <= g1; ++gg) {
-      const unsigned char *rec = part + (size_t)(gg + rt) * C::REC;
-      const float *rm = (const float *)(rec + (size_t)RW * DC * 2);
-      const float w = rm[RW + lrow] * fast_exp2(rm[lrow] - mmax);
-      wsum += w;
-      const bf16 *ro = (const bf16 *)rec + (int64_t)lrow * DC;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int f = lane + 64 * i;
-        if (f < DC) acc[i] += w * (float)ro[f];
-      }
-    }
-    const float inv = 1.0f / wsum;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int f = lane + 64 * i;
-      if (f < DC) o[((int64_t)b * s.R + row) * DC + f] = (bf16)(acc[i] * inv);
-    }
+  const int idx = (blockIdx.x % blocks_per_tile) * 256 + threadIdx.x;
+  const int lrow = idx / C8, c8 = (idx % C8) * 8;
+  const int b = rt / s.RTb, row = (rt % s.RTb) * RW + lrow;
+  if (lrow >= RW || row >= s.R) return;
+  float mmax = -INFINITY;
+  for (int gg = g0; gg <= g1; ++gg) {
+    const float *rm = (const float *)(part + (size_t)(gg + rt) * C::REC + (size_t)RW * DC * 2);
+    mmax = fmaxf(mmax, rm[lrow]);
   }
+  float wsum = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int gg = g0; gg <= g1; ++gg) {
+    const unsigned char *rec = part + (size_t)(gg + rt) * C::REC;
+    const float *rm = (const float *)(rec + (size_t)RW * DC * 2);
+    const float w = rm[RW + lrow] * fast_exp2(rm[lrow] - mmax);
+    wsum += w;
+    const bf16x8 v = *(const bf16x8 *)((const bf16 *)rec + (int64_t)lrow * DC + c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
+  }
+  const float inv = 1.0f / wsum;
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (bf16)(acc[e] * inv);
+  *(bf16x8 *)(o + ((int64_t)b * s.R + row) * DC + c8) = out;
 }
 
 // Safe recomputation of the row tiles the fast kernel flagged: the whole window per
 // workgroup, reference max raised lazily (by more than kSafeThreshold) with O
 // rescaled, result written directly.  Workgroups of unflagged tiles exit at once.
-template <int DC, int DR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_latent_attn_safe(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
                         bf16 *__restrict__ o, const int *__restrict__ flags, Sched s,
                         int fast_rw) {
-  constexpr int QT = kSafeQT;
-  using C = Cfg<DC, DR, QT>;
-  constexpr int KB = C::KB, FT = C::FT, RW = C::RW;
+  constexpr int QT = C::QT, KB = C::KB, FT = C::FT, RW = C::RW;
   const int RTb = (s.R + RW - 1) / RW;
   const int b = blockIdx.x / RTb, row0 = (blockIdx.x % RTb) * RW;
   if (!flags[b * s.RTb + row0 / fast_rw]) return;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  Tile<DC, DR, QT> tl;
-  tl.Ks = (bf16 *)lds;
-  tl.Vt = tl.Ks + BN * C::KS;
+  Tile<C> tl;
+  tl.base = (bf16 *)lds;
   tl.nk = s.nk;
   tl.start0 = s.start0;
   tl.len0 = s.len0;
@@ -429,11 +463,11 @@ void k_latent_attn_safe(const bf16 *__restrict__ q, const bf16 *__restrict__ cac
   tl.load(0, tid);
   for (int kt = 0; kt < s.KT; ++kt) {
     __syncthreads();
-    tl.store(tid);
+    tl.store(tid, 0);
     __syncthreads();
     if (kt + 1 < s.KT) tl.load(kt + 1, tid);
     f32x16 S[2][QT];
-    tl.scores(S, Qr, kt, l32, g);
+    tl.scores(S, Qr, kt, 0, l32, g);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float mx = tile_max<QT>(S, qt);
@@ -449,13 +483,13 @@ void k_latent_attn_safe(const bf16 *__restrict__ q, const bf16 *__restrict__ cac
       }
       l[qt] += exp_and_pack<QT>(S, P, qt, m[qt]);
     }
-    tl.values(O, P, l32, g);
+    tl.values(O, P, 0, lane);
   }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
     const int row = row0 + wave * QT * 32 + qt * 32 + l32;
-    if (row < s.R) store_rows<FT, QT>(o + ((int64_t)b * s.R + row) * DC, DC, O, qt, 1.0f / lt, g);
+    if (row < s.R) store_rows<FT, QT>(o + ((int64_t)b * s.R + row) * C::DC, O, qt, 1.0f / lt, g);
   }
 }
 
@@ -511,7 +545,7 @@ __global__ __launch_bounds__(256) void k_latent_attn_f32(const float *__restrict
   }
 }
 
-Sched make_sched(const AttnArgs &a, int rows_per_wg) {
+Sched make_sched(const AttnArgs &a, int rows_per_wg, int grid) {
   Sched s;
   s.B = a.B;
   s.R = a.R;
@@ -523,7 +557,7 @@ Sched make_sched(const AttnArgs &a, int rows_per_wg) {
   s.len0 = a.len0;
   s.cache_rows = a.cache_rows;
   s.T = (int64_t)s.RT * s.KT;
-  s.G = (int)((int64_t)a.grid < s.T ? (int64_t)a.grid : s.T);
+  s.G = (int)((int64_t)grid < s.T ? (int64_t)grid : s.T);
   return s;
 }
 
@@ -534,31 +568,37 @@ hipError_t allow_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <int DC, int DR, int QT>
+template <int DC, int DR>
 hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
-  using C = Cfg<DC, DR, QT>;
-  using CS = Cfg<DC, DR, kSafeQT>;
-  Sched s = make_sched(a, C::RW);
+  using F = typename Choice<DC, DR>::Fast;
+  using S = typename Choice<DC, DR>::Safe;
+  Sched s = make_sched(a, F::RW, a.grid * F::WPC);
   if (s.T <= 0) return hipSuccess;
-  hipError_t e = allow_lds(k_latent_attn<DC, DR, QT>, C::LDS);
-  if (e == hipSuccess) e = allow_lds(k_latent_attn_safe<DC, DR>, CS::LDS);
+  hipError_t e = allow_lds(k_latent_attn<F>, F::LDS);
+  if (e == hipSuccess) e = allow_lds(k_latent_attn_safe<S>, S::LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_fill_i32, dim3((s.RT + 255) / 256), dim3(256), 0, st, a.flags, s.RT, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_latent_attn<DC, DR, QT>), dim3(s.G), dim3(256), C::LDS, st,
-                     (const bf16 *)a.q, (const bf16 *)a.cache, (bf16 *)a.o,
-                     (unsigned char *)a.part, a.flags, s);
+  hipLaunchKernelGGL(k_latent_attn<F>, dim3(s.G), dim3(F::NT), F::LDS, st, (const bf16 *)a.q,
+                     (const bf16 *)a.cache, (bf16 *)a.o, (unsigned char *)a.part, a.flags, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_attn_merge<DC, DR, QT>), dim3(s.RT), dim3(256), 0, st, (bf16 *)a.o,
-                     (const unsigned char *)a.part, s);
+  const int merge_blocks = (F::RW * (DC / 8) + 255) / 256;
+  hipLaunchKernelGGL(k_attn_merge<F>, dim3(s.RT * merge_blocks), dim3(256), 0, st, (bf16 *)a.o,
+                     (const unsigned char *)a.part, s, merge_blocks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int safe_tiles = s.B * ((s.R + CS::RW - 1) / CS::RW);
-  hipLaunchKernelGGL((k_latent_attn_safe<DC, DR>), dim3(safe_tiles), dim3(256), CS::LDS, st,
+  const int safe_tiles = s.B * ((s.R + S::RW - 1) / S::RW);
+  hipLaunchKernelGGL(k_latent_attn_safe<S>, dim3(safe_tiles), dim3(S::NT), S::LDS, st,
                      (const bf16 *)a.q, (const bf16 *)a.cache, (bf16 *)a.o,
-                     (const int *)a.flags, s, C::RW);
+                     (const int *)a.flags, s, F::RW);
   return hipGetLastError();
+}
+
+template <int DC, int DR>
+AttnLayout layout() {
+  using F = typename Choice<DC, DR>::Fast;
+  return AttnLayout{F::RW, F::WPC, F::REC};
 }
 
 }  // namespace
@@ -568,22 +608,20 @@ bool latent_attention_bf16_supported(int dc, int dr) {
          (dc == 192 && dr == 64);
 }
 
-int latent_attention_rows_per_wg(int dc, int dr) {
-  (void)dr;
-  return dc >= 256 ? Cfg<256, 32, 1>::RW : Cfg<192, 32, 2>::RW;
-}
-
-size_t latent_attention_record_bytes(int dc, int dr) {
-  const size_t rw = (size_t)latent_attention_rows_per_wg(dc, dr);
-  return rw * dc * 2 + rw * 8;
+AttnLayout latent_attention_layout(int dc, int dr) {
+  if (dc == 192 && dr == 32) return layout<192, 32>();
+  if (dc == 128 && dr == 32) return layout<128, 32>();
+  if (dc == 256 && dr == 32) return layout<256, 32>();
+  if (dc == 192 && dr == 64) return layout<192, 64>();
+  return AttnLayout{0, 0, 0};
 }
 
 hipError_t latent_attention_bf16(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1,
                                  hipStream_t st) {
-  if (a.DC == 192 && a.DR == 32) return launch<192, 32, 2>(a, ev0, ev1, st);
-  if (a.DC == 128 && a.DR == 32) return launch<128, 32, 2>(a, ev0, ev1, st);
-  if (a.DC == 256 && a.DR == 32) return launch<256, 32, 1>(a, ev0, ev1, st);
-  if (a.DC == 192 && a.DR == 64) return launch<192, 64, 2>(a, ev0, ev1, st);
+  if (a.DC == 192 && a.DR == 32) return launch<192, 32>(a, ev0, ev1, st);
+  if (a.DC == 128 && a.DR == 32) return launch<128, 32>(a, ev0, ev1, st);
+  if (a.DC == 256 && a.DR == 32) return launch<256, 32>(a, ev0, ev1, st);
+  if (a.DC == 192 && a.DR == 64) return launch<192, 64>(a, ev0, ev1, st);
   return hipErrorInvalidValue;
 }
 
@@ -592,7 +630,7 @@ hipError_t latent_attention_f32(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev
   if (a.DC + a.DR > 512 || a.DC > 512) return hipErrorInvalidValue;
   const int64_t rows = (int64_t)a.B * a.R;
   if (rows <= 0 || a.nk <= 0) return hipSuccess;
-  Sched s = make_sched(a, 1);
+  Sched s = make_sched(a, 1, 1);
   hipError_t e;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_latent_attn_f32, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,

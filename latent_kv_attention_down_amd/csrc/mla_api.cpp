@@ -9,7 +9,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "mla_launch.h"
 
 namespace {
@@ -155,18 +155,15 @@ mla::RopeTable rope_table(const mla_config &c) {
   return t;
 }
 
-int attn_grid(const Dims &d, const mla_config &c, const mla_chunk &k) {
+// Compute units of the current device (capped), the persistent grid's unit.
+int attn_grid_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       cus = v;
   }
-  int g = cus < kMaxAttnGrid ? cus : kMaxAttnGrid;
-  (void)d;
-  (void)c;
-  (void)k;
-  return g;
+  return cus < kMaxAttnGrid ? cus : kMaxAttnGrid;
 }
 
 // Workspace carving (offsets in bytes, each 256-aligned).
@@ -192,9 +189,11 @@ Workspace carve(const mla_config &c, const mla_chunk &k) {
   w.o_lat = take((size_t)k.batch * d.R * c.d_c * d.esz);
   size_t part = 0, flags = 0;
   if (c.dtype == MLA_BF16) {
-    const int64_t rw = mla::latent_attention_rows_per_wg(c.d_c, c.d_rope);
+    // split records are indexed (workgroup + row tile) < grid + row tiles
+    const mla::AttnLayout al = mla::latent_attention_layout(c.d_c, c.d_rope);
+    const int64_t rw = al.rows_per_wg;
     const int64_t rt = (int64_t)k.batch * ((d.R + rw - 1) / rw);
-    part = (size_t)(kMaxAttnGrid + rt) * mla::latent_attention_record_bytes(c.d_c, c.d_rope);
+    part = (size_t)((int64_t)kMaxAttnGrid * al.wgs_per_cu + rt) * al.record_bytes;
     flags = (size_t)rt * sizeof(int);
   }
   w.part = take(part);
@@ -260,7 +259,7 @@ int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_
   a.nk = (int)d.nk;
   a.start0 = (int)d.start0;
   a.len0 = (int)d.len0;
-  a.grid = attn_grid(d, c, k);
+  a.grid = attn_grid_cus();
   if (c.dtype == MLA_BF16)
     MLA_HIP(mla::latent_attention_bf16(a, g_ev_start, g_ev_stop, st), "latent attention");
   else
@@ -465,10 +464,11 @@ int mla_attention_grid(const mla_config *cfg, const mla_chunk *chunk) {
   if (validate(cfg, chunk) != MLA_OK) return 0;
   const Dims d = dims(*cfg, *chunk);
   if (cfg->dtype != MLA_BF16) return (int)((d.M * cfg->n_heads + 3) / 4);
-  const int64_t rw = mla::latent_attention_rows_per_wg(cfg->d_c, cfg->d_rope);
+  const mla::AttnLayout al = mla::latent_attention_layout(cfg->d_c, cfg->d_rope);
+  const int64_t rw = al.rows_per_wg;
   const int64_t t = (int64_t)chunk->batch * ((d.R + rw - 1) / rw) *
                     ((d.nk + mla::kAttnKeyTile - 1) / mla::kAttnKeyTile);
-  const int64_t g = attn_grid(d, *cfg, *chunk);
+  const int64_t g = (int64_t)attn_grid_cus() * al.wgs_per_cu;
   return (int)(g < t ? g : t);
 }
 

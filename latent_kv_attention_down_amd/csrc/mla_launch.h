@@ -74,10 +74,15 @@ hipError_t latent_attention_bf16(const AttnArgs &a, hipEvent_t ev0, hipEvent_t e
 hipError_t latent_attention_f32(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1,
                                 hipStream_t st);
 bool latent_attention_bf16_supported(int dc, int dr);
-// Rows of queries per workgroup and key tile length of the bf16 kernel.
-int latent_attention_rows_per_wg(int dc, int dr);
-constexpr int kAttnKeyTile = 64;
-// Bytes of one split record (rows_per_wg rows of DC bf16 plus m and l in fp32).
-size_t latent_attention_record_bytes(int dc, int dr);
+constexpr int kAttnKeyTile = 64;  // keys per tile of the bf16 kernel
+// Launch geometry of the bf16 kernel for (d_c, d_rope): query rows per workgroup,
+// workgroups resident per CU, and bytes of one split record (rows x d_c bf16 plus
+// m and l in fp32 per row).
+struct AttnLayout {
+  int rows_per_wg;
+  int wgs_per_cu;
+  size_t record_bytes;
+};
+AttnLayout latent_attention_layout(int dc, int dr);
 
 }  // namespace mla

@@ -39,7 +39,7 @@ namespace mla {
 namespace {
 
 constexpr int BN = kAttnKeyTile;       // keys per tile
-constexpr float kFastHeadroom = 64.f;  // log2 units above the fixed reference
+constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: weights above it fall back
 constexpr float kSafeThreshold = 8.f;  // lazy rescale threshold of the safe kernel
 
 struct Sched {
@@ -56,11 +56,12 @@ __host__ __device__ __forceinline__ int wg_of(const Sched &s, int64_t flat) {
 }
 
 // DC/DR: latent and RoPE widths; QT: 32-row query tiles per wave; NW: waves per
-// workgroup; DB: double-buffered LDS stage; WPC: workgroups resident per CU.
-template <int DC_, int DR_, int QT_, int NW_, bool DB_, int WPC_>
+// workgroup; PIPE: 0 = one LDS stage (two barriers per tile), 1 = two stages,
+// 2 = three stages with skewed waves; WPC: workgroups resident per CU.
+template <int DC_, int DR_, int QT_, int NW_, int PIPE_, int WPC_>
 struct Cfg {
-  static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_, WPC = WPC_;
-  static constexpr bool DB = DB_;
+  static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_, WPC = WPC_, PIPE = PIPE_;
+  static constexpr int NBUF = PIPE == 2 ? 3 : (PIPE == 1 ? 2 : 1);
   static constexpr int NT = NW * 64;
   static constexpr int DK = DC + DR;
   static constexpr int KB = DK / 16;
@@ -71,7 +72,7 @@ struct Cfg {
   static constexpr int CHUNKS = BN * CPR;     // chunks per key tile
   static constexpr int CH_PER_T = (CHUNKS + NT - 1) / NT;
   static constexpr int STAGE = BN * KS;       // elements per LDS stage
-  static constexpr size_t LDS = (size_t)STAGE * 2 * (DB ? 2 : 1);
+  static constexpr size_t LDS = (size_t)STAGE * 2 * NBUF;
   static constexpr size_t REC = (size_t)RW * DC * 2 + (size_t)RW * 8;
   static constexpr int WAVES_PER_SIMD = (NW / 4) * WPC;
   static_assert(NW % 4 == 0, "whole waves per SIMD");
@@ -81,8 +82,8 @@ struct Cfg {
 // Production configuration per (d_c, d_rope), and the safe-path configuration.
 template <int DC, int DR>
 struct Choice {
-  using Fast = Cfg<DC, DR, 1, 8, false, 1>;
-  using Safe = Cfg<DC, DR, 1, 4, false, 1>;
+  using Fast = Cfg<DC, DR, 1, 8, 2, 1>;
+  using Safe = Cfg<DC, DR, 1, 4, 0, 1>;
 };
 
 // One workgroup's view of the ring: global -> registers -> LDS (one key-major tile
@@ -326,23 +327,45 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[ft][qt][r] = 0.f;
     }
-    bool over = false;
 
-    auto compute = [&](int kt, int buf) {
+    // scores and probabilities of tile kt (into P)
+    auto softmax_tile = [&](int kt, int buf) {
       f32x16 S[2][QT];
       tl.scores(S, Qr, kt, buf, l32, g);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float mx = tile_max<QT>(S, qt);
-        if (kt == kt0) m[qt] = mx;  // fixed reference for this piece
-        over |= mx > m[qt] + kFastHeadroom;
+        if (kt == kt0) m[qt] = tile_max<QT>(S, qt);  // fixed reference for this piece
         l[qt] += exp_and_pack<QT>(S, P, qt, m[qt]);
       }
+    };
+    auto compute = [&](int kt, int buf) {
+      softmax_tile(kt, buf);
       tl.values(O, P, buf, lane);
     };
 
     tl.load(kt0, tid);
-    if (C::DB) {
+    if (C::PIPE == 2) {
+      // Skewed waves: the second half of the workgroup (one wave per SIMD) takes
+      // its value MFMAs one tile late, so on every SIMD one wave's softmax VALU
+      // work runs beside the other wave's MFMAs.  Three LDS stages: tile kt+1 is
+      // written while tiles kt and kt-1 are read.
+      const bool lag = wave >= C::NW / 2;
+      tl.store(tid, kt0 % 3);
+      __syncthreads();
+      for (int kt = kt0; kt < kt1; ++kt) {
+        if (kt + 1 < kt1) tl.load(kt + 1, tid);
+        if (!lag) {
+          compute(kt, kt % 3);
+        } else {
+          if (kt > kt0) tl.values(O, P, (kt - 1) % 3, lane);
+          softmax_tile(kt, kt % 3);
+        }
+        if (kt + 1 < kt1) tl.store(tid, (kt + 1) % 3);
+        __syncthreads();
+      }
+      if (lag) tl.values(O, P, (kt1 - 1) % 3, lane);
+      __syncthreads();
+    } else if (C::PIPE == 1) {
       tl.store(tid, 0);
       __syncthreads();
       for (int kt = kt0; kt < kt1; ++kt) {
@@ -362,7 +385,6 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
       }
     }
 
-    if (over) flags[rt] = 1;
     const bool whole = (kt0 == 0 && kt1 == s.KT);
     unsigned char *rec = part + (size_t)(wg + rt) * C::REC;
     float *rec_m = (float *)(rec + (size_t)RW * DC * 2);
@@ -370,6 +392,11 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+      // The reference key of the first tile has weight 1, so lt >= 1.  Any weight
+      // above 2^64 (a score more than 64 above the reference) makes lt exceed
+      // 2^64, as does inf or NaN: such a row tile is recomputed by the safe kernel.
+      // Sums above 2^64 made only of smaller weights are flagged too (harmless).
+      if (!(lt <= kFastSumLimit)) flags[rt] = 1;
       const int lrow = wave * QT * 32 + qt * 32 + l32;
       const int row = row0 + lrow;
       if (row < s.R) {

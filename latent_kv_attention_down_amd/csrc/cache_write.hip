@@ -3,10 +3,9 @@
 // RMS-normalises the d_c latent columns (times the gain), rotates the d_rope
 // positional columns by 3D-RoPE at the token's absolute (t, y, x), rounds to the
 // cache type and stores the row into ring slot (frame mod W).
-//  * bf16: 32 tokens per workgroup, the full N = d_c + d_rope columns, 16x16x32
-//    MFMA tiles spread over 4 waves, K tiles of 32 through LDS; the fp32 results
-//    are then reread from LDS for the row-wise norm and rotation and stored as
-//    16-byte chunks.
+//  * bf16: 32 tokens per workgroup and the full N = d_c + d_rope columns, one
+//    wave per 32 columns with 16x16x32 MFMA tiles; the fp32 results are reread
+//    from LDS for the row-wise norm and rotation and stored as 16-byte chunks.
 //  * fp32: one token per workgroup, SIMT dot products.
 #include "mla_device.h"
 #include "mla_launch.h"
@@ -15,8 +14,6 @@ namespace mla {
 namespace {
 
 constexpr int kBM = 32;   // tokens per workgroup (bf16 path)
-constexpr int kBK = 32;
-constexpr int kLds = kBK + 8;
 
 // Row-wise finish on an fp32 tile in LDS: tile[r * ld + c] holds the projections
 // of token m0 + r.  8 threads per row.  Results are written back into the tile.
@@ -58,83 +55,113 @@ __device__ __forceinline__ int64_t ring_row(const CacheWriteArgs &a, int m) {
   return (int64_t)b * a.cache_batch_rows + (f % a.W) * a.tpf + (i % a.tpf);
 }
 
+// bf16: the 32-token x tile stays in LDS for the whole reduction; wave w owns
+// output columns [32w, 32w+32) and streams those weight rows from global memory
+// straight into 16x16x32 MFMA B operands (lane: column l%16, 8 consecutive k),
+// PREF k-steps ahead, so the per-CU weight stream is not serialised behind one
+// load round trip per k-step.
 template <int N>
-__global__ __launch_bounds__(256) void k_cache_write_bf16(CacheWriteArgs a) {
-  constexpr int TILES = (kBM / 16) * (N / 16);
-  static_assert(TILES % 4 == 0, "tiles must split evenly over 4 waves");
-  constexpr int TPW = TILES / 4;
-  constexpr int LDO = N + 4;  // fp32 epilogue tile stride
-  constexpr int STAGE = (kBM + N) * kLds * 2;
-  constexpr int EPI = kBM * LDO * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE > EPI ? STAGE : EPI];
+__global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteArgs a) {
+  constexpr int NWAVE = N / 32;
+  constexpr int NT = 64 * NWAVE;
+  constexpr int PREF = 8;  // k-steps of 32 in flight per lane
+  constexpr int LDO = N + 4;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int LDX = a.d + 8;
   bf16 *sX = (bf16 *)smem;
-  bf16 *sW = sX + kBM * kLds;
   float *tile = (float *)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, kg = (lane >> 4) * 8;
   const int m0 = blockIdx.x * kBM;
   const bf16 *X = (const bf16 *)a.x;
-  const bf16 *Wkv = (const bf16 *)a.w_kv, *Wkr = (const bf16 *)a.w_kr;
 
-  constexpr int W_CH = (N * 4 + 255) / 256;
-  uint4 rx, rw[W_CH];
-  auto load = [&](int k0) {
-    if (tid < kBM * 4) {
-      int r = tid >> 2, kc = (tid & 3) * 8, gm = m0 + r;
-      rx = gm < a.M ? *(const uint4 *)(X + (int64_t)gm * a.d + k0 + kc) : make_uint4(0, 0, 0, 0);
+  // x tile -> LDS (rows past the end are zero), XB loads in flight per thread
+  constexpr int XB = 16;
+  const int cpr = a.d / 8, nchunk = kBM * cpr;
+  for (int c0 = 0; c0 < nchunk; c0 += XB * NT) {
+    uint4 v[XB];
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      const int c = c0 + i * NT + tid, r = c / cpr, gm = m0 + r;
+      v[i] = (c < nchunk && gm < a.M) ? *(const uint4 *)(X + (int64_t)gm * a.d + (c % cpr) * 8)
+                                      : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int c = 0; c < W_CH; ++c) {
-      int id = tid + c * 256;
-      if (id < N * 4) {
-        int r = id >> 2, kc = (id & 3) * 8;
-        const bf16 *src = r < a.d_c ? Wkv + (int64_t)r * a.d : Wkr + (int64_t)(r - a.d_c) * a.d;
-        rw[c] = *(const uint4 *)(src + k0 + kc);
-      }
+    for (int i = 0; i < XB; ++i) {
+      const int c = c0 + i * NT + tid;
+      if (c < nchunk) *(uint4 *)(sX + (c / cpr) * LDX + (c % cpr) * 8) = v[i];
+    }
+  }
+
+  // this lane's two weight rows (columns n of the two 16-wide output tiles)
+  const bf16 *wrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = wave * 32 + j * 16 + l16;
+    wrow[j] = (n < a.d_c ? (const bf16 *)a.w_kv + (int64_t)n * a.d
+                         : (const bf16 *)a.w_kr + (int64_t)(n - a.d_c) * a.d) + kg;
+  }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  auto step = [&](int k, const bf16x8 (&b)[2]) {
+    const bf16x8 a0 = *(const bf16x8 *)(sX + l16 * LDX + k + kg);
+    const bf16x8 a1 = *(const bf16x8 *)(sX + (16 + l16) * LDX + k + kg);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[0][j] = mfma16(a0, b[j], acc[0][j]);
+      acc[1][j] = mfma16(a1, b[j], acc[1][j]);
     }
   };
-  auto store = [&]() {
-    if (tid < kBM * 4) *(uint4 *)(sX + (tid >> 2) * kLds + (tid & 3) * 8) = rx;
+  const int nsteps = a.d / 32, nfull = nsteps / PREF;
+  bf16x8 cur[PREF][2], nxt[PREF][2];
+  if (nfull > 0) {
 #pragma unroll
-    for (int c = 0; c < W_CH; ++c) {
-      int id = tid + c * 256;
-      if (id < N * 4) *(uint4 *)(sW + (id >> 2) * kLds + (id & 3) * 8) = rw[c];
+    for (int s = 0; s < PREF; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) cur[s][j] = *(const bf16x8 *)(wrow[j] + s * 32);
+  }
+  for (int c = 0; c < nfull; ++c) {
+    const int kbase = c * PREF * 32;
+    if (c + 1 < nfull) {
+#pragma unroll
+      for (int s = 0; s < PREF; ++s)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) nxt[s][j] = *(const bf16x8 *)(wrow[j] + kbase + (PREF + s) * 32);
     }
-  };
-
-  f32x4 acc[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int l16 = lane & 15, kg = (lane >> 4) * 8;
-  const int nk = a.d / kBK;
-  load(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (kt + 1 < nk) load((kt + 1) * kBK);
+    for (int s = 0; s < PREF; ++s) step(kbase + s * 32, cur[s]);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int tile_id = wave + 4 * t, tr = tile_id % (kBM / 16), tc = tile_id / (kBM / 16);
-      bf16x8 av = *(const bf16x8 *)(sX + (tr * 16 + l16) * kLds + kg);
-      bf16x8 bv = *(const bf16x8 *)(sW + (tc * 16 + l16) * kLds + kg);
-      acc[t] = mfma16(av, bv, acc[t]);
-    }
+    for (int s = 0; s < PREF; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) cur[s][j] = nxt[s][j];
+  }
+  for (int st = nfull * PREF; st < nsteps; ++st) {  // remaining k-steps, one at a time
+    bf16x8 b[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8 *)(wrow[j] + st * 32);
+    step(st * 32, b);
   }
   __syncthreads();
-  // spill the accumulators to the fp32 tile: lane holds column l16, rows 4*(lane/16)+j
+  // accumulators -> fp32 tile: lane holds column l16, rows 4*(lane/16)+r of each 16x16 tile
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile_id = wave + 4 * t, tr = tile_id % (kBM / 16), tc = tile_id / (kBM / 16);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tile[(tr * 16 + (lane >> 4) * 4 + j) * LDO + tc * 16 + l16] = acc[t][j];
-  }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        tile[(i * 16 + (lane >> 4) * 4 + r) * LDO + wave * 32 + j * 16 + l16] = acc[i][j][r];
   __syncthreads();
   finish_rows<bf16>(tile, LDO, kBM, m0, a);
   __syncthreads();
   // 16-byte stores of the finished rows into the ring
   bf16 *cache = (bf16 *)a.cache;
-  for (int id = tid; id < kBM * (N / 8); id += 256) {
+  for (int id = tid; id < kBM * (N / 8); id += NT) {
     const int r = id / (N / 8), c8 = (id % (N / 8)) * 8, m = m0 + r;
     if (m >= a.M) continue;
     bf16x8 v;
@@ -142,6 +169,20 @@ __global__ __launch_bounds__(256) void k_cache_write_bf16(CacheWriteArgs a) {
     for (int e = 0; e < 8; ++e) v[e] = (bf16)tile[r * LDO + c8 + e];
     *(bf16x8 *)(cache + ring_row(a, m) * N + c8) = v;
   }
+}
+
+template <int N>
+hipError_t launch_bf16(const CacheWriteArgs &a, hipStream_t st) {
+  const size_t lds_x = (size_t)kBM * (a.d + 8) * 2, lds_t = (size_t)kBM * (N + 4) * 4;
+  const size_t lds = lds_x > lds_t ? lds_x : lds_t;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void *)k_cache_write_bf16<N>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_cache_write_bf16<N>, dim3((a.M + kBM - 1) / kBM), dim3(64 * (N / 32)), lds,
+                     st, a);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void k_cache_write_f32(CacheWriteArgs a) {
@@ -172,15 +213,13 @@ __global__ __launch_bounds__(256) void k_cache_write_f32(CacheWriteArgs a) {
 
 hipError_t cache_write_bf16(const CacheWriteArgs &a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
-  dim3 grid((a.M + kBM - 1) / kBM);
   switch (a.d_c + a.d_rope) {
-    case 160: hipLaunchKernelGGL(k_cache_write_bf16<160>, grid, dim3(256), 0, st, a); break;
-    case 224: hipLaunchKernelGGL(k_cache_write_bf16<224>, grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL(k_cache_write_bf16<256>, grid, dim3(256), 0, st, a); break;
-    case 288: hipLaunchKernelGGL(k_cache_write_bf16<288>, grid, dim3(256), 0, st, a); break;
+    case 160: return launch_bf16<160>(a, st);
+    case 224: return launch_bf16<224>(a, st);
+    case 256: return launch_bf16<256>(a, st);
+    case 288: return launch_bf16<288>(a, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t cache_write_f32(const CacheWriteArgs &a, hipStream_t st) {

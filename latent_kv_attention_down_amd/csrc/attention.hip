@@ -58,7 +58,7 @@ __host__ __device__ __forceinline__ int wg_of(const Sched &s, int64_t flat) {
 // DC/DR: latent and RoPE widths; QT: 32-row query tiles per wave; NW: waves per
 // workgroup; PIPE: 0 = one LDS stage (two barriers per tile), 1 = two stages,
 // 2 = three stages with skewed waves; WPC: workgroups resident per CU.
-template <int DC_, int DR_, int QT_, int NW_, int PIPE_, int WPC_>
+template <int DC_, int DR_, int QT_, int NW_, int PIPE_, int WPC_, int PAD_ = 8>
 struct Cfg {
   static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_, WPC = WPC_, PIPE = PIPE_;
   static constexpr int NBUF = PIPE == 2 ? 3 : (PIPE == 1 ? 2 : 1);
@@ -67,7 +67,8 @@ struct Cfg {
   static constexpr int KB = DK / 16;
   static constexpr int FT = DC / 32;
   static constexpr int RW = NW * QT * 32;
-  static constexpr int KS = DK + 8;           // LDS row stride (elements) of the key tile
+  static constexpr int KS = DK + PAD_;        // LDS row stride (elements) of the key tile
+  static_assert(PAD_ % 8 == 0, "rows must stay 16-byte aligned");
   static constexpr int CPR = DK / 8;          // 16-byte chunks per ring row
   static constexpr int CHUNKS = BN * CPR;     // chunks per key tile
   static constexpr int CH_PER_T = (CHUNKS + NT - 1) / NT;
@@ -82,7 +83,7 @@ struct Cfg {
 // Production configuration per (d_c, d_rope), and the safe-path configuration.
 template <int DC, int DR>
 struct Choice {
-  using Fast = Cfg<DC, DR, 1, 8, 2, 1>;
+  using Fast = Cfg<DC, DR, 1, 8, 2, 1, 56>;
   using Safe = Cfg<DC, DR, 1, 4, 0, 1>;
 };
 
@@ -152,15 +153,23 @@ struct Tile {
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[t][qt][r] = 0.f;
+    // Fragments of k-block kb+1 are read before the MFMAs of k-block kb, so each
+    // LDS read has a k-block of MFMA work to hide behind.
+    const bf16 *kr = ks + l32 * KS + g * 8;
+    bf16x8 fr[2][2];  // [k-block parity][key half]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) fr[0][t] = *(const bf16x8 *)(kr + t * 32 * KS);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      if (kb + 1 < KB) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = *(const bf16x8 *)(ks + (t * 32 + l32) * KS + kb * 16 + g * 8);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) S[t][qt] = mfma32(a, Qr[qt][kb], S[t][qt]);
+        for (int t = 0; t < 2; ++t)
+          fr[(kb + 1) & 1][t] = *(const bf16x8 *)(kr + t * 32 * KS + (kb + 1) * 16);
       }
-      // keep one k-block of fragments in flight: 2 LDS reads, then their MFMAs
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) S[t][qt] = mfma32(fr[kb & 1][t], Qr[qt][kb], S[t][qt]);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * QT, 0);
     }
@@ -187,26 +196,28 @@ struct Tile {
                                          int buf, int lane) const {
     typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
     const int G = lane >> 4, r = lane & 15, g = lane >> 5;
     const bf16 *vt = Ks(buf) + (4 * g + (r >> 2)) * KS + 16 * (G & 1) + 4 * (r & 3);
+    auto frag = [&](int i) {  // block i = ft * (BN/16) + kb
+      const bf16 *p0 = vt + ((i % (BN / 16)) * 16) * KS + (i / (BN / 16)) * 32;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(p0 + 8 * KS));
+      return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NB = FT * (BN / 16);
+    bf16x8 fr[2];  // ping-pong: the next fragment is read before this MFMA
+    fr[0] = frag(0);
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
+    for (int i = 0; i < NB; ++i) {
+      if (i + 1 < NB) fr[(i + 1) & 1] = frag(i + 1);
 #pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb) {
-        const bf16 *p0 = vt + (kb * 16) * KS + ft * 32;
-        const bf16 *p1 = p0 + 8 * KS;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)p0);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)p1);
-        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-        const s16x8 u = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) O[ft][qt] = mfma32(a, P[kb][qt], O[ft][qt]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
-      }
+      for (int qt = 0; qt < QT; ++qt)
+        O[i / (BN / 16)][qt] = mfma32(fr[i & 1], P[i % (BN / 16)][qt], O[i / (BN / 16)][qt]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
     }
   }
 };

@@ -1,7 +1,9 @@
 // Projection GEMMs of the MLA chunk step: C = alpha * A * B^T with both operands
 // K-contiguous (x W^T for row-major [out][in] weights).
-//  * bf16: 2x2 waves, each a (BM/2)x(BN/2) block of 32x32x16 MFMA tiles; K tiles of
-//    32 staged through padded LDS with a register prefetch of the next tile.
+//  * bf16: 2x2 waves, each a (BM/2)x(BN/2) block of 32x32x16 MFMA tiles.  K tiles
+//    of BK are staged through two padded LDS stages: the next stage's global loads
+//    are issued before this stage's MFMAs and written to LDS after them, with one
+//    barrier per K tile.
 //  * fp32: plain 16x16 SIMT tiles (the small fp32 path).
 #include "mla_device.h"
 #include "mla_launch.h"
@@ -9,16 +11,16 @@
 namespace mla {
 namespace {
 
-constexpr int kBK = 32;
-constexpr int kLdsStride = kBK + 8;  // pad rows by 16 B
-
-template <int BM, int BN, bool OUT_F32>
+template <int BM, int BN, int BK, bool OUT_F32>
 __global__ __launch_bounds__(256) void k_gemm_bf16_nt(GemmArgs g) {
   constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 tiles per wave
-  constexpr int A_CH = BM * kBK / 8 / 256;   // 16-byte chunks per thread
-  constexpr int B_CH = BN * kBK / 8 / 256;
-  __shared__ __attribute__((aligned(16))) bf16 sA[BM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) bf16 sB[BN * kLdsStride];
+  constexpr int LS = BK + 8;                 // LDS row stride (pads rows by 16 B)
+  constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
+  constexpr int A_CH = BM * CPR / 256;       // chunks per thread
+  constexpr int B_CH = BN * CPR / 256;
+  constexpr int STAGE = (BM + BN) * LS;
+  static_assert(A_CH * 256 == BM * CPR && B_CH * 256 == BN * CPR, "tile/threads mismatch");
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -30,27 +32,26 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_nt(GemmArgs g) {
   auto load = [&](int k0) {
 #pragma unroll
     for (int c = 0; c < A_CH; ++c) {
-      int id = tid + c * 256, r = id >> 2, kc = (id & 3) * 8;
-      int gm = m0 + r;
+      const int id = tid + c * 256, r = id / CPR, kc = (id % CPR) * 8, gm = m0 + r;
       ra[c] = gm < g.M ? *(const uint4 *)(A + (int64_t)gm * g.lda + k0 + kc) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < B_CH; ++c) {
-      int id = tid + c * 256, r = id >> 2, kc = (id & 3) * 8;
-      int gn = n0 + r;
+      const int id = tid + c * 256, r = id / CPR, kc = (id % CPR) * 8, gn = n0 + r;
       rb[c] = gn < g.N ? *(const uint4 *)(B + (int64_t)gn * g.ldb + k0 + kc) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store = [&]() {
+  auto store = [&](int st) {
+    bf16 *sA = smem + st * STAGE, *sB = sA + BM * LS;
 #pragma unroll
     for (int c = 0; c < A_CH; ++c) {
-      int id = tid + c * 256, r = id >> 2, kc = (id & 3) * 8;
-      *(uint4 *)(sA + r * kLdsStride + kc) = ra[c];
+      const int id = tid + c * 256;
+      *(uint4 *)(sA + (id / CPR) * LS + (id % CPR) * 8) = ra[c];
     }
 #pragma unroll
     for (int c = 0; c < B_CH; ++c) {
-      int id = tid + c * 256, r = id >> 2, kc = (id & 3) * 8;
-      *(uint4 *)(sB + r * kLdsStride + kc) = rb[c];
+      const int id = tid + c * 256;
+      *(uint4 *)(sB + (id / CPR) * LS + (id % CPR) * 8) = rb[c];
     }
   };
 
@@ -63,41 +64,45 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_nt(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int l32 = lane & 31, kg = (lane >> 5) * 8;
-  const int nk = g.K / kBK;
+  const int nk = g.K / BK;
   load(0);
+  store(0);
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (kt + 1 < nk) load((kt + 1) * kBK);
+    const int st = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * BK);
+    const bf16 *sA = smem + st * STAGE, *sB = sA + BM * LS;
 #pragma unroll
-    for (int ks = 0; ks < kBK; ks += 16) {
+    for (int ks = 0; ks < BK; ks += 16) {
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *(const bf16x8 *)(sA + (wm * (BM / 2) + i * 32 + l32) * kLdsStride + ks + kg);
+        af[i] = *(const bf16x8 *)(sA + (wm * (BM / 2) + i * 32 + l32) * LS + ks + kg);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfr[j] = *(const bf16x8 *)(sB + (wn * (BN / 2) + j * 32 + l32) * kLdsStride + ks + kg);
+        bfr[j] = *(const bf16x8 *)(sB + (wn * (BN / 2) + j * 32 + l32) * LS + ks + kg);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
     }
+    if (kt + 1 < nk) store(st ^ 1);
+    __syncthreads();
   }
 
+  // lane holds column l32 of each 32x32 tile, rows 8*(r/4) + 4*(lane/32) + r%4
   const int g4 = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      int col = n0 + wn * (BN / 2) + j * 32 + l32;
+      const int col = n0 + wn * (BN / 2) + j * 32 + l32;
       if (col >= g.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int row = m0 + wm * (BM / 2) + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
+        const int row = m0 + wm * (BM / 2) + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
         if (row >= g.M) continue;
-        float v = acc[i][j][r] * g.alpha;
+        const float v = acc[i][j][r] * g.alpha;
         if (OUT_F32)
           ((float *)g.C)[b * g.sC + (int64_t)row * g.ldc + col] = v;
         else
@@ -125,13 +130,13 @@ __global__ __launch_bounds__(256) void k_gemm_f32_nt(GemmArgs g) {
   if (row < g.M && col < g.N) ((float *)g.C)[b * g.sC + (int64_t)row * g.ldc + col] = acc * g.alpha;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 hipError_t launch_bf16(const GemmArgs &g, bool out_f32, hipStream_t st) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.batch);
   if (out_f32)
-    hipLaunchKernelGGL((k_gemm_bf16_nt<BM, BN, true>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_bf16_nt<BM, BN, BK, true>), grid, dim3(256), 0, st, g);
   else
-    hipLaunchKernelGGL((k_gemm_bf16_nt<BM, BN, false>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_bf16_nt<BM, BN, BK, false>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
@@ -139,10 +144,13 @@ hipError_t launch_bf16(const GemmArgs &g, bool out_f32, hipStream_t st) {
 
 hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  // Large problems take 128x128 tiles when that still gives about a full chip.
-  int64_t tiles128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch;
-  if (tiles128 >= 240) return launch_bf16<128, 128>(g, out_f32, st);
-  return launch_bf16<64, 64>(g, out_f32, st);
+  // 128x128 tiles when N fills them and there are enough tiles for the chip
+  // (two workgroups fit per CU); otherwise 64x64.
+  const int64_t tiles128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch;
+  const bool big = (g.N % 128 == 0) && tiles128 >= 200;
+  if (g.K % 64 == 0)
+    return big ? launch_bf16<128, 128, 64>(g, out_f32, st) : launch_bf16<64, 64, 64>(g, out_f32, st);
+  return big ? launch_bf16<128, 128, 32>(g, out_f32, st) : launch_bf16<64, 64, 32>(g, out_f32, st);
 }
 
 hipError_t gemm_f32_nt(const GemmArgs &g, hipStream_t st) {

@@ -123,7 +123,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan1.3b-w21")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2340)
+    ap.add_argument("--cpu-tokens", type=int, default=4680)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of MIB MiB first (a known-size kernel "
+                         "for scaling FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -140,6 +143,13 @@ def main():
     s = W.shape_by_name(args.workload)
     print(f"[bench] workload {s.name}: {s.chunk_tokens} query tokens x {s.n_heads} heads over "
           f"{s.window_tokens} keys", file=sys.stderr, flush=True)
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     stored, w_exact = W.draw_weights(s)
     ids = s.window_frame_ids
     xs, xe = W.draw_frames(s, ids)

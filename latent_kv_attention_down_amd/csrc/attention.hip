@@ -320,11 +320,15 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
   bf16x8 P[BN / 16][QT];
   float m[QT], l[QT];
 
-  int64_t flat = begin;
-  while (flat < end) {
-    const int rt = (int)(flat / s.KT);
-    const int kt0 = (int)(flat - (int64_t)rt * s.KT);
-    const int kt1 = (int)min((int64_t)s.KT, end - (int64_t)rt * s.KT);
+  // Pieces are taken last row tile first: a range that crosses a row-tile boundary
+  // then starts at key tile 0, so at step t nearly every workgroup reads key tile t
+  // (or t + a fixed offset) and the workgroups of one XCD share their L2 lines.
+  const int rt_first = (int)(begin / s.KT), rt_last = (int)((end - 1) / s.KT);
+  const int kt_begin = (int)(begin - (int64_t)rt_first * s.KT);    // first key tile of rt_first
+  const int kt_end = (int)(end - (int64_t)rt_last * s.KT);         // end key tile of rt_last
+  for (int rt = rt_last; rt >= rt_first; --rt) {
+    const int kt0 = rt == rt_first ? kt_begin : 0;
+    const int kt1 = rt == rt_last ? kt_end : s.KT;
     const int b = rt / s.RTb;
     const int row0 = (rt % s.RTb) * RW;
     tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
@@ -419,7 +423,6 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
         }
       }
     }
-    flat = (int64_t)rt * s.KT + kt1;
   }
 }
 

@@ -10,13 +10,16 @@
 // gfx950 mapping (bf16):
 //  * a workgroup is NW waves; each wave owns QT tiles of 32 query rows and keeps
 //    their q_lat in registers as MFMA B operands for the whole window;
-//  * key tiles of 64 ring rows are staged once per workgroup in LDS twice: key-
-//    major (A operand of S^T = K Q^T, contraction over features) and, for the d_c
-//    latent columns, feature-major (A operand of O^T = V^T P^T, contraction over
-//    keys).  The transposed copy is written from the registers that carry the
-//    global loads, so HBM/L2 is read once per tile.  With DB the stage is double
-//    buffered: the next tile's global loads fly during this tile's MFMAs and one
-//    barrier per tile remains;
+//  * key tiles of 64 ring rows are staged once per workgroup in LDS, key-major
+//    only: the score contraction S^T = K Q^T reads 16-byte K fragments, and the
+//    value contraction O^T = V^T P^T reads V^T fragments of the same rows with the
+//    LDS transpose load ds_read_b64_tr_b16, so no transposed copy is written;
+//  * k_latent_attn_w1 (the fast kernel where its registers fit): one wave per
+//    SIMD with 64 query rows, tiles brought in by direct global->LDS loads into an
+//    unpadded swizzled four-stage ring, and the softmax of one half tile
+//    interleaved with the score MFMAs of the next;  k_latent_attn: two waves per
+//    SIMD with 32 rows each, register-staged loads, waves skewed so one wave's
+//    softmax runs beside the other's MFMAs;
 //  * S^T comes out of v_mfma_f32_32x32x16_bf16 with one query per lane column, so
 //    the row max needs one cross-lane step (lane l and l^32) and the bf16
 //    probabilities feed the next MFMA as its B operand without a shuffle;
@@ -60,6 +63,7 @@ __host__ __device__ __forceinline__ int wg_of(const Sched &s, int64_t flat) {
 // 2 = three stages with skewed waves; WPC: workgroups resident per CU.
 template <int DC_, int DR_, int QT_, int NW_, int PIPE_, int WPC_, int PAD_ = 8>
 struct Cfg {
+  static constexpr bool DIRECT = false;
   static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_, WPC = WPC_, PIPE = PIPE_;
   static constexpr int NBUF = PIPE == 2 ? 3 : (PIPE == 1 ? 2 : 1);
   static constexpr int NT = NW * 64;
@@ -80,10 +84,31 @@ struct Cfg {
   static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
 };
 
+// One wave per SIMD, 64 query rows per wave, key tiles brought into an unpadded
+// swizzled four-stage LDS ring by direct global->LDS loads (k_latent_attn_w1).
+template <int DC_, int DR_>
+struct CfgW {
+  static constexpr bool DIRECT = true;
+  static constexpr int DC = DC_, DR = DR_, QT = 2, NW = 4, WPC = 1, NBUF = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int DK = DC + DR;
+  static constexpr int KB = DK / 16;
+  static constexpr int FT = DC / 32;
+  static constexpr int RW = NW * QT * 32;
+  static constexpr int CPR = DK / 8;          // 16-byte chunks per ring row
+  static constexpr int LOADS = CPR / NW;      // 64-chunk loads per wave per key tile
+  static constexpr int STAGE = BN * DK;       // elements per LDS stage (no padding)
+  static constexpr size_t LDS = (size_t)STAGE * 2 * NBUF;
+  static constexpr size_t REC = (size_t)RW * DC * 2 + (size_t)RW * 8;
+  static constexpr int WAVES_PER_SIMD = 1;
+  static_assert(CPR % 4 == 0 && LOADS * NW * 64 == BN * CPR, "tile does not split into loads");
+  static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
+};
+
 // Production configuration per (d_c, d_rope), and the safe-path configuration.
 template <int DC, int DR>
 struct Choice {
-  using Fast = Cfg<DC, DR, 1, 8, 2, 1, 56>;
+  using Fast = CfgW<DC, DR>;
   using Safe = Cfg<DC, DR, 1, 4, 0, 1>;
 };
 
@@ -426,6 +451,313 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
   }
 }
 
+// Chunk swizzle of the unpadded key tile: 16-byte chunk c of tile row r sits at
+// chunk position c ^ swz4(r) of that row.  With it the 32-row K fragment reads and
+// the V^T transpose reads below touch every LDS bank equally often.
+__device__ __forceinline__ int swz4(int r) { return (r ^ (r >> 2)) & 3; }
+
+// Key tiles of the one-wave-per-SIMD kernel.  A tile is 64 ring rows of DK bf16,
+// unpadded and swizzled, brought in by global_load_lds_dwordx4: each load puts 64
+// lanes' 16 bytes at consecutive LDS chunk positions, so the swizzle is applied on
+// the global side (lane p of the tile fetches the chunk that belongs at position p).
+template <class C>
+struct TileW {
+  static constexpr int DK = C::DK, KB = C::KB, FT = C::FT, QT = C::QT, LOADS = C::LOADS;
+  bf16 *base;
+  const bf16 *cb;
+  int nk, start0, len0;
+  int goff[LOADS];  // element offset, within the tile's rows, of this lane's chunks
+  int dst0;         // element offset of this wave's first load in a stage
+
+  __device__ __forceinline__ void init(int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int p = (wave * LOADS + i) * 64 + lane;
+      const int r = p / C::CPR;
+      goff[i] = r * DK + (((p % C::CPR) ^ swz4(r)) * 8);
+    }
+    dst0 = wave * LOADS * 64 * 8;
+  }
+
+  __device__ __forceinline__ bf16 *Ks(int buf) const { return base + buf * C::STAGE; }
+
+  __device__ __forceinline__ int64_t key_row(int kk) const {
+    return kk < len0 ? (int64_t)(start0 + kk) : (int64_t)(kk - len0);
+  }
+
+  // Issue the loads of tile kt into stage buf (completion: vmcnt).  Keys past nk
+  // repeat key nk-1, a finite row whose probability is zero.
+  __device__ __forceinline__ void load(int kt, int buf) const {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int k0 = kt * BN;
+    bf16 *dst = Ks(buf) + dst0;
+    const bool contiguous = (k0 + BN <= nk) && (k0 + BN <= len0 || k0 >= len0);
+    if (contiguous) {
+      const bf16 *tb = cb + key_row(k0) * DK;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_global_load_lds((const void *)(tb + goff[i]),
+                                         (lds_void *)(dst + i * 512), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = goff[i] / DK;
+        const int kk = min(k0 + r, nk - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(cb + key_row(kk) * DK + (goff[i] - r * DK)),
+                                         (lds_void *)(dst + i * 512), 16, 0, 0);
+      }
+    }
+  }
+
+  // S^T of one 32-key half T of the tile for both query tiles.  K fragments run
+  // three k-blocks ahead of their MFMAs; after the MFMA of (k-block kb, query tile
+  // qt) the caller's work(2kb + qt) is emitted, each group fenced so the order
+  // stays MFMA / VALU / MFMA / VALU.
+  template <int T, class Work>
+  __device__ __forceinline__ void scores(f32x16 (&S)[QT], const bf16x8 (&Qr)[QT][KB], int buf,
+                                         int l32, int g, Work &&work) const {
+    // k-block kb is chunk 2kb + g of row T*32 + l32; the swizzle only flips the low
+    // two chunk bits, so even and odd k-blocks each have one base address.
+    const int sw = swz4(l32);
+    const bf16 *rb = Ks(buf) + (T * 32 + l32) * DK;
+    const bf16 *kr[2] = {rb + ((g ^ sw) * 8), rb + (((2 + g) ^ sw) * 8)};
+    auto kfrag = [&](int kb) { return *(const bf16x8 *)(kr[kb & 1] + (kb >> 1) * 32); };
+    constexpr int D = 3;  // fragments in flight
+    bf16x8 fr[D + 1];
+#pragma unroll
+    for (int kb = 0; kb < D; ++kb) fr[kb] = kfrag(kb);
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + D < KB) fr[(kb + D) % (D + 1)] = kfrag(kb + D);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        S[qt] = mfma32(fr[kb % (D + 1)], Qr[qt][kb], kb == 0 ? zero : S[qt]);
+        work(kb * QT + qt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // O^T += V^T P^T over the tile's four 16-key blocks (fragment mapping as in
+  // Tile::values, addresses through the swizzle).
+  __device__ __forceinline__ void values(f32x16 (&O)[FT][QT], const bf16x8 (&P)[BN / 16][QT],
+                                         int buf, int lane) const {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+    const int G = lane >> 4, r = lane & 15, g = lane >> 5;
+    const bf16 *vt[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + 4 * g + (r >> 2);
+      const int chunk = (2 * (G & 1) + ((r & 3) >> 1)) ^ swz4(row);
+      vt[h] = Ks(buf) + row * DK + chunk * 8 + (r & 1) * 4;
+    }
+#pragma unroll
+    for (int i = 0; i < FT * (BN / 16); ++i) {
+      const int off = (i % (BN / 16)) * 16 * DK + (i / (BN / 16)) * 32;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(vt[0] + off));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(vt[1] + off));
+      const bf16x8 f =
+          __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        O[i / (BN / 16)][qt] = mfma32(f, P[i % (BN / 16)][qt], O[i / (BN / 16)][qt]);
+    }
+  }
+};
+
+// Keys of half T past nk get -inf (only the window's last tile has any).
+template <int QT>
+__device__ __forceinline__ void mask_half(f32x16 (&S)[QT], int key0, int nk, int g) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (key0 + (r >> 2) * 8 + g * 4 + (r & 3) >= nk)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) S[qt][r] = -INFINITY;
+}
+
+// Softmax of one 32-key half T, split into NS slots so that it can be spread over
+// the MFMAs of another step: slot i takes elements [i*16QT/NS, (i+1)*16QT/NS),
+// element j being row j % 16 of query tile j / 16.  Block 2T + h of P takes S
+// elements 8h..8h+7 (keys T*32 + 16h + 4g + e and T*32 + 16h + 8 + 4g + e), as the
+// V^T fragments expect.  Row sums go to two partial sums per query tile.
+template <int T, int QT, int NS>
+__device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], bf16x8 (&P)[BN / 16][QT],
+                                         const float (&m)[QT], float (&ls)[QT][2]) {
+  constexpr int NE = 16 * QT;
+#pragma unroll
+  for (int j = slot * NE / NS; j < (slot + 1) * NE / NS; ++j) {
+    const int qt = j / 16, r = j % 16;
+    const float p = fast_exp2(S[qt][r] - m[qt]);
+    ls[qt][r & 1] += p;
+    P[2 * T + r / 8][qt][r % 8] = (bf16)p;
+  }
+}
+
+template <int T, int QT>
+__device__ __forceinline__ void exp_half(const f32x16 (&S)[QT], bf16x8 (&P)[BN / 16][QT],
+                                         const float (&m)[QT], float (&l)[QT]) {
+  float ls[QT][2] = {};
+  exp_slot<T, QT, 1>(0, S, P, m, ls);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding (loads
+// complete in order, so every older load has landed).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Instruction order of the value step: three V^T fragments (two reads each) in
+// flight, then per fragment its two MFMAs and the next fragment's reads.
+template <int NF>
+__device__ __forceinline__ void order_values_step() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
+// Fast latent attention, one wave per SIMD.  Each wave owns 64 query rows (two
+// 32-row MFMA tiles) whose q_lat stays in registers; O^T (DC x 64 fp32) lives in
+// the accumulation registers.  Key tile kt is handled in three steps:
+//   1. S^T of keys 0-31 of kt, beside the softmax VALU work of keys 32-63 of kt-1;
+//   2. O^T += V^T P^T of tile kt-1, then the loads of tile kt+2 are issued;
+//   3. S^T of keys 32-63 of kt, beside the softmax VALU work of keys 0-31 of kt,
+// so the wave's own MFMAs cover its exponentials.  Four LDS stages: at the end of
+// step 3 tile kt+1 has landed (tile kt+2 may still be in flight), one barrier per
+// tile.  Reference max, flags, pieces and records are as in k_latent_attn.
+template <class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
+                      bf16 *__restrict__ o, unsigned char *__restrict__ part,
+                      int *__restrict__ flags, Sched s) {
+  constexpr int DC = C::DC, QT = C::QT, KB = C::KB, FT = C::FT, RW = C::RW, NB = C::NBUF;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  TileW<C> tl;
+  tl.base = (bf16 *)lds;
+  tl.nk = s.nk;
+  tl.start0 = s.start0;
+  tl.len0 = s.len0;
+  tl.init(lane, wave);
+
+  const int wg = blockIdx.x;
+  const int64_t begin = (int64_t)wg * s.T / s.G, end = (int64_t)(wg + 1) * s.T / s.G;
+
+  bf16x8 Qr[QT][KB];
+  f32x16 O[FT][QT];
+  bf16x8 P[BN / 16][QT];
+  f32x16 S0[QT], S1[QT];
+  float m[QT], l[QT];
+
+  const int rt_first = (int)(begin / s.KT), rt_last = (int)((end - 1) / s.KT);
+  const int kt_begin = (int)(begin - (int64_t)rt_first * s.KT);
+  const int kt_end = (int)(end - (int64_t)rt_last * s.KT);
+  const int last_kt = s.KT - 1;
+  for (int rt = rt_last; rt >= rt_first; --rt) {
+    const int kt0 = rt == rt_first ? kt_begin : 0;
+    const int kt1 = rt == rt_last ? kt_end : s.KT;
+    const int b = rt / s.RTb;
+    const int row0 = (rt % s.RTb) * RW;
+    tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
+
+    tl.load(kt0, kt0 % NB);
+    load_queries<C::DK, QT, KB>(Qr, q, s, b, row0 + wave * QT * 32, l32, g);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      l[qt] = 0.f;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[ft][qt][r] = 0.f;
+    }
+    wait_loads<0>();
+    __syncthreads();
+    if (kt0 + 1 < kt1) tl.load(kt0 + 1, (kt0 + 1) % NB);
+
+    // first tile: both halves, the fixed reference max, probabilities of keys 0-31
+    tl.template scores<0>(S0, Qr, kt0 % NB, l32, g, [](int) {});
+    tl.template scores<1>(S1, Qr, kt0 % NB, l32, g, [](int) {});
+    if (kt0 == last_kt) {
+      mask_half<QT>(S0, kt0 * BN, s.nk, g);
+      mask_half<QT>(S1, kt0 * BN + 32, s.nk, g);
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[qt][r], S1[qt][r]));
+      m[qt] = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    exp_half<0, QT>(S0, P, m, l);
+    if (kt0 + 2 < kt1) {
+      tl.load(kt0 + 2, (kt0 + 2) % NB);
+      wait_loads<C::LOADS>();
+    } else {
+      wait_loads<0>();
+    }
+    __syncthreads();
+
+    for (int kt = kt0 + 1; kt < kt1; ++kt) {
+      const int cur = kt % NB, prev = (kt + NB - 1) % NB;
+      float ls[QT][2] = {};
+      tl.template scores<0>(S0, Qr, cur, l32, g,
+                            [&](int i) { exp_slot<1, QT, KB * QT>(i, S1, P, m, ls); });
+      tl.values(O, P, prev, lane);
+      order_values_step<FT * (BN / 16)>();
+      __builtin_amdgcn_sched_barrier(0);
+      const bool more = kt + 2 < kt1;
+      if (more) tl.load(kt + 2, (kt + 2) % NB);
+      if (kt == last_kt) mask_half<QT>(S0, kt * BN, s.nk, g);
+      tl.template scores<1>(S1, Qr, cur, l32, g,
+                            [&](int i) { exp_slot<0, QT, KB * QT>(i, S0, P, m, ls); });
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
+      if (kt == last_kt) mask_half<QT>(S1, kt * BN + 32, s.nk, g);
+      if (more)
+        wait_loads<C::LOADS>();
+      else
+        wait_loads<0>();
+      __syncthreads();
+    }
+    exp_half<1, QT>(S1, P, m, l);
+    tl.values(O, P, (kt1 - 1) % NB, lane);
+    __syncthreads();
+
+    const bool whole = (kt0 == 0 && kt1 == s.KT);
+    unsigned char *rec = part + (size_t)(wg + rt) * C::REC;
+    float *rec_m = (float *)(rec + (size_t)RW * DC * 2);
+    float *rec_l = rec_m + RW;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+      if (!(lt <= kFastSumLimit)) flags[rt] = 1;
+      const int lrow = wave * QT * 32 + qt * 32 + l32;
+      const int row = row0 + lrow;
+      if (row < s.R) {
+        bf16 *dst = whole ? o + ((int64_t)b * s.R + row) * DC : (bf16 *)rec + (int64_t)lrow * DC;
+        store_rows<FT, QT>(dst, O, qt, 1.0f / lt, g);
+        if (!whole && g == 0) {
+          rec_m[lrow] = m[qt];
+          rec_l[lrow] = lt;
+        }
+      }
+    }
+  }
+}
+
 // Merge the pieces of every row tile that more than one workgroup worked on.  One
 // thread per (row, 8 latent columns): it weighs each piece's normalised partial by
 // l_p * 2^(m_p - max m) and renormalises.  Workgroups of unsplit tiles exit at once.
@@ -609,19 +941,28 @@ hipError_t allow_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
+template <class F>
+auto fast_kernel() {
+  if constexpr (F::DIRECT)
+    return k_latent_attn_w1<F>;
+  else
+    return k_latent_attn<F>;
+}
+
 template <int DC, int DR>
 hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   using F = typename Choice<DC, DR>::Fast;
   using S = typename Choice<DC, DR>::Safe;
   Sched s = make_sched(a, F::RW, a.grid * F::WPC);
   if (s.T <= 0) return hipSuccess;
-  hipError_t e = allow_lds(k_latent_attn<F>, F::LDS);
+  const auto fast = fast_kernel<F>();
+  hipError_t e = allow_lds(fast, F::LDS);
   if (e == hipSuccess) e = allow_lds(k_latent_attn_safe<S>, S::LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_fill_i32, dim3((s.RT + 255) / 256), dim3(256), 0, st, a.flags, s.RT, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_latent_attn<F>, dim3(s.G), dim3(F::NT), F::LDS, st, (const bf16 *)a.q,
+  hipLaunchKernelGGL(fast, dim3(s.G), dim3(F::NT), F::LDS, st, (const bf16 *)a.q,
                      (const bf16 *)a.cache, (bf16 *)a.o, (unsigned char *)a.part, a.flags, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;

@@ -42,6 +42,8 @@ namespace mla {
 namespace {
 
 constexpr int BN = kAttnKeyTile;       // keys per tile
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: weights above it fall back
 constexpr float kSafeThreshold = 8.f;  // lazy rescale threshold of the safe kernel
 
@@ -110,6 +112,13 @@ template <int DC, int DR>
 struct Choice {
   using Fast = CfgW<DC, DR>;
   using Safe = Cfg<DC, DR, 1, 4, 0, 1>;
+};
+// At d_c = 256 the 64-row O^T alone needs all 256 accumulation registers, so the
+// one-wave kernel would spill; two waves per SIMD with 32 rows each fit.
+template <>
+struct Choice<256, 32> {
+  using Fast = Cfg<256, 32, 1, 8, 2, 1, 56>;
+  using Safe = Cfg<256, 32, 1, 4, 0, 1>;
 };
 
 // One workgroup's view of the ring: global -> registers -> LDS (one key-major tile
@@ -485,28 +494,34 @@ struct TileW {
     return kk < len0 ? (int64_t)(start0 + kk) : (int64_t)(kk - len0);
   }
 
-  // Issue the loads of tile kt into stage buf (completion: vmcnt).  Keys past nk
-  // repeat key nk-1, a finite row whose probability is zero.
-  __device__ __forceinline__ void load(int kt, int buf) const {
-    typedef __attribute__((address_space(3))) void lds_void;
+  // Loads of tile kt into stage buf: plan once, then issue the LOADS pieces one at
+  // a time (completion: vmcnt).  Keys past nk repeat key nk-1, a finite row whose
+  // probability is zero.
+  struct Plan {
+    const bf16 *tb;  // first row of a tile that is contiguous in the ring, else null
+    int k0;
+    bf16 *dst;
+  };
+  __device__ __forceinline__ Plan plan(int kt, int buf) const {
     const int k0 = kt * BN;
-    bf16 *dst = Ks(buf) + dst0;
     const bool contiguous = (k0 + BN <= nk) && (k0 + BN <= len0 || k0 >= len0);
-    if (contiguous) {
-      const bf16 *tb = cb + key_row(k0) * DK;
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)(tb + goff[i]),
-                                         (lds_void *)(dst + i * 512), 16, 0, 0);
+    return Plan{contiguous ? cb + key_row(k0) * DK : nullptr, k0, Ks(buf) + dst0};
+  }
+  __device__ __forceinline__ void issue(const Plan &pl, int i) const {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const bf16 *src;
+    if (pl.tb) {
+      src = pl.tb + goff[i];
     } else {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int r = goff[i] / DK;
-        const int kk = min(k0 + r, nk - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(cb + key_row(kk) * DK + (goff[i] - r * DK)),
-                                         (lds_void *)(dst + i * 512), 16, 0, 0);
-      }
+      const int r = goff[i] / DK;
+      src = cb + key_row(min(pl.k0 + r, nk - 1)) * DK + (goff[i] - r * DK);
     }
+    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(pl.dst + i * 512), 16, 0, 0);
+  }
+  __device__ __forceinline__ void load(int kt, int buf) const {
+    const Plan pl = plan(kt, buf);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) issue(pl, i);
   }
 
   // S^T of one 32-key half T of the tile for both query tiles.  K fragments run
@@ -541,8 +556,8 @@ struct TileW {
   }
 
   // O^T += V^T P^T over the tile's four 16-key blocks (fragment mapping as in
-  // Tile::values, addresses through the swizzle).
-  __device__ __forceinline__ void values(f32x16 (&O)[FT][QT], const bf16x8 (&P)[BN / 16][QT],
+  // Tile::values, addresses through the swizzle); P holds packed bf16 pairs.
+  __device__ __forceinline__ void values(f32x16 (&O)[FT][QT], const u32x4 (&P)[BN / 16][QT],
                                          int buf, int lane) const {
     typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -566,7 +581,8 @@ struct TileW {
           __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
-        O[i / (BN / 16)][qt] = mfma32(f, P[i % (BN / 16)][qt], O[i / (BN / 16)][qt]);
+        O[i / (BN / 16)][qt] = mfma32(f, __builtin_bit_cast(bf16x8, P[i % (BN / 16)][qt]),
+                                      O[i / (BN / 16)][qt]);
     }
   }
 };
@@ -581,29 +597,49 @@ __device__ __forceinline__ void mask_half(f32x16 (&S)[QT], int key0, int nk, int
       for (int qt = 0; qt < QT; ++qt) S[qt][r] = -INFINITY;
 }
 
+// Keeps v where the surrounding code put it: the value must exist at this point
+// and the empty statement cannot move past the scheduling fences around it, so
+// the arithmetic feeding it stays in its MFMA slot instead of being sunk towards
+// its first use.
+template <typename T>
+__device__ __forceinline__ void pin(T &v) {
+  asm volatile("" : "+v"(v));
+}
+
 // Softmax of one 32-key half T, split into NS slots so that it can be spread over
 // the MFMAs of another step: slot i takes elements [i*16QT/NS, (i+1)*16QT/NS),
 // element j being row j % 16 of query tile j / 16.  Block 2T + h of P takes S
-// elements 8h..8h+7 (keys T*32 + 16h + 4g + e and T*32 + 16h + 8 + 4g + e), as the
-// V^T fragments expect.  Row sums go to two partial sums per query tile.
+// elements 8h..8h+7 (keys T*32 + 16h + 4g + e and T*32 + 16h + 8 + 4g + e) as
+// packed bf16 pairs, as the V^T fragments expect.  Row sums go to two partial sums
+// per query tile; pend carries an even element to the slot that completes its pair.
 template <int T, int QT, int NS>
-__device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], bf16x8 (&P)[BN / 16][QT],
-                                         const float (&m)[QT], float (&ls)[QT][2]) {
+__device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], u32x4 (&P)[BN / 16][QT],
+                                         const float (&m)[QT], float (&ls)[QT][2],
+                                         float (&pend)[QT]) {
   constexpr int NE = 16 * QT;
 #pragma unroll
   for (int j = slot * NE / NS; j < (slot + 1) * NE / NS; ++j) {
     const int qt = j / 16, r = j % 16;
-    const float p = fast_exp2(S[qt][r] - m[qt]);
+    float p = fast_exp2(S[qt][r] - m[qt]);
     ls[qt][r & 1] += p;
-    P[2 * T + r / 8][qt][r % 8] = (bf16)p;
+    pin(p);
+    pin(ls[qt][r & 1]);
+    if (r & 1) {
+      bf16x2 w2 = {(bf16)pend[qt], (bf16)p};
+      unsigned w = __builtin_bit_cast(unsigned, w2);
+      pin(w);
+      P[2 * T + r / 8][qt][(r % 8) / 2] = w;
+    } else {
+      pend[qt] = p;
+    }
   }
 }
 
 template <int T, int QT>
-__device__ __forceinline__ void exp_half(const f32x16 (&S)[QT], bf16x8 (&P)[BN / 16][QT],
+__device__ __forceinline__ void exp_half(const f32x16 (&S)[QT], u32x4 (&P)[BN / 16][QT],
                                          const float (&m)[QT], float (&l)[QT]) {
-  float ls[QT][2] = {};
-  exp_slot<T, QT, 1>(0, S, P, m, ls);
+  float ls[QT][2] = {}, pend[QT];
+  exp_slot<T, QT, 1>(0, S, P, m, ls, pend);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
 }
@@ -658,9 +694,9 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
 
   bf16x8 Qr[QT][KB];
   f32x16 O[FT][QT];
-  bf16x8 P[BN / 16][QT];
+  u32x4 P[BN / 16][QT];
   f32x16 S0[QT], S1[QT];
-  float m[QT], l[QT];
+  float m[QT], l[QT], pend[QT];
 
   const int rt_first = (int)(begin / s.KT), rt_last = (int)((end - 1) / s.KT);
   const int kt_begin = (int)(begin - (int64_t)rt_first * s.KT);
@@ -714,15 +750,17 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       const int cur = kt % NB, prev = (kt + NB - 1) % NB;
       float ls[QT][2] = {};
       tl.template scores<0>(S0, Qr, cur, l32, g,
-                            [&](int i) { exp_slot<1, QT, KB * QT>(i, S1, P, m, ls); });
+                            [&](int i) { exp_slot<1, QT, KB * QT>(i, S1, P, m, ls, pend); });
       tl.values(O, P, prev, lane);
       order_values_step<FT * (BN / 16)>();
       __builtin_amdgcn_sched_barrier(0);
+      // Tile kt+2 is requested only now: the transpose reads above would otherwise
+      // make the compiler wait for these loads before the value step.
       const bool more = kt + 2 < kt1;
       if (more) tl.load(kt + 2, (kt + 2) % NB);
       if (kt == last_kt) mask_half<QT>(S0, kt * BN, s.nk, g);
       tl.template scores<1>(S1, Qr, cur, l32, g,
-                            [&](int i) { exp_slot<0, QT, KB * QT>(i, S0, P, m, ls); });
+                            [&](int i) { exp_slot<0, QT, KB * QT>(i, S0, P, m, ls, pend); });
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
       if (kt == last_kt) mask_half<QT>(S1, kt * BN + 32, s.nk, g);

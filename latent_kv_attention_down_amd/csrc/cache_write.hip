@@ -15,6 +15,22 @@ namespace {
 
 constexpr int kBM = 32;   // tokens per workgroup (bf16 path)
 
+// Cross-lane steps inside a 16-lane row with DPP (no LDS round trip): the partner
+// of lane l^1, and the sum over the row (quad swaps, then half-row and row mirrors,
+// which pair up every 4- and 8-lane group with its complement).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor1(float v) { return dpp_mov<0xB1>(v); }  // quad_perm [1,0,3,2]
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
 // Row-wise finish on an fp32 tile in LDS: tile[r * ld + c] holds the projections
 // of token m0 + r.  8 threads per row.  Results are written back into the tile.
 template <typename T>
@@ -57,27 +73,57 @@ __device__ __forceinline__ int64_t ring_row(const CacheWriteArgs &a, int m) {
 
 // bf16: the 32-token x tile stays in LDS for the whole reduction; wave w owns
 // output columns [32w, 32w+32) and streams those weight rows from global memory
-// straight into 16x16x32 MFMA B operands (lane: column l%16, 8 consecutive k),
-// PREF k-steps ahead, so the per-CU weight stream is not serialised behind one
-// load round trip per k-step.
+// straight into 16x16x32 MFMA B operands through a ring of PREF k-steps per lane
+// (each slot is refilled right after its MFMAs, so PREF steps stay in flight).
+// The first weight loads are issued before the x tile's, so the L2-resident
+// weights arrive while x comes from HBM.  The finish works on the accumulators:
+// per-token sums of squares are reduced across the 16 lanes of a column tile and
+// across waves through LDS, the RoPE pair partner is the neighbouring lane, and
+// the bf16 rows go through a small LDS tile for 16-byte ring stores.
 template <int N>
 __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteArgs a) {
   constexpr int NWAVE = N / 32;
   constexpr int NT = 64 * NWAVE;
-  constexpr int PREF = 8;  // k-steps of 32 in flight per lane
-  constexpr int LDO = N + 4;
+  // k-steps of 32 in flight per lane; nine waves (N = 288) leave fewer registers
+  constexpr int PREF = N <= 256 ? 12 : 6;
+  constexpr int LDT = N + 8; // row stride (elements) of the bf16 output tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int LDX = a.d + 8;
   bf16 *sX = (bf16 *)smem;
-  float *tile = (float *)smem;
+  bf16 *tileo = (bf16 *)smem;                            // after the reduction
+  float *ssum = (float *)(smem + kBM * LDT * 2);         // [NWAVE][kBM]
+  float *sinv = ssum + NWAVE * kBM;                      // [kBM]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kg = (lane >> 4) * 8;
   const int m0 = blockIdx.x * kBM;
+  const int nsteps = a.d / 32;
   const bf16 *X = (const bf16 *)a.x;
 
+  // this lane's two weight rows (columns n of the two 16-wide output tiles)
+  const bf16 *wrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = wave * 32 + j * 16 + l16;
+    wrow[j] = (n < a.d_c ? (const bf16 *)a.w_kv + (int64_t)n * a.d
+                         : (const bf16 *)a.w_kr + (int64_t)(n - a.d_c) * a.d) + kg;
+  }
+  // Every workgroup needs all of W.  Workgroups start the k loop at different
+  // k-steps (step st reads k-block (st + rot) mod nsteps), so at any moment they
+  // request different weight lines and the reads spread over all L2 channels
+  // instead of queueing on the few that hold one k-block.
+  const int rot = (int)((blockIdx.x * 7u) % (unsigned)nsteps);
+  auto kblk = [&](int st) { return st + rot < nsteps ? st + rot : st + rot - nsteps; };
+  bf16x8 ring[PREF][2];
+#pragma unroll
+  for (int s = 0; s < PREF; ++s)
+    if (s < nsteps)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ring[s][j] = *(const bf16x8 *)(wrow[j] + kblk(s) * 32);
+
   // x tile -> LDS (rows past the end are zero), XB loads in flight per thread
-  constexpr int XB = 16;
+  constexpr int XB = N <= 256 ? 16 : 8;
   const int cpr = a.d / 8, nchunk = kBM * cpr;
   for (int c0 = 0; c0 < nchunk; c0 += XB * NT) {
     uint4 v[XB];
@@ -93,87 +139,338 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteAr
       if (c < nchunk) *(uint4 *)(sX + (c / cpr) * LDX + (c % cpr) * 8) = v[i];
     }
   }
+  __syncthreads();
 
-  // this lane's two weight rows (columns n of the two 16-wide output tiles)
-  const bf16 *wrow[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = wave * 32 + j * 16 + l16;
-    wrow[j] = (n < a.d_c ? (const bf16 *)a.w_kv + (int64_t)n * a.d
-                         : (const bf16 *)a.w_kr + (int64_t)(n - a.d_c) * a.d) + kg;
-  }
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
-
-  auto step = [&](int k, const bf16x8 (&b)[2]) {
-    const bf16x8 a0 = *(const bf16x8 *)(sX + l16 * LDX + k + kg);
-    const bf16x8 a1 = *(const bf16x8 *)(sX + (16 + l16) * LDX + k + kg);
+  // x fragments of step st (tokens l16 and 16 + l16), read one step ahead
+  auto xfr = [&](int st, int h) {
+    return *(const bf16x8 *)(sX + (h * 16 + l16) * LDX + kblk(st) * 32 + kg);
+  };
+  auto mma = [&](const bf16x8 (&xa)[2], const bf16x8 (&w)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      acc[0][j] = mfma16(a0, b[j], acc[0][j]);
-      acc[1][j] = mfma16(a1, b[j], acc[1][j]);
+      acc[0][j] = mfma16(xa[0], w[j], acc[0][j]);
+      acc[1][j] = mfma16(xa[1], w[j], acc[1][j]);
     }
   };
-  const int nsteps = a.d / 32, nfull = nsteps / PREF;
-  bf16x8 cur[PREF][2], nxt[PREF][2];
-  if (nfull > 0) {
+  // Whole chunks of PREF steps run without branches: every step refills its ring
+  // slot (past the end with a clamped, unused k-block), so the number of loads in
+  // flight is the same on every path and each wait is for exactly the slot's load.
+  const int nfull = nsteps / PREF;
+  bf16x8 xa[2][2];
+  xa[0][0] = xfr(0, 0);
+  xa[0][1] = xfr(0, 1);
+  for (int c = 0; c < nfull * PREF; c += PREF) {
 #pragma unroll
-    for (int s = 0; s < PREF; ++s)
+    for (int s = 0; s < PREF; ++s) {
+      const int st = c + s, nx = min(st + 1, nsteps - 1);
+      xa[(s + 1) & 1][0] = xfr(nx, 0);
+      xa[(s + 1) & 1][1] = xfr(nx, 1);
+      mma(xa[s & 1], ring[s]);
+      const int kr = kblk(min(st + PREF, nsteps - 1)) * 32;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) cur[s][j] = *(const bf16x8 *)(wrow[j] + s * 32);
-  }
-  for (int c = 0; c < nfull; ++c) {
-    const int kbase = c * PREF * 32;
-    if (c + 1 < nfull) {
-#pragma unroll
-      for (int s = 0; s < PREF; ++s)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) nxt[s][j] = *(const bf16x8 *)(wrow[j] + kbase + (PREF + s) * 32);
+      for (int j = 0; j < 2; ++j) ring[s][j] = *(const bf16x8 *)(wrow[j] + kr);
     }
-#pragma unroll
-    for (int s = 0; s < PREF; ++s) step(kbase + s * 32, cur[s]);
-#pragma unroll
-    for (int s = 0; s < PREF; ++s)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) cur[s][j] = nxt[s][j];
   }
-  for (int st = nfull * PREF; st < nsteps; ++st) {  // remaining k-steps, one at a time
-    bf16x8 b[2];
+  // remaining steps (nsteps not a multiple of PREF): their weights are in the ring
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8 *)(wrow[j] + st * 32);
-    step(st * 32, b);
+  for (int s = 0; s < PREF; ++s) {
+    const int st = nfull * PREF + s;
+    if (st < nsteps) {
+      const bf16x8 xt[2] = {xfr(st, 0), xfr(st, 1)};
+      mma(xt, ring[s]);
+    }
+  }
+
+  // Lane holds column l16 of each 16x16 tile, tokens 16i + 4(lane/16) + r.
+  const bool latent = wave * 32 < a.d_c;  // d_c is a multiple of 32: whole waves
+  __syncthreads();                         // x tile no longer read
+  if (latent) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float q = row16_sum(acc[i][0][r] * acc[i][0][r] + acc[i][1][r] * acc[i][1][r]);
+        if (l16 == 0) ssum[wave * kBM + i * 16 + (lane >> 4) * 4 + r] = q;
+      }
   }
   __syncthreads();
-  // accumulators -> fp32 tile: lane holds column l16, rows 4*(lane/16)+r of each 16x16 tile
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        tile[(i * 16 + (lane >> 4) * 4 + r) * LDO + wave * 32 + j * 16 + l16] = acc[i][j][r];
+  if (tid < kBM) {
+    float q = 0.f;
+    for (int w = 0; w < a.d_c / 32; ++w) q += ssum[w * kBM + tid];
+    sinv[tid] = 1.0f / sqrtf(q / (float)a.d_c + a.eps);
+  }
   __syncthreads();
-  finish_rows<bf16>(tile, LDO, kBM, m0, a);
+
+  if (latent) {
+    const bf16 *gk = (const bf16 *)a.g_kv;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wave * 32 + j * 16 + l16;
+      const float gain = gk ? to_f32(gk[col]) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = i * 16 + (lane >> 4) * 4 + r;
+          tileo[t * LDT + col] = (bf16)(acc[i][j][r] * sinv[t] * gain);
+        }
+    }
+  } else {
+    // RoPE columns: pair p = (col - d_c)/2 holds (re, im) in lanes l16 even / odd.
+    // The wave's pairs are p0 + (0..15); each lane picks its two (axis, omega)
+    // with wave-uniform table reads.
+    const int p0 = (wave * 32 - a.d_c) / 2;
+    int ax[2] = {0, 0};
+    float om[2] = {0.f, 0.f};
+    for (int q = 0; q < 16; ++q) {
+      const int pq = p0 + q;
+      const int axq = a.rope.axis[pq];
+      const float omq = a.rope.omega[pq];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (j * 8 + (l16 >> 1) == q) {
+          ax[j] = axq;
+          om[j] = omq;
+        }
+    }
+    const bool even = (l16 & 1) == 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = i * 16 + (lane >> 4) * 4 + r, m = m0 + t, ti = m % a.T_q, n = ti % a.tpf;
+        const float pos[3] = {(float)(a.t0 + ti / a.tpf), (float)(n / a.grid_w), (float)(n % a.grid_w)};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float v = acc[i][j][r], other = dpp_xor1(v);
+          float re = even ? v : other, im = even ? other : v;
+          rope_rotate(re, im, pos[ax[j]], om[j]);
+          tileo[t * LDT + wave * 32 + j * 16 + l16] = (bf16)(even ? re : im);
+        }
+      }
+  }
   __syncthreads();
   // 16-byte stores of the finished rows into the ring
   bf16 *cache = (bf16 *)a.cache;
   for (int id = tid; id < kBM * (N / 8); id += NT) {
     const int r = id / (N / 8), c8 = (id % (N / 8)) * 8, m = m0 + r;
-    if (m >= a.M) continue;
-    bf16x8 v;
+    if (m < a.M) *(bf16x8 *)(cache + ring_row(a, m) * N + c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
+  }
+}
+
+// bf16 with direct global->LDS loads (d a multiple of 64).  Per 64-wide k chunk a
+// stage holds the 32 x rows and all N weight rows (128 bytes each), filled by
+// global_load_lds_dwordx4: wave w brings its own 32 weight rows, waves 0-3 the x
+// rows.  NS stages are in flight.  16-byte chunk c of stage row r sits at chunk
+// c ^ ((r >> 1) & 7), which keeps the 16-row fragment reads free of bank
+// conflicts; the swizzle is applied on the global side of each load.  The RoPE
+// cos/sin of the workgroup's (token, pair)s are computed by all threads while the
+// first stages are in flight.  The finish is that of k_cache_write_bf16.
+template <int N>
+struct CwDma {
+  static constexpr int NWAVE = N / 32, NT = 64 * NWAVE;
+  static constexpr int KC = 64;                         // k per stage
+  static constexpr int NS = N <= 256 ? 4 : 3;           // stages
+  static constexpr int XB = kBM * KC * 2;               // x bytes per stage
+  static constexpr int WB = N * KC * 2;                 // weight bytes per stage
+  static constexpr int SB = XB + WB;
+  static constexpr int MAX_PAIRS = 32;
+  static constexpr size_t LDS = (size_t)SB * NS + (size_t)kBM * MAX_PAIRS * 8;
+  static_assert(NWAVE >= 4, "waves 0-3 load the x rows");
+};
+
+__device__ __forceinline__ int cw_swz(int row) { return (row >> 1) & 7; }
+
+// wait until this wave's loads of the stages after the current one are all that
+// is outstanding (LPS loads per stage)
+template <int LPS>
+__device__ __forceinline__ void wait_stage(int after) {
+  if (after >= 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
+  else if (after == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int N>
+__global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArgs a) {
+  using C = CwDma<N>;
+  constexpr int NT = C::NT, KC = C::KC, NS = C::NS, NWAVE = C::NWAVE;
+  constexpr int LDT = N + 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  typedef __attribute__((address_space(3))) void lds_void;
+  float2 *rtab = (float2 *)(smem + (size_t)C::SB * NS);  // [kBM][n_pairs]: (cos, sin)
+  bf16 *tileo = (bf16 *)smem;                             // after the k loop
+  float *ssum = (float *)(smem + kBM * LDT * 2);          // [NWAVE][kBM]
+  float *sinv = ssum + NWAVE * kBM;                       // [kBM]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int m0 = blockIdx.x * kBM;
+  const int nk = a.d / KC;
+  const int np = a.d_rope / 2;
+
+  // sources of this lane's loads: load i of wave w fills stage rows 8i + lane/8 of
+  // the wave's weight rows (and, for waves 0-3, x rows 8w + lane/8), slot lane%8
+  const int slot = lane & 7, rsub = lane >> 3;
+  const bf16 *wsrc[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (bf16)tile[r * LDO + c8 + e];
-    *(bf16x8 *)(cache + ring_row(a, m) * N + c8) = v;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * i + rsub, n = wave * 32 + row;
+    const bf16 *base = n < a.d_c ? (const bf16 *)a.w_kv + (int64_t)n * a.d
+                                 : (const bf16 *)a.w_kr + (int64_t)(n - a.d_c) * a.d;
+    wsrc[i] = base + (slot ^ cw_swz(row)) * 8;
+  }
+  const bool xload = wave < 4;
+  const bf16 *xsrc = (const bf16 *)a.x;
+  if (xload) {
+    const int row = 8 * wave + rsub, gm = min(m0 + row, a.M - 1);  // rows past M: any valid row
+    xsrc += (int64_t)gm * a.d + (slot ^ cw_swz(row)) * 8;
+  }
+  auto issue = [&](int kc) {
+    unsigned char *st = smem + (size_t)(kc % NS) * C::SB;
+    const int k0 = kc * KC;
+    if (xload)
+      __builtin_amdgcn_global_load_lds((const void *)(xsrc + k0), (lds_void *)(st + wave * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void *)(wsrc[i] + k0),
+                                       (lds_void *)(st + C::XB + wave * 4096 + i * 1024), 16, 0, 0);
+  };
+#pragma unroll
+  for (int kc = 0; kc < NS - 1; ++kc)
+    if (kc < nk) issue(kc);
+
+  // RoPE table of this workgroup's tokens
+  for (int e = tid; e < kBM * np; e += NT) {
+    const int t = e / np, p = e % np, m = m0 + t, ti = m % a.T_q, n = ti % a.tpf;
+    // unrolled over the table so its scalar loads are issued together
+    int ax = 0;
+    float om = 0.f;
+#pragma unroll
+    for (int q = 0; q < C::MAX_PAIRS; ++q)
+      if (q == p) {
+        ax = a.rope.axis[q];
+        om = a.rope.omega[q];
+      }
+    const float pos = ax == 0 ? (float)(a.t0 + ti / a.tpf) : (ax == 1 ? (float)(n / a.grid_w) : (float)(n % a.grid_w));
+    float sn, cs;
+    sincosf(pos * om, &sn, &cs);
+    rtab[e] = make_float2(cs, sn);
+  }
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < nk; ++kc) {
+    const int after = min(NS - 2, nk - 1 - kc);
+    if (xload)
+      wait_stage<5>(after);
+    else
+      wait_stage<4>(after);
+    __syncthreads();
+    if (kc + NS - 1 < nk) issue(kc + NS - 1);
+    const unsigned char *st = smem + (size_t)(kc % NS) * C::SB;
+    const unsigned char *sw = st + C::XB + wave * 4096;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 xa[2], wb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * h + l16, ch = (4 * s + kg) ^ cw_swz(row);
+        xa[h] = *(const bf16x8 *)(st + row * 128 + ch * 16);
+        wb[h] = *(const bf16x8 *)(sw + row * 128 + ch * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[0][j] = mfma16(xa[0], wb[j], acc[0][j]);
+        acc[1][j] = mfma16(xa[1], wb[j], acc[1][j]);
+      }
+    }
+  }
+
+  // Lane holds column l16 of each 16x16 tile, tokens 16i + 4(lane/16) + r.
+  const bool latent = wave * 32 < a.d_c;
+  __syncthreads();  // stages no longer read
+  if (latent) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float q = row16_sum(acc[i][0][r] * acc[i][0][r] + acc[i][1][r] * acc[i][1][r]);
+        if (l16 == 0) ssum[wave * kBM + i * 16 + (lane >> 4) * 4 + r] = q;
+      }
+  }
+  __syncthreads();
+  if (tid < kBM) {
+    float q = 0.f;
+    for (int w = 0; w < a.d_c / 32; ++w) q += ssum[w * kBM + tid];
+    sinv[tid] = 1.0f / sqrtf(q / (float)a.d_c + a.eps);
+  }
+  __syncthreads();
+  if (latent) {
+    const bf16 *gk = (const bf16 *)a.g_kv;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wave * 32 + j * 16 + l16;
+      const float gain = gk ? to_f32(gk[col]) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = i * 16 + (lane >> 4) * 4 + r;
+          tileo[t * LDT + col] = (bf16)(acc[i][j][r] * sinv[t] * gain);
+        }
+    }
+  } else {
+    // RoPE columns: pair p = (col - d_c)/2 holds (re, im) in lanes l16 even / odd
+    const bool even = (l16 & 1) == 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wave * 32 + j * 16 + l16, p = (col - a.d_c) >> 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = i * 16 + (lane >> 4) * 4 + r;
+          const float v = acc[i][j][r], other = dpp_xor1(v);
+          const float re = even ? v : other, im = even ? other : v;
+          const float2 cs = rtab[t * np + p];
+          tileo[t * LDT + col] = (bf16)(even ? re * cs.x - im * cs.y : re * cs.y + im * cs.x);
+        }
+    }
+  }
+  __syncthreads();
+  bf16 *cache = (bf16 *)a.cache;
+  for (int id = tid; id < kBM * (N / 8); id += NT) {
+    const int r = id / (N / 8), c8 = (id % (N / 8)) * 8, m = m0 + r;
+    if (m < a.M) *(bf16x8 *)(cache + ring_row(a, m) * N + c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
   }
 }
 
 template <int N>
+hipError_t launch_dma(const CacheWriteArgs &a, hipStream_t st) {
+  using C = CwDma<N>;
+  hipError_t e = hipFuncSetAttribute((const void *)k_cache_write_dma<N>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cache_write_dma<N>, dim3((a.M + kBM - 1) / kBM), dim3(C::NT), C::LDS, st, a);
+  return hipGetLastError();
+}
+
+template <int N>
 hipError_t launch_bf16(const CacheWriteArgs &a, hipStream_t st) {
-  const size_t lds_x = (size_t)kBM * (a.d + 8) * 2, lds_t = (size_t)kBM * (N + 4) * 4;
+  const size_t lds_x = (size_t)kBM * (a.d + 8) * 2;
+  const size_t lds_t = (size_t)kBM * (N + 8) * 2 + (size_t)(N / 32 + 1) * kBM * 4;
   const size_t lds = lds_x > lds_t ? lds_x : lds_t;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void *)k_cache_write_bf16<N>,
@@ -213,6 +510,15 @@ __global__ __launch_bounds__(256) void k_cache_write_f32(CacheWriteArgs a) {
 
 hipError_t cache_write_bf16(const CacheWriteArgs &a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
+  if (a.d % CwDma<224>::KC == 0 && a.d_rope / 2 <= CwDma<224>::MAX_PAIRS) {
+    switch (a.d_c + a.d_rope) {
+      case 160: return launch_dma<160>(a, st);
+      case 224: return launch_dma<224>(a, st);
+      case 256: return launch_dma<256>(a, st);
+      case 288: return launch_dma<288>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.d_c + a.d_rope) {
     case 160: return launch_bf16<160>(a, st);
     case 224: return launch_bf16<224>(a, st);

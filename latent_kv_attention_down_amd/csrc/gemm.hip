@@ -1,9 +1,15 @@
 // Projection GEMMs of the MLA chunk step: C = alpha * A * B^T with both operands
 // K-contiguous (x W^T for row-major [out][in] weights).
-//  * bf16: 2x2 waves, each a (BM/2)x(BN/2) block of 32x32x16 MFMA tiles.  K tiles
-//    of BK are staged through two padded LDS stages: the next stage's global loads
-//    are issued before this stage's MFMAs and written to LDS after them, with one
-//    barrier per K tile.
+//  * bf16, direct loads (K a multiple of 32, 16-byte aligned rows): BM x BN tiles,
+//    waves of WTM x WTN built from 32x32x16 MFMAs.  KC-wide k chunks of A and B go
+//    through an NS-stage LDS ring filled by global_load_lds_dwordx4 (vector loads
+//    into registers top out near 34 GB/s per CU, the direct path near 100 GB/s for
+//    L2-resident operands).  16-byte chunk c of stage row r sits at chunk
+//    c ^ ((r >> 1) & (KC/8 - 1)), applied on the global side of each load, so the
+//    32-row fragment reads are free of bank conflicts.  Rows past M or N read a
+//    clamped valid row; their results are not stored.
+//  * bf16, register-staged: 2x2 waves, each a (BM/2)x(BN/2) block of MFMA tiles,
+//    two padded LDS stages (the fallback for other shapes).
 //  * fp32: plain 16x16 SIMT tiles (the small fp32 path).
 #include "mla_device.h"
 #include "mla_launch.h"
@@ -111,6 +117,147 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_nt(GemmArgs g) {
     }
 }
 
+template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32>
+struct GemmDma {
+  static constexpr int NW = (BM / WTM) * (BN / WTN), NT = NW * 64;
+  static constexpr int ROWB = KC * 2;                  // bytes per stage row
+  static constexpr int RPL = 1024 / ROWB;              // rows per 1 KB load
+  static constexpr int A_LOADS = BM / RPL, B_LOADS = BN / RPL;
+  static constexpr int LPW = (A_LOADS + B_LOADS) / NW;  // loads per wave per stage
+  static constexpr int SB = (BM + BN) * ROWB;          // stage bytes
+  static constexpr size_t LDS = (size_t)SB * NS;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(LPW * NW == A_LOADS + B_LOADS, "loads do not split over the waves");
+  static_assert(NS >= 2 && NS <= 4, "stage count");
+};
+
+template <int KC>
+__device__ __forceinline__ int gswz(int row) { return (row >> 1) & (KC / 8 - 1); }
+
+template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32>
+__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm_dma(GemmArgs g) {
+  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32>;
+  constexpr int TM = D::TM, TN = D::TN, LPW = D::LPW, RPL = D::RPL, CPR = KC / 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / (BN / WTN), wn = wave % (BN / WTN);
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN, b = blockIdx.z;
+  const bf16 *A = (const bf16 *)g.A + b * g.sA;
+  const bf16 *B = (const bf16 *)g.B + b * g.sB;
+
+  // this lane's source rows: load L = wave*LPW + i covers stage rows L*RPL.. of A
+  // (then of B), lane -> row lane / CPR, 16-byte slot lane % CPR
+  const bf16 *src[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int L = wave * LPW + i;
+    const bool isA = L < D::A_LOADS;
+    const int row = (isA ? L : L - D::A_LOADS) * RPL + lane / CPR;   // row within the tile
+    const int ch = (lane % CPR) ^ gswz<KC>(row);
+    if (isA)
+      src[i] = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + ch * 8;
+    else
+      src[i] = B + (int64_t)min(n0 + row, g.N - 1) * g.ldb + ch * 8;
+  }
+  auto issue = [&](int kc) {
+    unsigned char *st = smem + (size_t)(kc % NS) * D::SB;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void *)(src[i] + kc * KC),
+                                       (lds_void *)(st + (wave * LPW + i) * 1024), 16, 0, 0);
+  };
+  const int nk = g.K / KC;
+#pragma unroll
+  for (int kc = 0; kc < NS - 1; ++kc)
+    if (kc < nk) issue(kc);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int l32 = lane & 31, g8 = lane >> 5;
+  for (int kc = 0; kc < nk; ++kc) {
+    const int after = min(NS - 2, nk - 1 - kc);
+    if (after >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+    else if (after == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kc + NS - 1 < nk) issue(kc + NS - 1);
+    const unsigned char *sa = smem + (size_t)(kc % NS) * D::SB;
+    const unsigned char *sb = sa + BM * D::ROWB;
+#pragma unroll
+    for (int s = 0; s < KC / 16; ++s) {
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WTM + i * 32 + l32;
+        af[i] = *(const bf16x8 *)(sa + row * D::ROWB + ((2 * s + g8) ^ gswz<KC>(row)) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WTN + j * 32 + l32;
+        bfr[j] = *(const bf16x8 *)(sb + row * D::ROWB + ((2 * s + g8) ^ gswz<KC>(row)) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+  // acc[i][j][4q + r]: row 8q + 4*(lane/32) + r, column l32 of the 32x32 tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + l32;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + g8 * 4 + (r & 3);
+        if (row >= g.M) continue;
+        const float v = acc[i][j][r] * g.alpha;
+        if (OUT_F32)
+          ((float *)g.C)[b * g.sC + (int64_t)row * g.ldc + col] = v;
+        else
+          ((bf16 *)g.C)[b * g.sC + (int64_t)row * g.ldc + col] = (bf16)v;
+      }
+    }
+}
+
+template <int BM, int BN, int WTM, int WTN, int KC, int NS>
+hipError_t launch_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
+  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.batch);
+  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, false>;
+  const auto kern = out_f32 ? k_gemm_dma<BM, BN, WTM, WTN, KC, NS, true>
+                            : k_gemm_dma<BM, BN, WTM, WTN, KC, NS, false>;
+  if (D::LDS > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)D::LDS);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(D::NT), D::LDS, st, g);
+  return hipGetLastError();
+}
+
+template <int KC>
+hipError_t gemm_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
+  const int64_t mt128 = (g.M + 127) / 128;
+  if (g.N >= 1024) return launch_dma<256, 128, 64, 64, KC, 3>(g, out_f32, st);
+  if (g.N % 128 == 0 && mt128 * (g.N / 128) * g.batch >= 200)
+    return launch_dma<128, 128, 64, 64, KC, 4>(g, out_f32, st);
+  return launch_dma<128, 64, 64, 32, KC, 4>(g, out_f32, st);
+}
+
 __global__ __launch_bounds__(256) void k_gemm_f32_nt(GemmArgs g) {
   __shared__ float sA[16][17], sB[16][17];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -144,6 +291,10 @@ hipError_t launch_bf16(const GemmArgs &g, bool out_f32, hipStream_t st) {
 
 hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) && g.lda % 8 == 0 &&
+                       g.ldb % 8 == 0 && g.sA % 8 == 0 && g.sB % 8 == 0;
+  if (aligned && g.K > 0 && g.K % 64 == 0) return gemm_dma<64>(g, out_f32, st);
+  if (aligned && g.K > 0 && g.K % 32 == 0) return gemm_dma<32>(g, out_f32, st);
   // 128x128 tiles when N fills them and there are enough tiles for the chip
   // (two workgroups fit per CU); otherwise 64x64.
   const int64_t tiles128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch;

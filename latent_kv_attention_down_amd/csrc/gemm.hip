@@ -11,6 +11,8 @@
 //  * bf16, register-staged: 2x2 waves, each a (BM/2)x(BN/2) block of MFMA tiles,
 //    two padded LDS stages (the fallback for other shapes).
 //  * fp32: plain 16x16 SIMT tiles (the small fp32 path).
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_launch.h"
 
@@ -143,7 +145,18 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm_dma(GemmA
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / (BN / WTN), wn = wave % (BN / WTN);
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN, b = blockIdx.z;
+  // Workgroups go to the 8 XCDs round-robin by linear id.  Tiles are renumbered
+  // so that each XCD gets a contiguous run of the row-major tile order: the column
+  // tiles that share an A row block then run on one XCD and reuse its L2.
+  int m_t, n_t;
+  {
+    const int nbx = gridDim.x, total = nbx * gridDim.y, lin = blockIdx.y * nbx + blockIdx.x;
+    const int xcd = lin % 8, slot = lin / 8, q = total / 8, rem = total % 8;
+    const int t = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + slot;
+    m_t = t / nbx;
+    n_t = t % nbx;
+  }
+  const int m0 = m_t * BM, n0 = n_t * BN, b = blockIdx.z;
   const bf16 *A = (const bf16 *)g.A + b * g.sA;
   const bf16 *B = (const bf16 *)g.B + b * g.sB;
 
@@ -182,56 +195,81 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm_dma(GemmA
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int l32 = lane & 31, g8 = lane >> 5;
-  for (int kc = 0; kc < nk; ++kc) {
+  constexpr int KS = KC / 16;  // k-steps per chunk
+  // wait until stage kc has landed (every later stage may still be in flight),
+  // then make it visible to the workgroup.  This wave's own LDS reads are drained
+  // first: after the barrier another wave may refill the stage they read.
+  auto arrive = [&](int kc) {
     const int after = min(NS - 2, nk - 1 - kc);
     if (after >= 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LPW) : "memory");
     else if (after == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPW) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kc + NS - 1 < nk) issue(kc + NS - 1);
+  };
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto frags = [&](int kc, int s, int p) {
     const unsigned char *sa = smem + (size_t)(kc % NS) * D::SB;
     const unsigned char *sb = sa + BM * D::ROWB;
 #pragma unroll
-    for (int s = 0; s < KC / 16; ++s) {
-      bf16x8 af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WTM + i * 32 + l32;
+      af[p][i] = *(const bf16x8 *)(sa + row * D::ROWB + ((2 * s + g8) ^ gswz<KC>(row)) * 16);
+    }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WTM + i * 32 + l32;
-        af[i] = *(const bf16x8 *)(sa + row * D::ROWB + ((2 * s + g8) ^ gswz<KC>(row)) * 16);
-      }
+    for (int j = 0; j < TN; ++j) {
+      const int row = wn * WTN + j * 32 + l32;
+      bfr[p][j] = *(const bf16x8 *)(sb + row * D::ROWB + ((2 * s + g8) ^ gswz<KC>(row)) * 16);
+    }
+  };
+  // Fragments run one k-step ahead.  At a chunk's last k-step the next stage is
+  // awaited first: once every wave has passed that barrier it has read all of the
+  // current stage into registers, so the stage can be refilled (chunk kc + NS).
+  arrive(0);
+  if (NS - 1 < nk) issue(NS - 1);
+  frags(0, 0, 0);
+  for (int kc = 0; kc < nk; ++kc) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WTN + j * 32 + l32;
-        bfr[j] = *(const bf16x8 *)(sb + row * D::ROWB + ((2 * s + g8) ^ gswz<KC>(row)) * 16);
+    for (int s = 0; s < KS; ++s) {
+      const int p = (kc * KS + s) & 1;
+      if (s + 1 < KS) {
+        frags(kc, s + 1, p ^ 1);
+      } else if (kc + 1 < nk) {
+        arrive(kc + 1);
+        if (kc + NS < nk) issue(kc + NS);
+        frags(kc + 1, 0, p ^ 1);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[p][i], bfr[p][j], acc[i][j]);
     }
   }
 
-  // acc[i][j][4q + r]: row 8q + 4*(lane/32) + r, column l32 of the 32x32 tile
+  // Results through LDS for 16-byte stores.  acc[i][j][4q + r] is row
+  // 8q + 4*(lane/32) + r, column l32 of the 32x32 tile.
+  typedef typename std::conditional<OUT_F32, float, bf16>::type OutT;
+  constexpr int VEC = 16 / sizeof(OutT), LDC = BN + VEC;  // padded row of the tile
+  OutT *tile = (OutT *)smem;
+  __syncthreads();  // stages no longer read
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + l32;
-      if (col >= g.N) continue;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + g8 * 4 + (r & 3);
-        if (row >= g.M) continue;
-        const float v = acc[i][j][r] * g.alpha;
-        if (OUT_F32)
-          ((float *)g.C)[b * g.sC + (int64_t)row * g.ldc + col] = v;
-        else
-          ((bf16 *)g.C)[b * g.sC + (int64_t)row * g.ldc + col] = (bf16)v;
+        const int row = wm * WTM + i * 32 + (r >> 2) * 8 + g8 * 4 + (r & 3);
+        tile[row * LDC + wn * WTN + j * 32 + l32] = (OutT)(acc[i][j][r] * g.alpha);
       }
-    }
+  __syncthreads();
+  OutT *C = (OutT *)g.C + b * g.sC;
+  for (int id = tid; id < BM * (BN / VEC); id += D::NT) {
+    const int r = id / (BN / VEC), c = (id % (BN / VEC)) * VEC;
+    if (m0 + r < g.M && n0 + c < g.N)
+      *(uint4 *)(C + (int64_t)(m0 + r) * g.ldc + n0 + c) = *(const uint4 *)(tile + r * LDC + c);
+  }
 }
 
 template <int BM, int BN, int WTM, int WTN, int KC, int NS>
@@ -291,8 +329,13 @@ hipError_t launch_bf16(const GemmArgs &g, bool out_f32, hipStream_t st) {
 
 hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) && g.lda % 8 == 0 &&
-                       g.ldb % 8 == 0 && g.sA % 8 == 0 && g.sB % 8 == 0;
+  // direct loads need 16-byte aligned rows; the 16-byte tile stores need the same
+  // of C and whole 16-byte pieces of every row (N a multiple of 8 bf16 / 4 fp32)
+  const int vec = out_f32 ? 4 : 8;
+  const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) &&
+                       ((uintptr_t)g.C % 16 == 0) && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+                       g.sA % 8 == 0 && g.sB % 8 == 0 && g.ldc % vec == 0 && g.sC % vec == 0 &&
+                       g.N % vec == 0;
   if (aligned && g.K > 0 && g.K % 64 == 0) return gemm_dma<64>(g, out_f32, st);
   if (aligned && g.K > 0 && g.K % 32 == 0) return gemm_dma<32>(g, out_f32, st);
   // 128x128 tiles when N fills them and there are enough tiles for the chip

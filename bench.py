@@ -82,10 +82,10 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_src, units):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on the
+def traffic_from_profiles(kernel_src, summary):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on the
     current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "latent_attention_wan1.3b_w21_traffic.json")
+    p = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -208,8 +208,11 @@ def main():
     attn_tflops = fl["attention"] / (attn_avg * 1e-3) / 1e12
     wbytes = cache_write_bytes(s)
     write_gbs = wbytes / (write_ms * 1e-3) / 1e9
-    kernel_src = os.path.join(ROOT, "latent_kv_attention_down_amd", "csrc", "attention.hip")
-    traffic = traffic_from_profiles(kernel_src, 1)
+    csrc = os.path.join(ROOT, "latent_kv_attention_down_amd", "csrc")
+    traffic = traffic_from_profiles(os.path.join(csrc, "attention.hip"),
+                                    "latent_attention_wan1.3b_w21_traffic.json")
+    cw_traffic = traffic_from_profiles(os.path.join(csrc, "cache_write.hip"),
+                                       "cache_write_wan1.3b_w21_traffic.json")
 
     line = {
         "metric": "MLA chunk-attention TFLOP/s + cache GB/s, Wan-1.3B shape, 21-frame window",
@@ -236,11 +239,13 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "k_latent_attn (latent attention, fast path)",
+                     "kernel": "k_latent_attn_w1 (latent attention, fast path)",
                      "kernel_ms": round(attn_avg, 4)},
         "cache_write_roofline": {"bound": "hbm", "achieved": round(write_gbs, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(write_gbs / HBM_PEAK_GBS, 4),
+                                 "traffic": cw_traffic,
+                                 "kernel": "k_cache_write_dma (cache write)",
                                  "bytes_per_launch": wbytes},
     }
     if not args.no_cpu_baseline:

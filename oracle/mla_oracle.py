@@ -29,12 +29,18 @@ Readings taken where the paper is silent (same numbering as the design notes):
     window (the chunk's own frames included) is attended with no mask.
   * Ring buffer: latent frame f lives in slot f mod W (FIFO eviction of whole
     frames, App. D.4).
+  * Read-time rotation with a sink (the long-rollout cache of App. D.4-D.5, and
+    §3.2 where the cache keeps k^R unrotated): the first S frames keep slots
+    0..S-1 for good; frame f >= S lives in slot S + (f - S) mod W.  The attended
+    context is the sink frames generated so far followed by the n_valid most
+    recent frames, in that order, and its frame i takes temporal coordinate i
+    (keys and the query chunk alike); y and x stay as they are.
 """
 import numpy as np
 
 __all__ = [
     "rope_pair_split", "rope_omegas", "rope3d", "rmsnorm", "token_positions",
-    "ring_slot", "window_frames", "ring_rows_for_window", "cache_entries",
+    "ring_slot", "window_frames", "ring_rows_for_window", "context_times", "cache_entries",
     "expected_ring", "query_parts", "reconstruct_kv", "attention_unabsorbed",
     "attention_absorbed", "output_projection", "step", "cache_scalars_per_token",
     "dense_scalars_per_token",
@@ -93,35 +99,53 @@ def rmsnorm(u, g, eps):
     return u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps) * g
 
 
-def token_positions(frames, grid_h, grid_w):
+def token_positions(frames, grid_h, grid_w, times=None):
     """(t, y, x) for every token of the given latent frames, frame-major then
-    row-major (App. C.1: S = F*H*W)."""
+    row-major (App. C.1: S = F*H*W).  t is the frame's absolute index, or
+    times[frame] when a temporal coordinate per frame is given (App. D.5)."""
     pos = []
     for f in frames:
+        t = f if times is None else times[f]
         for n in range(grid_h * grid_w):
-            pos.append((f, n // grid_w, n % grid_w))
+            pos.append((t, n // grid_w, n % grid_w))
     return np.array(pos, dtype=np.int64).reshape(-1, 3)
 
 
 # ----------------------------------------------------------------- ring bookkeeping
-def ring_slot(frame, window_frames):
-    """Ring slot of an absolute latent frame: FIFO over whole frames (App. D.4)."""
-    return frame % window_frames
+def ring_slot(frame, window_frames, sink_frames=0):
+    """Ring slot of an absolute latent frame (App. D.4): FIFO over whole frames;
+    the first sink_frames frames keep their own slots and are never evicted."""
+    if frame < sink_frames:
+        return frame
+    return sink_frames + (frame - sink_frames) % window_frames
 
 
-def window_frames(t0, chunk_frames, n_valid_frames):
-    """Chronological list of frames attended once the chunk [t0, t0+C) is written."""
+def window_frames(t0, chunk_frames, n_valid_frames, sink_frames=0):
+    """Frames attended once the chunk [t0, t0+C) is written, in context order:
+    the sink frames generated so far, then the n_valid most recent frames
+    (App. D.4).  Without a sink this is the chronological window."""
     last = t0 + chunk_frames - 1
-    return list(range(last - n_valid_frames + 1, last + 1))
+    local = list(range(last - n_valid_frames + 1, last + 1))
+    if sink_frames and local and local[0] < sink_frames:
+        raise ValueError("local frames overlap the sink")
+    return list(range(min(sink_frames, last + 1))) + local
 
 
-def ring_rows_for_window(t0, chunk_frames, n_valid_frames, window_frames_, tpf):
-    """Ring rows holding the window, in chronological token order."""
+def ring_rows_for_window(t0, chunk_frames, n_valid_frames, window_frames_, tpf, sink_frames=0):
+    """Ring rows holding the attended frames, in context order."""
     rows = []
-    for f in window_frames(t0, chunk_frames, n_valid_frames):
-        base = ring_slot(f, window_frames_) * tpf
+    for f in window_frames(t0, chunk_frames, n_valid_frames, sink_frames):
+        base = ring_slot(f, window_frames_, sink_frames) * tpf
         rows.extend(range(base, base + tpf))
     return np.array(rows, dtype=np.int64)
+
+
+def context_times(frames, rope_at_read):
+    """Temporal RoPE coordinate of each attended frame: its absolute index when
+    keys are rotated as they are written; its index in the attended context when
+    the cache keeps k^R unrotated and the window is re-indexed on assembly
+    (§3.2 Eq. 5, App. D.5)."""
+    return {f: (i if rope_at_read else f) for i, f in enumerate(frames)}
 
 
 # ----------------------------------------------------------------- the layer
@@ -129,36 +153,41 @@ def _head_rows(w, h, width):
     return w[h * width:(h + 1) * width]
 
 
-def cache_entries(s, w, x, frames):
+def cache_entries(s, w, x, frames, times=None):
     """Per-token cache state (c^KV, k^R) for tokens x of the given frames.
     c = RMSNorm(W_down^KV x) (§3.1 Eq. 1, App. D.2); k^R = W_R^K x (§3.2 Eq. 5);
-    the rotated key k^rope = RoPE3D(k^R) at the token's absolute position.
-    x: (N, d).  Returns (c (N, d_c), k_r_raw (N, d_rope), k_rope (N, d_rope))."""
+    the rotated key k^rope = RoPE3D(k^R) at the token's position (absolute t, or
+    times[frame]).  x: (N, d).
+    Returns (c (N, d_c), k_r_raw (N, d_rope), k_rope (N, d_rope))."""
     x = np.asarray(x, dtype=np.float64)
     c = rmsnorm(x @ w["w_kv_down"].T, w["g_kv"], s.rms_eps)
     k_r = x @ w["w_kr"].T
     om, ax = rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
-    pos = token_positions(frames, s.grid_h, s.grid_w)
+    pos = token_positions(frames, s.grid_h, s.grid_w, times)
     return c, k_r, rope3d(k_r, pos, om, ax)
 
 
 def expected_ring(s, w, x, frames, ring=None):
     """Ring contents after writing the tokens x of the given frames.  Row
-    (f mod W)*tpf + n holds [c^KV | RoPE3D(k^R)] (keys rotated at write)."""
+    slot(f)*tpf + n holds [c^KV | RoPE3D(k^R)] when keys are rotated at write,
+    [c^KV | k^R] when they are rotated on window assembly (§3.2, App. D.4-D.5)."""
     tpf = s.tokens_per_frame
+    sink = getattr(s, "sink_frames", 0)
+    at_read = getattr(s, "rope_at_read", False)
     if ring is None:
-        ring = np.zeros((s.window_frames * tpf, s.d_c + s.d_rope))
-    c, _, k_rope = cache_entries(s, w, x, frames)
+        ring = np.zeros(((sink + s.window_frames) * tpf, s.d_c + s.d_rope))
+    c, k_r, k_rope = cache_entries(s, w, x, frames)
     for i, f in enumerate(frames):
-        base = ring_slot(f, s.window_frames) * tpf
+        base = ring_slot(f, s.window_frames, sink) * tpf
         ring[base:base + tpf, :s.d_c] = c[i * tpf:(i + 1) * tpf]
-        ring[base:base + tpf, s.d_c:] = k_rope[i * tpf:(i + 1) * tpf]
+        ring[base:base + tpf, s.d_c:] = (k_r if at_read else k_rope)[i * tpf:(i + 1) * tpf]
     return ring
 
 
-def query_parts(s, w, x, frames):
+def query_parts(s, w, x, frames, times=None):
     """Per-head queries (§3.1 Eq. 3-4, §3.2 Eq. 6): c^Q = RMSNorm(W_down^Q x),
-    q^nope_h = W_up,h^Q c^Q, q^rope_h = RoPE3D(W_R,h^Q c^Q).
+    q^nope_h = W_up,h^Q c^Q, q^rope_h = RoPE3D(W_R,h^Q c^Q) at the token's
+    position (absolute t, or times[frame] in the re-indexed context, App. D.5).
     Returns (c_q (N, d_q), q_nope (N, H, d_nope), q_rope (N, H, d_rope))."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[0]
@@ -166,7 +195,7 @@ def query_parts(s, w, x, frames):
     q_nope = (c_q @ w["w_q_up"].T).reshape(n, s.n_heads, s.d_nope)
     q_r = (c_q @ w["w_qr"].T).reshape(n, s.n_heads, s.d_rope)
     om, ax = rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
-    pos = token_positions(frames, s.grid_h, s.grid_w)[:, None, :]
+    pos = token_positions(frames, s.grid_h, s.grid_w, times)[:, None, :]
     return c_q, q_nope, rope3d(q_r, pos, om, ax)
 
 
@@ -227,16 +256,20 @@ def attention_absorbed(s, w, c_q, q_rope, c, k_rope):
 
 
 def step(s, w, x_window, window_ids, chunk_ids, query_rows=None):
-    """One chunk step for one batch element: cache entries for every window frame,
-    queries for the chunk, attention, and W_O.  x_window holds the tokens of
-    window_ids (chronological); the chunk frames are the last ones.  query_rows
+    """One chunk step for one batch element: cache entries for every attended
+    frame, queries for the chunk, attention, and W_O.  x_window holds the tokens
+    of window_ids (context order: sink frames, then the local window
+    chronologically); the chunk frames are the last ones, or all frames so far.
+    Keys and queries are rotated at absolute t, or at their frame's index in the
+    context when the shape rotates on window assembly (App. D.5).  query_rows
     optionally restricts the queries to a subset of chunk tokens (indices into
     the chunk).  Returns dict(out=(Nq, H*d_h), y=(Nq, d), c, k_rope)."""
     tpf = s.tokens_per_frame
-    c, _, k_rope = cache_entries(s, w, x_window, window_ids)
+    times = context_times(window_ids, getattr(s, "rope_at_read", False))
+    c, _, k_rope = cache_entries(s, w, x_window, window_ids, times)
     first = window_ids.index(chunk_ids[0])
     x_chunk = np.asarray(x_window[first * tpf:(first + len(chunk_ids)) * tpf], dtype=np.float64)
-    _, q_nope, q_rope = query_parts(s, w, x_chunk, chunk_ids)
+    _, q_nope, q_rope = query_parts(s, w, x_chunk, chunk_ids, times)
     if query_rows is not None:
         q_nope, q_rope = q_nope[query_rows], q_rope[query_rows]
     out = attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope)

@@ -98,9 +98,10 @@ def pin_sdpa(o, s=None):
     assert err < 1e-12, err
 
 
-def brute_force_y(s, w, x, ids, chunk_ids, token):
+def brute_force_y(s, w, x, ids, chunk_ids, token, times=None):
     """One output row of the layer with explicit scalar loops only, for tiny
-    shapes (§3.1 Eq. 1-4, §3.2 Eq. 5-6, §3.3 Eq. 7, App. D.2-D.3)."""
+    shapes (§3.1 Eq. 1-4, §3.2 Eq. 5-6, §3.3 Eq. 7, App. D.2-D.3).  times maps a
+    frame to its temporal RoPE coordinate (default: the absolute index)."""
     tpf = s.grid_h * s.grid_w
     d = s.d_model
 
@@ -121,7 +122,7 @@ def brute_force_y(s, w, x, ids, chunk_ids, token):
             pair_k.append(k)
 
     def rot(vec, f, n):
-        p = (f, n // s.grid_w, n % s.grid_w)
+        p = (f if times is None else times[f], n // s.grid_w, n % s.grid_w)
         out = list(vec)
         for m in range(len(vec) // 2):
             ang = p[pair_axis[m]] * s.rope_theta ** (-2.0 * pair_k[m] / width[pair_axis[m]])
@@ -226,7 +227,71 @@ def pin_positions(o):
     assert tuple(pos[1560]) == (6, 0, 0)
 
 
-ALL_PINS = [pin_accounting, pin_absorbed, pin_sdpa, pin_bruteforce, pin_rope, pin_positions]
+def pin_sink_context(o):
+    """Long-rollout cache of App. D.4: one sink latent frame kept for good plus the
+    six most recent frames, FIFO over whole frames.  Explicit cases, and a deque
+    simulation of a 100-frame rollout written one 3-frame chunk at a time."""
+    assert o.window_frames(238, 3, 6, sink_frames=1) == [0, 235, 236, 237, 238, 239, 240]
+    assert o.window_frames(0, 3, 2, sink_frames=1) == [0, 1, 2]
+    assert o.window_frames(18, 3, 21) == list(range(0, 21))
+    assert [o.ring_slot(f, 6, 1) for f in (0, 1, 6, 7, 12, 13)] == [0, 1, 6, 1, 6, 1]
+    assert o.ring_slot(240, 6, 1) == 6 and o.ring_slot(240, 21) == 240 % 21
+    sink, W, tpf = 1, 6, 4
+    local = collections.deque(maxlen=W)
+    slots = {}
+    for t0 in range(0, 99, 3):
+        for f in range(t0, t0 + 3):
+            slots[o.ring_slot(f, W, sink)] = f
+            if f >= sink:
+                local.append(f)
+        present = sorted(slots.values())
+        assert present == list(range(sink)) + list(local)
+        ctx = o.window_frames(t0, 3, len(local), sink_frames=sink)
+        assert ctx == list(range(sink)) + list(local)
+        rows = o.ring_rows_for_window(t0, 3, len(local), W, tpf, sink_frames=sink)
+        assert [slots[int(r) // tpf] for r in rows[::tpf]] == ctx
+
+
+def pin_read_rotation(o):
+    """Read-time rotation (§3.2: the cache keeps k^R unrotated; App. D.5: the
+    window is re-indexed to local temporal coordinates on assembly).
+    (a) Without a sink it equals rotation at write: RoPE depends on relative
+    positions only, and the re-indexing is a uniform shift.  (b) With a sink the
+    result does not depend on absolute rollout time: the same tokens at frames
+    (0 | 235..240) and (0 | 35..40) give the same outputs, while rotating at the
+    absolute positions does not.  (c) It equals scalar loops that rotate every
+    key and query at its frame's index in the context."""
+    s = small_wan(window_frames=4, n_valid_frames=4, chunk_frames=2, t0=8)
+    w, ids, x = layer_inputs(s)
+    a = o.step(s, w, x, ids, s.chunk_frame_ids)
+    b = o.step(s.with_(rope_at_read=True), w, x, ids, s.chunk_frame_ids)
+    assert np.abs(a["y"] - b["y"]).max() < 1e-12 * np.abs(a["y"]).max()
+    sr = small_wan(window_frames=3, n_valid_frames=3, chunk_frames=2, t0=38, rope_at_read=True,
+                   sink_frames=1)
+    w, ids, x = layer_inputs(sr)
+    assert ids == [0, 37, 38, 39]
+    early = sr.with_(t0=8)
+    ids_e = early.window_frame_ids
+    assert ids_e == [0, 7, 8, 9]
+    r1 = o.step(sr, w, x, ids, sr.chunk_frame_ids)
+    r2 = o.step(early, w, x, ids_e, early.chunk_frame_ids)
+    assert np.abs(r1["y"] - r2["y"]).max() < 1e-12 * np.abs(r1["y"]).max()
+    a1 = o.step(sr.with_(rope_at_read=False), w, x, ids, sr.chunk_frame_ids)
+    a2 = o.step(early.with_(rope_at_read=False), w, x, ids_e, early.chunk_frame_ids)
+    assert not np.allclose(a1["y"], a2["y"])
+    sb = tiny_brute_shape().with_(rope_at_read=True, sink_frames=1)
+    w, ids, x = layer_inputs(sb, seed=5)
+    assert ids == [0, 4, 5, 6]
+    times = {f: i for i, f in enumerate(ids)}
+    r = o.step(sb, w, x, ids, sb.chunk_frame_ids)
+    for token in (0, 5, 9, 11):
+        yb = np.array(brute_force_y(sb, w, x, ids, sb.chunk_frame_ids, token, times=times))
+        err = np.abs(yb - r["y"][token]).max() / np.abs(yb).max()
+        assert err < 1e-12, (token, err)
+
+
+ALL_PINS = [pin_accounting, pin_absorbed, pin_sdpa, pin_bruteforce, pin_rope, pin_positions,
+            pin_sink_context, pin_read_rotation]
 
 
 # ---------------------------------------------------------------- the pins as tests
@@ -389,6 +454,31 @@ def test_expected_ring_layout():
     assert ring.shape[1] == O.cache_scalars_per_token(s.d_c, s.d_rope)
 
 
+def test_sink_context_and_slots():
+    pin_sink_context(O)
+
+
+def test_read_time_rotation():
+    pin_read_rotation(O)
+
+
+def test_expected_ring_with_sink_keeps_raw_keys():
+    """With read-time rotation the ring keeps [c^KV | k^R] unrotated (§3.2); the sink
+    frame sits in slot 0 for good and later frames go FIFO over slots 1..W."""
+    s = small_wan(window_frames=3, n_valid_frames=3, chunk_frames=1, t0=8, rope_at_read=True,
+                  sink_frames=1)
+    w, ids, x = layer_inputs(s)
+    assert ids == [0, 6, 7, 8]
+    ring = O.expected_ring(s, w, x, ids)
+    c, kr_raw, _ = O.cache_entries(s, w, x, ids)
+    tpf = s.tokens_per_frame
+    assert ring.shape[0] == (1 + 3) * tpf
+    for i, f in enumerate(ids):
+        r0 = (0 if f == 0 else 1 + (f - 1) % 3) * tpf
+        assert np.array_equal(ring[r0:r0 + tpf, :s.d_c], c[i * tpf:(i + 1) * tpf])
+        assert np.array_equal(ring[r0:r0 + tpf, s.d_c:], kr_raw[i * tpf:(i + 1) * tpf])
+
+
 # ---------------------------------------------------------------- planted mistakes
 # Each mutant replaces one oracle function (module attribute, so every caller
 # inside the oracle sees it) with a plausible mistake.
@@ -435,6 +525,19 @@ def _mut_omega_lowband(d_head, pairs, theta=10000.0):
     return out, ax
 
 
+def _mut_times_absolute(frames, rope_at_read):
+    return {f: f for f in frames}
+
+
+def _mut_sink_evicted(frame, window_frames, sink_frames=0):
+    return frame % window_frames
+
+
+def _mut_sink_last(t0, chunk_frames, n_valid_frames, sink_frames=0):
+    last = t0 + chunk_frames - 1
+    return list(range(last - n_valid_frames + 1, last + 1)) + list(range(min(sink_frames, last + 1)))
+
+
 MUTANTS = {
     "rope rotation sign": dict(rope3d=_mut_rope_sign),
     "rope axis order": dict(rope3d=_mut_rope_axes),
@@ -443,6 +546,9 @@ MUTANTS = {
     "dropped RoPE score term": dict(attention_unabsorbed=_mut_drop_rope_term),
     "scale 1/sqrt(d_nope)": dict(attention_unabsorbed=_mut_scale_nope_only),
     "lowest instead of highest bands": dict(rope_omegas=_mut_omega_lowband),
+    "absolute times at read": dict(context_times=_mut_times_absolute),
+    "sink frame evicted": dict(ring_slot=_mut_sink_evicted),
+    "sink after the local frames": dict(window_frames=_mut_sink_last),
 }
 
 

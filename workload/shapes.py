@@ -29,6 +29,8 @@ class MLAShape:
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
     batch: int = 1
+    rope_at_read: bool = False # cache keeps k^R unrotated; rotation on window assembly
+    sink_frames: int = 0       # leading frames kept for good (read-time rotation only)
 
     @property
     def tokens_per_frame(self) -> int:
@@ -40,7 +42,12 @@ class MLAShape:
 
     @property
     def window_tokens(self) -> int:
-        return self.n_valid_frames * self.tokens_per_frame
+        return len(self.window_frame_ids) * self.tokens_per_frame
+
+    @property
+    def cache_frames(self) -> int:
+        """Frame slots of the ring: the sink slots plus the W local slots."""
+        return self.sink_frames + self.window_frames
 
     @property
     def chunk_frame_ids(self):
@@ -48,15 +55,18 @@ class MLAShape:
 
     @property
     def window_frame_ids(self):
+        """Attended frames in context order: the sink frames generated so far,
+        then the n_valid most recent frames (the chunk's own among them)."""
         last = self.t0 + self.chunk_frames - 1
-        return list(range(last - self.n_valid_frames + 1, last + 1))
+        sinks = list(range(min(self.sink_frames, last + 1)))
+        return sinks + list(range(last - self.n_valid_frames + 1, last + 1))
 
     def with_(self, **kw) -> "MLAShape":
         return replace(self, **kw)
 
 
 def _wan(name, d_c=192, d_rope=32, window=21, chunk=3, t0=18, n_valid=None,
-         pairs=None, dtype="bf16"):
+         pairs=None, dtype="bf16", rope_at_read=False, sink=0):
     if pairs is None:
         pairs = (6, 5, 5) if d_rope == 32 else (12, 10, 10)
     return MLAShape(name=name, d_model=1536, n_heads=12, d_head=128,
@@ -64,7 +74,7 @@ def _wan(name, d_c=192, d_rope=32, window=21, chunk=3, t0=18, n_valid=None,
                     rope_pairs=pairs, grid_h=30, grid_w=52, window_frames=window,
                     chunk_frames=chunk, t0=t0,
                     n_valid_frames=window if n_valid is None else n_valid,
-                    dtype=dtype)
+                    dtype=dtype, rope_at_read=rope_at_read, sink_frames=sink)
 
 
 SHAPES = {
@@ -84,6 +94,14 @@ SHAPES["wan1.3b-w21-t240-q1"] = _wan("wan1.3b-w21-t240-q1", window=21, chunk=1, 
 for _dc, _dr in ((128, 32), (256, 32), (192, 64)):
     SHAPES[f"wan1.3b-w21-dc{_dc}-dr{_dr}"] = _wan(f"wan1.3b-w21-dc{_dc}-dr{_dr}", d_c=_dc,
                                                   d_rope=_dr)
+
+
+# Keys kept unrotated and rotated at window-local positions on assembly (§3.2,
+# App. D.5): the 21-frame window, and the long-rollout cache of one sink frame plus
+# the six most recent frames with the chunk at frames 238-240 (App. D.4).
+SHAPES["wan1.3b-w21-read"] = _wan("wan1.3b-w21-read", rope_at_read=True)
+SHAPES["wan1.3b-sink1-w6-t240"] = _wan("wan1.3b-sink1-w6-t240", window=6, t0=238,
+                                       rope_at_read=True, sink=1)
 
 
 def shape_by_name(name: str) -> MLAShape:

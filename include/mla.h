@@ -51,6 +51,15 @@ typedef enum {
 
 typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
 
+/* Where the shared positional key k^R is rotated (§3.2 Eq. 5, App. D.5).
+ *   MLA_ROPE_AT_WRITE: rotated at the token's absolute position when it is written.
+ *   MLA_ROPE_AT_READ:  stored unrotated; when a chunk attends, the window is
+ *     assembled with window-local temporal coordinates (frame i of the attended
+ *     context -- sink frames first, then the local frames in time order -- takes
+ *     t = i) and the chunk's queries are rotated in the same frame of reference.
+ *     Needed for a sink frame (the long-rollout cache of App. D.4).              */
+typedef enum { MLA_ROPE_AT_WRITE = 0, MLA_ROPE_AT_READ = 1 } mla_rope_mode;
+
 /* Layer shape, token grid and ring geometry (VideoMLA Table 4, App. D.1-D.3). */
 typedef struct {
   int32_t d_model;       /* d: model width (1536)                                  */
@@ -66,9 +75,12 @@ typedef struct {
                          /* D_t = d_head - 2*D_y (highest bands first, §3.2)       */
   int32_t grid_h;        /* latent tokens per frame = grid_h * grid_w (30 x 52)    */
   int32_t grid_w;
-  int32_t window_frames; /* W: ring capacity in latent frames (21)                 */
+  int32_t window_frames; /* W: local ring capacity in latent frames (21, or 6)     */
   int32_t dtype;         /* mla_dtype                                              */
   float rms_eps;         /* RMSNorm epsilon (1e-6)                                 */
+  int32_t rope_mode;     /* mla_rope_mode                                          */
+  int32_t sink_frames;   /* S: leading frames kept for good (0, or 1 in App. D.4); */
+                         /* S > 0 needs MLA_ROPE_AT_READ                           */
 } mla_config;
 
 /* Weights, element type cfg->dtype, row-major [out][in] (App. D.2 shapes).      */
@@ -90,18 +102,23 @@ typedef struct {
   int32_t batch;          /* B >= 1 independent requests (separate caches)        */
   int32_t chunk_frames;   /* C: latent frames in the query chunk (3)              */
   int64_t t0;             /* absolute index of the chunk's first latent frame     */
-  int32_t n_valid_frames; /* frames attended after the chunk is written: the      */
-                          /* frames t0+C-n_valid .. t0+C-1, C <= n_valid <= W     */
+  int32_t n_valid_frames; /* local frames attended after the chunk is written:    */
+                          /* frames t0+C-n_valid .. t0+C-1, none of them a sink   */
+                          /* frame, n_valid <= W and covering every chunk frame   */
+                          /* >= S.  The sink frames written so far (f < S) are    */
+                          /* attended as well.                                    */
 } mla_chunk;
 
 /*
- * Cache layout (every entry point that takes `cache`): a ring of W latent-frame
- * slots per request, contiguous, shape (B, W * grid_h * grid_w, d_c + d_rope),
- * element type cfg->dtype.  Latent frame f occupies slot f mod W; token n of
- * the frame (row-major over the grid) is row (f mod W) * grid_h * grid_w + n,
- * holding [ c^KV (d_c) | RoPE3D(k^R) (d_rope) ] with k^R rotated at the
- * token's absolute position (t, y, x) = (f, n / grid_w, n % grid_w).
- * Only the d_c + d_rope scalars per token are stored (App. E, Eq. 13).
+ * Cache layout (every entry point that takes `cache`): S + W latent-frame slots
+ * per request, contiguous, shape (B, (S + W) * grid_h * grid_w, d_c + d_rope),
+ * element type cfg->dtype.  Frame f < S occupies slot f for good; frame f >= S
+ * occupies slot S + (f - S) mod W (FIFO over the local slots).  Token n of the
+ * frame (row-major over the grid) is row slot * grid_h * grid_w + n, holding
+ * [ c^KV (d_c) | k (d_rope) ] with k = RoPE3D(k^R) at the token's absolute
+ * position (t, y, x) = (f, n / grid_w, n % grid_w) under MLA_ROPE_AT_WRITE, or
+ * the unrotated k^R under MLA_ROPE_AT_READ.  Only the d_c + d_rope scalars per
+ * token are stored (App. E, Eq. 13).
  */
 
 /* Host-only checks of cfg and chunk (no HIP call).  MLA_OK, INVALID_ARG or
@@ -114,18 +131,20 @@ int mla_validate(const mla_config *cfg, const mla_chunk *chunk);
  * problem; 0 if cfg/chunk are invalid.  Host-only. */
 size_t mla_workspace_bytes(const mla_config *cfg, const mla_chunk *chunk);
 
-/* Bytes of the ring cache for `batch` requests: batch * W * tokens_per_frame *
- * (d_c + d_rope) * element size.  0 if cfg is invalid.  Host-only. */
+/* Bytes of the ring cache for `batch` requests: batch * (S + W) *
+ * tokens_per_frame * (d_c + d_rope) * element size.  0 if cfg is invalid.
+ * Host-only. */
 size_t mla_cache_bytes(const mla_config *cfg, int32_t batch);
 
 /*
  * Cache write (§3.1 Eq. 1, App. D.2 RMSNorm, §3.2 Eq. 5, App. D.4 FIFO).
  *   x     (B, C * grid_h * grid_w, d) tokens of frames t0 .. t0+C-1, in order.
- *   cache ring described above; rows of slots (t0 .. t0+C-1) mod W are
- *         overwritten, evicting the frames that held them; nothing else is
- *         touched.
+ *   cache ring described above; the rows of the slots of frames t0 .. t0+C-1
+ *         are overwritten, evicting the frames that held them; nothing else is
+ *         touched.  Only batch, chunk_frames and t0 of `chunk` are used; the
+ *         chunk's frames >= S must fit the W local slots.
  * One fused kernel: [W^KV_down; W^K_R] x, RMSNorm of the latent, rotation of
- * k^R, rounding to cfg->dtype and the ring store.
+ * k^R (MLA_ROPE_AT_WRITE only), rounding to cfg->dtype and the ring store.
  */
 int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
                     const void *x, void *cache, void *stream);
@@ -139,6 +158,8 @@ int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk
  *             concatenated over heads (before W_O).
  *   workspace device scratch of at least mla_workspace_bytes(cfg, chunk).
  * Every query attends to every valid cached token (no mask inside the window).
+ * Under MLA_ROPE_AT_READ the attended frames are first gathered into the
+ * workspace in context order with k^R rotated at window-local positions.
  */
 int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
                         const void *x, const void *cache, void *out_heads,
@@ -163,6 +184,8 @@ int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk
  *   o_lat  (B, C*tpf*n_h, d_c) cfg->dtype: sum_j a_j c_j with a the softmax over
  *          the window of the scores q_lat . [c_j | k_rope_j] (base-2 logits).
  *   workspace  at least mla_workspace_bytes(cfg, chunk) bytes.
+ * Needs MLA_ROPE_AT_WRITE and S = 0 (MLA_ERR_UNSUPPORTED otherwise): the cache is
+ * attended as stored.
  */
 int mla_latent_attention(const mla_config *cfg, const mla_chunk *chunk, const void *q_lat,
                          const void *cache, void *o_lat, void *workspace, size_t ws_bytes,

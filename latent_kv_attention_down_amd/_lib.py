@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED = 0, -1, -2
 MLA_ERR_ALIGNMENT, MLA_ERR_WORKSPACE, MLA_ERR_HIP = -3, -4, -5
 MLA_BF16, MLA_F32 = 0, 1
+MLA_ROPE_AT_WRITE, MLA_ROPE_AT_READ = 0, 1
 
 # Every function include/mla.h declares, with (restype, argtypes).
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -23,7 +24,8 @@ class Config(ctypes.Structure):
     _fields_ = [("d_model", _i32), ("n_heads", _i32), ("d_head", _i32), ("d_nope", _i32),
                 ("d_rope", _i32), ("d_c", _i32), ("d_q", _i32), ("rope_pairs", _i32 * 3),
                 ("rope_theta", ctypes.c_float), ("grid_h", _i32), ("grid_w", _i32),
-                ("window_frames", _i32), ("dtype", _i32), ("rms_eps", ctypes.c_float)]
+                ("window_frames", _i32), ("dtype", _i32), ("rms_eps", ctypes.c_float),
+                ("rope_mode", _i32), ("sink_frames", _i32)]
 
 
 class Weights(ctypes.Structure):
@@ -97,6 +99,8 @@ def make_config(shape, dtype=None):
     c.rope_theta = float(shape.rope_theta)
     c.rms_eps = float(shape.rms_eps)
     c.dtype = MLA_BF16 if dt == "bf16" else MLA_F32
+    c.rope_mode = MLA_ROPE_AT_READ if getattr(shape, "rope_at_read", False) else MLA_ROPE_AT_WRITE
+    c.sink_frames = int(getattr(shape, "sink_frames", 0))
     return c
 
 

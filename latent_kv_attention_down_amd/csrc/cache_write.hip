@@ -54,6 +54,7 @@ __device__ void finish_rows(float *tile, int ld, int rows, int m0, const CacheWr
     float gain = g ? to_f32(g[c]) : 1.0f;
     tile[r * ld + c] = tile[r * ld + c] * inv * gain;
   }
+  if (!a.rotate) return;
   const int m = m0 + r, i = m % a.T_q, n = i % a.tpf;
   const float pos[3] = {(float)(a.t0 + i / a.tpf), (float)(n / a.grid_w), (float)(n % a.grid_w)};
   for (int p = sub; p < a.rope.n_pairs; p += 8) {
@@ -68,7 +69,8 @@ __device__ void finish_rows(float *tile, int ld, int rows, int m0, const CacheWr
 __device__ __forceinline__ int64_t ring_row(const CacheWriteArgs &a, int m) {
   const int b = m / a.T_q, i = m % a.T_q;
   const int64_t f = a.t0 + i / a.tpf;
-  return (int64_t)b * a.cache_batch_rows + (f % a.W) * a.tpf + (i % a.tpf);
+  const int64_t slot = f < a.S ? f : a.S + (f - a.S) % a.W;
+  return (int64_t)b * a.cache_batch_rows + slot * a.tpf + (i % a.tpf);
 }
 
 // bf16: the 32-token x tile stays in LDS for the whole reduction; wave w owns
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteAr
         for (int j = 0; j < 2; ++j) {
           const float v = acc[i][j][r], other = dpp_xor1(v);
           float re = even ? v : other, im = even ? other : v;
-          rope_rotate(re, im, pos[ax[j]], om[j]);
+          if (a.rotate) rope_rotate(re, im, pos[ax[j]], om[j]);
           tileo[t * LDT + wave * 32 + j * 16 + l16] = (bf16)(even ? re : im);
         }
       }
@@ -348,8 +350,8 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArg
   for (int kc = 0; kc < NS - 1; ++kc)
     if (kc < nk) issue(kc);
 
-  // RoPE table of this workgroup's tokens
-  for (int e = tid; e < kBM * np; e += NT) {
+  // RoPE table of this workgroup's tokens (keys kept unrotated need none)
+  for (int e = tid; a.rotate && e < kBM * np; e += NT) {
     const int t = e / np, p = e % np, m = m0 + t, ti = m % a.T_q, n = ti % a.tpf;
     // unrolled over the table so its scalar loads are issued together
     int ax = 0;
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArg
           const int t = i * 16 + (lane >> 4) * 4 + r;
           const float v = acc[i][j][r], other = dpp_xor1(v);
           const float re = even ? v : other, im = even ? other : v;
-          const float2 cs = rtab[t * np + p];
+          const float2 cs = a.rotate ? rtab[t * np + p] : make_float2(1.f, 0.f);
           tileo[t * LDT + col] = (bf16)(even ? re * cs.x - im * cs.y : re * cs.y + im * cs.x);
         }
     }

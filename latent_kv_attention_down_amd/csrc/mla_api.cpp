@@ -30,17 +30,27 @@ int fail(int status, const std::string &msg) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+#define MLA_TRY_LOCAL(expr)      \
+  do {                           \
+    int s_ = (expr);             \
+    if (s_ != MLA_OK) return s_; \
+  } while (0)
+
 // Shapes derived from the config and chunk.
 struct Dims {
-  int64_t tpf;       // tokens per latent frame
-  int64_t T_q;       // chunk tokens per request
-  int64_t M;         // B * T_q
-  int64_t R;         // rows per request = T_q * n_h
-  int64_t DK;        // d_c + d_rope
-  int64_t ring;      // W * tpf rows per request
-  int64_t nk;        // valid keys
-  int64_t start0;    // first contiguous ring range of the window
-  int64_t len0;
+  int64_t tpf;          // tokens per latent frame
+  int64_t T_q;          // chunk tokens per request
+  int64_t M;            // B * T_q
+  int64_t R;            // rows per request = T_q * n_h
+  int64_t DK;           // d_c + d_rope
+  int64_t ring;         // (S + W) * tpf cache rows per request
+  int64_t n_sink;       // sink frames attended (those written so far)
+  int64_t first_local;  // first local frame attended
+  int64_t nk;           // attended keys: (n_sink + n_valid) * tpf
+  bool at_read;         // keys rotated on window assembly
+  int64_t start0;       // rotate-at-write: the window as (up to) two ring ranges,
+  int64_t len0;         // [start0, start0 + len0) then [0, nk - len0)
+  int64_t t0_q;         // temporal coordinate of the chunk's first frame for queries
   size_t esz;
 };
 
@@ -51,14 +61,26 @@ Dims dims(const mla_config &c, const mla_chunk &k) {
   d.M = (int64_t)k.batch * d.T_q;
   d.R = d.T_q * c.n_heads;
   d.DK = (int64_t)c.d_c + c.d_rope;
-  d.ring = (int64_t)c.window_frames * d.tpf;
-  d.nk = (int64_t)k.n_valid_frames * d.tpf;
+  const int64_t S = c.sink_frames;
+  d.ring = (S + c.window_frames) * d.tpf;
   const int64_t last = k.t0 + k.chunk_frames - 1;
-  const int64_t first = last - k.n_valid_frames + 1;
-  const int64_t slot0 = first % c.window_frames;
-  const int64_t run = std::min<int64_t>(k.n_valid_frames, c.window_frames - slot0);
-  d.start0 = slot0 * d.tpf;
-  d.len0 = run * d.tpf;
+  d.n_sink = std::min<int64_t>(S, last + 1);
+  d.first_local = last - k.n_valid_frames + 1;
+  d.nk = (d.n_sink + k.n_valid_frames) * d.tpf;
+  d.at_read = c.rope_mode == MLA_ROPE_AT_READ;
+  if (d.at_read) {
+    // the assembled window is one contiguous range in context order; frame i of
+    // the context has temporal coordinate i, and the chunk's frames are consecutive
+    d.start0 = 0;
+    d.len0 = d.nk;
+    d.t0_q = k.t0 < S ? k.t0 : d.n_sink + (k.t0 - d.first_local);
+  } else {  // S == 0
+    const int64_t slot0 = d.first_local % c.window_frames;
+    const int64_t run = std::min<int64_t>(k.n_valid_frames, c.window_frames - slot0);
+    d.start0 = slot0 * d.tpf;
+    d.len0 = run * d.tpf;
+    d.t0_q = k.t0;
+  }
   d.esz = c.dtype == MLA_BF16 ? 2 : 4;
   return d;
 }
@@ -83,7 +105,12 @@ int validate_config(const mla_config *c) {
   if (c->grid_h <= 0 || c->grid_w <= 0) return fail(MLA_ERR_INVALID_ARG, "grid must be positive");
   if (c->window_frames <= 0) return fail(MLA_ERR_INVALID_ARG, "window_frames must be positive");
   if (c->dtype != MLA_BF16 && c->dtype != MLA_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype");
-  const int64_t ring = (int64_t)c->window_frames * c->grid_h * c->grid_w;
+  if (c->rope_mode != MLA_ROPE_AT_WRITE && c->rope_mode != MLA_ROPE_AT_READ)
+    return fail(MLA_ERR_INVALID_ARG, "unknown rope_mode");
+  if (c->sink_frames < 0) return fail(MLA_ERR_INVALID_ARG, "sink_frames must be >= 0");
+  if (c->sink_frames > 0 && c->rope_mode != MLA_ROPE_AT_READ)
+    return fail(MLA_ERR_INVALID_ARG, "sink frames need MLA_ROPE_AT_READ (window-local re-indexing)");
+  const int64_t ring = ((int64_t)c->sink_frames + c->window_frames) * c->grid_h * c->grid_w;
   if (ring >= (int64_t)1 << 30) return fail(MLA_ERR_INVALID_ARG, "ring too large");
   if (c->dtype == MLA_BF16) {
     if (c->d_model % 32 || c->d_q % 32 || c->d_c % 32 || c->d_nope % 32 ||
@@ -100,19 +127,37 @@ int validate_config(const mla_config *c) {
   return MLA_OK;
 }
 
-int validate_chunk(const mla_config *c, const mla_chunk *k) {
+// Chunk frames at or after the sink: they need local slots.
+int64_t local_chunk_frames(const mla_config *c, const mla_chunk *k) {
+  const int64_t end = k->t0 + k->chunk_frames;
+  return std::max<int64_t>(0, end - std::max<int64_t>(k->t0, c->sink_frames));
+}
+
+// Checks every entry point needs: the chunk itself and its place in the ring.
+int validate_chunk_write(const mla_config *c, const mla_chunk *k) {
   if (!k) return fail(MLA_ERR_INVALID_ARG, "chunk is NULL");
   if (k->batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
   if (k->chunk_frames <= 0) return fail(MLA_ERR_INVALID_ARG, "chunk_frames must be >= 1");
-  if (k->chunk_frames > c->window_frames)
-    return fail(MLA_ERR_INVALID_ARG, "chunk_frames must be <= window_frames");
   if (k->t0 < 0) return fail(MLA_ERR_INVALID_ARG, "t0 must be >= 0");
-  if (k->n_valid_frames < k->chunk_frames || k->n_valid_frames > c->window_frames)
-    return fail(MLA_ERR_INVALID_ARG, "need chunk_frames <= n_valid_frames <= window_frames");
-  if (k->n_valid_frames > k->t0 + k->chunk_frames)
-    return fail(MLA_ERR_INVALID_ARG, "window reaches before frame 0");
+  if (local_chunk_frames(c, k) > c->window_frames)
+    return fail(MLA_ERR_INVALID_ARG, "chunk_frames must fit the window_frames local slots");
   const int64_t rows = (int64_t)k->batch * k->chunk_frames * c->grid_h * c->grid_w * c->n_heads;
   if (rows >= (int64_t)1 << 30) return fail(MLA_ERR_INVALID_ARG, "chunk too large");
+  return MLA_OK;
+}
+
+// Attention also needs the window: n_valid local frames ending at the chunk's
+// last frame, covering every chunk frame that is not a sink, none of them a sink.
+int validate_chunk(const mla_config *c, const mla_chunk *k) {
+  MLA_TRY_LOCAL(validate_chunk_write(c, k));
+  const int64_t need = local_chunk_frames(c, k);
+  if (k->n_valid_frames < need || k->n_valid_frames > c->window_frames)
+    return fail(MLA_ERR_INVALID_ARG,
+                "need (chunk frames at or after the sink) <= n_valid_frames <= window_frames");
+  if (k->n_valid_frames > 0 &&
+      k->t0 + k->chunk_frames - k->n_valid_frames < (int64_t)c->sink_frames)
+    return fail(MLA_ERR_INVALID_ARG, c->sink_frames ? "local window reaches into the sink frames"
+                                                    : "window reaches before frame 0");
   return MLA_OK;
 }
 
@@ -168,7 +213,7 @@ int attn_grid_cus() {
 
 // Workspace carving (offsets in bytes, each 256-aligned).
 struct Workspace {
-  size_t u_q, c_q, q_nope, q_r, w_t, q_lat, o_lat, part, flags, out_heads, total;
+  size_t u_q, c_q, q_nope, q_r, w_t, q_lat, o_lat, part, flags, out_heads, win, total;
 };
 
 Workspace carve(const mla_config &c, const mla_chunk &k) {
@@ -199,6 +244,8 @@ Workspace carve(const mla_config &c, const mla_chunk &k) {
   w.part = take(part);
   w.flags = take(flags);
   w.out_heads = take((size_t)d.M * c.n_heads * c.d_head * d.esz);
+  // read-time rotation: the attended frames gathered in context order, rotated
+  w.win = take(d.at_read ? (size_t)k.batch * d.nk * d.DK * d.esz : 0);
   w.total = off;
   return w;
 }
@@ -230,6 +277,8 @@ int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &
   a.tpf = (int)d.tpf;
   a.grid_w = c.grid_w;
   a.W = c.window_frames;
+  a.S = c.sink_frames;
+  a.rotate = d.at_read ? 0 : 1;
   a.t0 = k.t0;
   a.cache_batch_rows = d.ring;
   a.eps = c.rms_eps;
@@ -241,13 +290,15 @@ int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &
   return MLA_OK;
 }
 
+// Latent attention over `keys`: the ring itself (rotate-at-write), or the window
+// assembled in context order in the workspace (read-time rotation).
 int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_lat,
-                         const void *cache, void *o_lat, unsigned char *ws, hipStream_t st) {
+                         const void *keys, void *o_lat, unsigned char *ws, hipStream_t st) {
   const Dims d = dims(c, k);
   const Workspace L = carve(c, k);
   mla::AttnArgs a;
   a.q = q_lat;
-  a.cache = cache;
+  a.cache = keys;
   a.o = o_lat;
   a.part = ws + L.part;
   a.flags = (int *)(ws + L.flags);
@@ -255,7 +306,7 @@ int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_
   a.R = (int)d.R;
   a.DC = c.d_c;
   a.DR = c.d_rope;
-  a.cache_rows = d.ring;
+  a.cache_rows = d.at_read ? d.nk : d.ring;
   a.nk = (int)d.nk;
   a.start0 = (int)d.start0;
   a.len0 = (int)d.len0;
@@ -345,12 +396,34 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
   rq.d_c = c.d_c;
   rq.tpf = (int)d.tpf;
   rq.grid_w = c.grid_w;
-  rq.t0 = k.t0;
+  rq.t0 = d.t0_q;  // absolute, or the chunk's place in the re-indexed context (App. D.5)
   rq.scale = scale;
   rq.rope = rope_table(c);
   MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
+  // read-time rotation: gather the sink and local frames in context order and
+  // rotate k^R at window-local positions (§3.2 Eq. 5, App. D.4-D.5)
+  const void *keys = cache;
+  if (d.at_read) {
+    mla::AssembleArgs wa;
+    wa.cache = cache;
+    wa.win = ws + L.win;
+    wa.B = k.batch;
+    wa.tpf = (int)d.tpf;
+    wa.grid_w = c.grid_w;
+    wa.d_c = c.d_c;
+    wa.d_rope = c.d_rope;
+    wa.ring = d.ring;
+    wa.nk = d.nk;
+    wa.S = c.sink_frames;
+    wa.W = c.window_frames;
+    wa.n_sink = (int)d.n_sink;
+    wa.first_local = d.first_local;
+    wa.rope = rope_table(c);
+    MLA_HIP(mla::assemble_window(wa, bf, st), "window assembly");
+    keys = ws + L.win;
+  }
   // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16)
-  MLA_TRY(run_latent_attention(c, k, q_lat, cache, o_lat, ws, st));
+  MLA_TRY(run_latent_attention(c, k, q_lat, keys, o_lat, ws, st));
   // o_h = W^V_up,h O_lat,h  (Eq. 2)
   MLA_TRY(run_gemm(c, gemm(o_lat, (int64_t)nh * c.d_c, c.d_c, w.w_v_up, c.d_c,
                            (int64_t)c.d_head * c.d_c, out_heads, (int64_t)nh * c.d_head, c.d_head,
@@ -384,14 +457,15 @@ size_t mla_workspace_bytes(const mla_config *cfg, const mla_chunk *chunk) {
 size_t mla_cache_bytes(const mla_config *cfg, int32_t batch) {
   if (validate_config(cfg) != MLA_OK || batch <= 0) return 0;
   const size_t esz = cfg->dtype == MLA_BF16 ? 2 : 4;
-  return (size_t)batch * cfg->window_frames * cfg->grid_h * cfg->grid_w *
-         (size_t)(cfg->d_c + cfg->d_rope) * esz;
+  return (size_t)batch * ((size_t)cfg->sink_frames + cfg->window_frames) * cfg->grid_h *
+         cfg->grid_w * (size_t)(cfg->d_c + cfg->d_rope) * esz;
 }
 
 int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
                     const void *x, void *cache, void *stream) {
   g_last_error.clear();
-  MLA_TRY(validate(cfg, chunk));
+  MLA_TRY(validate_config(cfg));
+  MLA_TRY(validate_chunk_write(cfg, chunk));
   MLA_TRY(validate_weights(*cfg, w, true, false, false));
   if (!x || !cache) return fail(MLA_ERR_INVALID_ARG, "x or cache is NULL");
   if (!aligned16(x) || !aligned16(cache)) return fail(MLA_ERR_ALIGNMENT, "x and cache must be 16-byte aligned");
@@ -442,6 +516,9 @@ int mla_latent_attention(const mla_config *cfg, const mla_chunk *chunk, const vo
                          void *stream) {
   g_last_error.clear();
   MLA_TRY(validate(cfg, chunk));
+  if (cfg->rope_mode != MLA_ROPE_AT_WRITE || cfg->sink_frames != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_latent_attention attends the cache as stored: "
+                                     "needs MLA_ROPE_AT_WRITE and no sink");
   if (!q_lat || !cache || !o_lat) return fail(MLA_ERR_INVALID_ARG, "q_lat, cache or o_lat is NULL");
   if (!aligned16(q_lat) || !aligned16(cache) || !aligned16(o_lat))
     return fail(MLA_ERR_ALIGNMENT, "q_lat, cache and o_lat must be 16-byte aligned");

@@ -29,8 +29,10 @@ struct CacheWriteArgs {
   int M;          // B * tokens in the chunk
   int T_q;        // tokens in the chunk per request
   int d, d_c, d_rope, tpf, grid_w, W;
+  int S;                     // sink frames: frame f < S in slot f, else S + (f - S) mod W
+  int rotate;                // 1: rotate k^R at the absolute position; 0: store it as is
   int64_t t0;
-  int64_t cache_batch_rows;  // W * tpf
+  int64_t cache_batch_rows;  // (S + W) * tpf
   float eps;
   RopeTable rope;
 };
@@ -51,6 +53,20 @@ struct RopeQArgs {
   RopeTable rope;
 };
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st);
+
+// Window assembly for read-time rotation: context frame i (the n_sink sink frames,
+// then frames first_local, first_local+1, ...) is copied from its ring slot to rows
+// i*tpf .. of `win`, with the d_rope positional columns rotated at (i, y, x).
+struct AssembleArgs {
+  const void *cache;  // (B, ring, d_c + d_rope)
+  void *win;          // (B, nk, d_c + d_rope)
+  int B, tpf, grid_w, d_c, d_rope;
+  int64_t ring, nk;
+  int S, W, n_sink;
+  int64_t first_local;
+  RopeTable rope;
+};
+hipError_t assemble_window(const AssembleArgs &a, bool bf16, hipStream_t st);
 
 // w_t[h][c][n] = w_k_up[h*d_nope + n][c]  (per-head transpose, element size esz).
 hipError_t transpose_heads(const void *w, void *w_t, int n_h, int d_nope, int d_c, int esz,

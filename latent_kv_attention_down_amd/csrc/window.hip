@@ -1,0 +1,87 @@
+// Window assembly for read-time rotation of the shared positional key (VideoMLA
+// §3.2 Eq. 5: the cache keeps k^R unrotated; App. D.4-D.5: the attended context
+// is the sink frame(s) plus the most recent local frames, re-indexed to local
+// temporal coordinates).  Context frame i -- sink frames first, then the local
+// frames in time order -- is copied from its ring slot into rows i*tpf .. of a
+// contiguous window, and its d_rope positional columns are rotated by 3D-RoPE at
+// (i, y, x).  The latent columns are copied unchanged.  The attention kernels then
+// read the window as one contiguous range.
+#include "mla_device.h"
+#include "mla_launch.h"
+
+namespace mla {
+namespace {
+
+__device__ __forceinline__ int64_t source_row(const AssembleArgs &a, int b, int64_t j) {
+  const int64_t i = j / a.tpf, n = j % a.tpf;
+  const int64_t f = i < a.n_sink ? i : a.first_local + (i - a.n_sink);
+  const int64_t slot = f < a.S ? f : a.S + (f - a.S) % a.W;
+  return (int64_t)b * a.ring + slot * a.tpf + n;
+}
+
+// bf16: one thread per 16 bytes (8 columns) of a window row.  d_c is a multiple
+// of 8, so a piece is either latent (copied) or four RoPE pairs (rotated).
+__global__ __launch_bounds__(256) void k_assemble_bf16(AssembleArgs a) {
+  const int DK = a.d_c + a.d_rope, CPR = DK / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.nk * CPR;
+  if (idx >= total) return;
+  const int ch = (int)(idx % CPR);
+  const int64_t bj = idx / CPR;
+  const int b = (int)(bj / a.nk);
+  const int64_t j = bj % a.nk;
+  const bf16x8 v = *(const bf16x8 *)((const bf16 *)a.cache + source_row(a, b, j) * DK + ch * 8);
+  bf16x8 out = v;
+  if (ch * 8 >= a.d_c) {
+    const int64_t i = j / a.tpf, n = j % a.tpf;
+    const float pos[3] = {(float)i, (float)(n / a.grid_w), (float)(n % a.grid_w)};
+    const int p0 = (ch * 8 - a.d_c) / 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float re = (float)v[2 * q], im = (float)v[2 * q + 1];
+      rope_rotate(re, im, pos[a.rope.axis[p0 + q]], a.rope.omega[p0 + q]);
+      out[2 * q] = (bf16)re;
+      out[2 * q + 1] = (bf16)im;
+    }
+  }
+  *(bf16x8 *)((bf16 *)a.win + ((int64_t)b * a.nk + j) * DK + ch * 8) = out;
+}
+
+// fp32: one thread per element.
+__global__ __launch_bounds__(256) void k_assemble_f32(AssembleArgs a) {
+  const int DK = a.d_c + a.d_rope;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.nk * DK;
+  if (idx >= total) return;
+  const int c = (int)(idx % DK);
+  const int64_t bj = idx / DK;
+  const int b = (int)(bj / a.nk);
+  const int64_t j = bj % a.nk;
+  const float *src = (const float *)a.cache + source_row(a, b, j) * DK;
+  float v = src[c];
+  if (c >= a.d_c) {
+    const int p = (c - a.d_c) / 2, e = (c - a.d_c) % 2;
+    const int64_t i = j / a.tpf, n = j % a.tpf;
+    const float pos[3] = {(float)i, (float)(n / a.grid_w), (float)(n % a.grid_w)};
+    float re = src[a.d_c + 2 * p], im = src[a.d_c + 2 * p + 1];
+    rope_rotate(re, im, pos[a.rope.axis[p]], a.rope.omega[p]);
+    v = e == 0 ? re : im;
+  }
+  ((float *)a.win)[((int64_t)b * a.nk + j) * DK + c] = v;
+}
+
+}  // namespace
+
+hipError_t assemble_window(const AssembleArgs &a, bool bf16_io, hipStream_t st) {
+  const int DK = a.d_c + a.d_rope;
+  const int64_t total = (int64_t)a.B * a.nk * (bf16_io ? DK / 8 : DK);
+  if (total <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (bf16_io)
+    hipLaunchKernelGGL(k_assemble_bf16, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_assemble_f32, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -37,7 +37,8 @@ class DeviceLayer:
         self.weights = _lib.make_weights(self.tensors)
         self.batch = batch
         tpf = shape.grid_h * shape.grid_w
-        self.cache = torch.zeros((batch, shape.window_frames * tpf, shape.d_c + shape.d_rope),
+        frames = getattr(shape, "sink_frames", 0) + shape.window_frames
+        self.cache = torch.zeros((batch, frames * tpf, shape.d_c + shape.d_rope),
                                  dtype=self.tdtype, device=device)
         assert self.cache.numel() * self.cache.element_size() == _lib.cache_bytes(self.cfg, batch)
         self._ws = None

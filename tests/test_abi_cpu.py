@@ -52,7 +52,8 @@ def chunk_of(s, **kw):
 
 @pytest.mark.parametrize("name", ["tiny-f32", "wan1.3b-w21", "wan1.3b-w42-t240",
                                   "wan1.3b-w21-t240-q1", "wan1.3b-w21-dc128-dr32",
-                                  "wan1.3b-w21-dc256-dr32", "wan1.3b-w21-dc192-dr64"])
+                                  "wan1.3b-w21-dc256-dr32", "wan1.3b-w21-dc192-dr64",
+                                  "wan1.3b-w21-read", "wan1.3b-sink1-w6-t240"])
 def test_workload_shapes_validate(name):
     s = W.shape_by_name(name)
     assert mla.validate(mla.make_config(s), chunk_of(s)) == mla.MLA_OK, mla.last_error()
@@ -111,6 +112,53 @@ def test_validate_rope_pairs_sum():
 def test_validate_rejects_bad_chunk(kw):
     s = W.shape_by_name("wan1.3b-w21")
     assert mla.validate(mla.make_config(s), chunk_of(s, **kw)) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_sink_needs_read_rotation():
+    """A sink frame only makes sense with window-local re-indexing (App. D.5), which
+    needs k^R kept unrotated; other rope_mode values and negative sinks are refused."""
+    s = W.shape_by_name("wan1.3b-sink1-w6-t240")
+    for field, value in (("rope_mode", mla.MLA_ROPE_AT_WRITE), ("rope_mode", 5),
+                         ("sink_frames", -1)):
+        cfg = mla.make_config(s)
+        setattr(cfg, field, value)
+        assert mla.validate(cfg, chunk_of(s)) == mla.MLA_ERR_INVALID_ARG, (field, value)
+
+
+@pytest.mark.parametrize("kw,ok", [
+    (dict(), True),                                       # sink 0 + frames 235..240
+    (dict(n_valid_frames=7), False),                      # more than W local frames
+    (dict(n_valid_frames=2), False),                      # misses a chunk frame
+    (dict(t0=0, n_valid_frames=2), True),                 # sink 0 + frames 1, 2
+    (dict(t0=0, n_valid_frames=3), False),                # local window reaches the sink
+    (dict(t0=1, n_valid_frames=3), True),                 # sink 0 + frames 1..3
+    (dict(t0=0, chunk_frames=1, n_valid_frames=0), True),  # the sink frame on its own
+])
+def test_sink_window_geometry(kw, ok):
+    s = W.shape_by_name("wan1.3b-sink1-w6-t240")
+    st = mla.validate(mla.make_config(s), chunk_of(s, **kw))
+    assert (st == mla.MLA_OK) == ok, (kw, st, mla.last_error())
+
+
+def test_cache_and_workspace_bytes_with_sink():
+    """The ring holds S sink slots plus W local slots; read-time rotation adds the
+    assembled window (attended keys x (d_c + d_rope)) to the workspace."""
+    s = W.shape_by_name("wan1.3b-sink1-w6-t240")
+    cfg = mla.make_config(s)
+    assert mla.cache_bytes(cfg, 1) == (1 + 6) * 1560 * 224 * 2
+    w21 = W.shape_by_name("wan1.3b-w21")
+    a = mla.workspace_bytes(mla.make_config(w21), chunk_of(w21))
+    b = mla.workspace_bytes(mla.make_config(w21.with_(rope_at_read=True)), chunk_of(w21))
+    assert b - a >= 21 * 1560 * 224 * 2
+
+
+def test_latent_attention_refuses_read_rotation(lib):
+    s = W.shape_by_name("wan1.3b-w21-read")
+    cfg = mla.make_config(s)
+    ch = chunk_of(s)
+    n = mla.workspace_bytes(cfg, ch)
+    assert lib.mla_latent_attention(ctypes.byref(cfg), ctypes.byref(ch), 4096, 4096, 4096, 4096, n,
+                                    None) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_fp32_path_accepts_odd_dims():

@@ -23,10 +23,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
 def step_flops(s):
-    """Algorithmic FLOP of one chunk step (each projection counted once, attention
-    as one (d_c+d_rope)-wide score plus one d_c-wide latent value per (query, key,
-    head))."""
-    tq, tw, nh = s.chunk_tokens, s.window_tokens, s.n_heads
+    """Algorithmic FLOP of one chunk step over the s.batch requests (each projection
+    counted once, attention as one (d_c+d_rope)-wide score plus one d_c-wide latent
+    value per (query, key, head))."""
+    tq, tw, nh = s.batch * s.chunk_tokens, s.window_tokens, s.n_heads
     write = 2 * tq * s.d_model * (s.d_c + s.d_rope)
     qprep = (2 * tq * s.d_model * s.d_q + 2 * tq * s.d_q * nh * (s.d_nope + s.d_rope)
              + 2 * tq * nh * s.d_nope * s.d_c)
@@ -38,13 +38,13 @@ def step_flops(s):
 
 
 def attention_flops(s):
-    return 2 * s.chunk_tokens * s.n_heads * s.window_tokens * (2 * s.d_c + s.d_rope)
+    return 2 * s.batch * s.chunk_tokens * s.n_heads * s.window_tokens * (2 * s.d_c + s.d_rope)
 
 
 def cache_write_bytes(s):
     """Algorithmic HBM bytes of one cache write: read x and the two weights once,
-    write the new ring rows."""
-    tq = s.chunk_tokens
+    write the new ring rows (all s.batch requests)."""
+    tq = s.batch * s.chunk_tokens
     return 2 * (tq * s.d_model + (s.d_c + s.d_rope) * s.d_model + tq * (s.d_c + s.d_rope))
 
 
@@ -109,7 +109,7 @@ def cpu_baseline(s, w_exact, x_window, n_tokens):
     t0 = time.perf_counter()
     O.step(s, w_exact, x_window, s.window_frame_ids, s.chunk_frame_ids, query_rows=rows)
     dt = time.perf_counter() - t0
-    flops = step_flops(s)["total"] * n_tokens / s.chunk_tokens
+    flops = step_flops(s.with_(batch=1))["total"] * n_tokens / s.chunk_tokens
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n_tokens} of {s.chunk_tokens} query tokens (all {s.n_heads} heads) over "
                       f"the full {s.window_tokens}-token window, fp64 NumPy; "
@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan1.3b-w21")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="independent requests per step, each with its own cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4680)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -140,9 +142,9 @@ def main():
     import latent_kv_attention_down_amd as mla
     from latent_kv_attention_down_amd.layer import DeviceLayer
 
-    s = W.shape_by_name(args.workload)
-    print(f"[bench] workload {s.name}: {s.chunk_tokens} query tokens x {s.n_heads} heads over "
-          f"{s.window_tokens} keys", file=sys.stderr, flush=True)
+    s = W.shape_by_name(args.workload).with_(batch=args.batch)
+    print(f"[bench] workload {s.name}: {s.batch} x {s.chunk_tokens} query tokens x {s.n_heads} "
+          f"heads over {s.window_tokens} keys", file=sys.stderr, flush=True)
     if args.copy_calibration > 0:
         src = torch.ones(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -153,7 +155,7 @@ def main():
     stored, w_exact = W.draw_weights(s)
     ids = s.window_frame_ids
     xs, xe = W.draw_frames(s, ids)
-    L = DeviceLayer(s, stored)
+    L = DeviceLayer(s, stored, batch=s.batch)
     tpf = s.tokens_per_frame
     for i, f in enumerate(ids):
         if f >= s.t0:
@@ -227,7 +229,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights; no trained model)",
-        "config": {"workload": s.name, "batch": 1, "query_tokens": s.chunk_tokens,
+        "config": {"workload": s.name, "batch": s.batch, "query_tokens": s.chunk_tokens,
                    "window_tokens": s.window_tokens, "chunk_frames": s.chunk_frames,
                    "window_frames": s.window_frames, "heads": s.n_heads, "d_c": s.d_c,
                    "d_rope": s.d_rope, "d_model": s.d_model, "grid": [s.grid_h, s.grid_w],
@@ -247,6 +249,9 @@ def main():
                                  "traffic": cw_traffic,
                                  "kernel": "k_cache_write_dma (cache write)",
                                  "bytes_per_launch": wbytes},
+        "device_bytes": {"cache_per_request": L.cache[0].numel() * L.cache.element_size(),
+                         "workspace": int(ws.numel()),
+                         "peak_allocated": int(torch.cuda.max_memory_allocated())},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)

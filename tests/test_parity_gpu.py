@@ -160,15 +160,16 @@ def sample_rows(shape, n=48, seed=1):
     return rows
 
 
-def sampled_full(shape):
-    run = Run(shape)
+def sampled_full(shape, batch=1):
+    run = Run(shape, batch=batch)
     y = full_step(run, check_cache=False, sample=sample_rows(shape))
-    # cache: sampled ring rows against the oracle's entries
+    # cache: sampled ring rows of every request against the oracle's entries
     rng = np.random.default_rng(2)
-    ring = to_host(run.L.cache)[0]
-    ref = run.oracle_ring()
-    rows = rng.choice(ring.shape[0], 600, replace=False)
-    assert_cache_rows(ring[rows], ref[rows], "bf16", "cache sample")
+    ring = to_host(run.L.cache)
+    for b in range(batch):
+        ref = run.oracle_ring(b)
+        rows = rng.choice(ring.shape[1], 600, replace=False)
+        assert_cache_rows(ring[b][rows], ref[rows], "bf16", f"cache sample[b={b}]")
     return run, y
 
 
@@ -176,6 +177,14 @@ def test_wan13b_layer_sampled():
     """Wan-1.3B layer, 3-frame chunk over the 21-frame window: the launch the
     benchmark times, checked on sampled query tokens (all heads) and cache rows."""
     sampled_full(W.shape_by_name("wan1.3b-w21"))
+
+
+@pytest.mark.parametrize("name,batch", [("wan1.3b-w21", 3), ("wan1.3b-sink1-w6-t240", 4)])
+def test_batched_requests_full_size_sampled(name, batch):
+    """Several independent requests in one call, each with its own ring and its own
+    tokens, at full Wan-1.3B size: every request is checked on sampled query rows
+    and sampled ring rows."""
+    sampled_full(W.shape_by_name(name), batch=batch)
 
 
 @pytest.mark.parametrize("name", ["wan1.3b-w6-t240", "wan1.3b-w42-t240", "wan1.3b-w21-t240-q1"])

@@ -35,12 +35,18 @@ Readings taken where the paper is silent (same numbering as the design notes):
     context is the sink frames generated so far followed by the n_valid most
     recent frames, in that order, and its frame i takes temporal coordinate i
     (keys and the query chunk alike); y and x stay as they are.
+  * Chunk-causal forward (the training-time pass of §3.3 with the block masks
+    of App. D.4): the query chunk is a whole clip (or any run of frames) split
+    into blocks of B consecutive frames; a token of block k attends every
+    context frame before the chunk, every frame of blocks 0..k, and nothing
+    after its block.  B = 0 means no mask: the whole window, as at inference.
 """
 import numpy as np
 
 __all__ = [
     "rope_pair_split", "rope_omegas", "rope3d", "rmsnorm", "token_positions",
-    "ring_slot", "window_frames", "ring_rows_for_window", "context_times", "cache_entries",
+    "ring_slot", "window_frames", "ring_rows_for_window", "context_times", "visible_keys",
+    "cache_entries",
     "expected_ring", "query_parts", "reconstruct_kv", "attention_unabsorbed",
     "attention_absorbed", "output_projection", "step", "cache_scalars_per_token",
     "dense_scalars_per_token",
@@ -148,6 +154,24 @@ def context_times(frames, rope_at_read):
     return {f: (i if rope_at_read else f) for i, f in enumerate(frames)}
 
 
+def visible_keys(s, window_ids, chunk_ids):
+    """How many context keys each chunk token may attend, as a prefix of the
+    context (keys are in context order, the chunk's frames last).  With causal
+    blocks of B frames (App. D.4: tokens see their own 3-frame chunk and earlier
+    ones, never a later one; §3.3 trains with these block masks), token i of the
+    chunk lies in block (i // tpf) // B and sees the context up to that block's
+    last frame.  Without blocks every token sees the whole window."""
+    tpf = s.tokens_per_frame
+    n = len(chunk_ids) * tpf
+    total = len(window_ids) * tpf
+    bf = getattr(s, "causal_frames", 0)
+    if not bf:
+        return np.full(n, total, dtype=np.int64)
+    first = window_ids.index(chunk_ids[0])
+    block = (np.arange(n) // tpf) // bf
+    return np.minimum((first + (block + 1) * bf) * tpf, total)
+
+
 # ----------------------------------------------------------------- the layer
 def _head_rows(w, h, width):
     return w[h * width:(h + 1) * width]
@@ -208,14 +232,16 @@ def reconstruct_kv(s, w, c):
     return k_nope, v
 
 
-def attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope, block=1024):
+def attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope, block=1024, visible=None):
     """Chunk attention as defined in §3.3 Eq. 7: per head, score =
     (q^nope.k^nope + q^rope.k^rope) / sqrt(d_nope + d_rope) over every window
     token, softmax over the window, weighted sum of v_{j,h}; heads concatenated.
     q_nope (N, H, d_nope), q_rope (N, H, d_rope), c (M, d_c), k_rope (M, d_rope).
-    Returns out (N, H*d_head)."""
+    visible (N,) optionally limits query i to keys 0..visible[i]-1 (the block
+    mask of the chunk-causal forward).  Returns out (N, H*d_head)."""
     k_nope, v = reconstruct_kv(s, w, c)
     n = q_nope.shape[0]
+    m = c.shape[0]
     scale = 1.0 / np.sqrt(s.d_nope + s.d_rope)
     out = np.empty((n, s.n_heads, s.d_head))
     for h in range(s.n_heads):
@@ -224,6 +250,8 @@ def attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope, block=1024):
         for i0 in range(0, n, block):
             i1 = min(n, i0 + block)
             sc = (q_nope[i0:i1, h, :] @ kn.T + q_rope[i0:i1, h, :] @ k_rope.T) * scale
+            if visible is not None:
+                sc[np.arange(m)[None, :] >= np.asarray(visible[i0:i1])[:, None]] = -np.inf
             sc = sc - sc.max(axis=1, keepdims=True)
             a = np.exp(sc)
             a /= a.sum(axis=1, keepdims=True)
@@ -263,14 +291,20 @@ def step(s, w, x_window, window_ids, chunk_ids, query_rows=None):
     Keys and queries are rotated at absolute t, or at their frame's index in the
     context when the shape rotates on window assembly (App. D.5).  query_rows
     optionally restricts the queries to a subset of chunk tokens (indices into
-    the chunk).  Returns dict(out=(Nq, H*d_h), y=(Nq, d), c, k_rope)."""
+    the chunk).  With causal blocks (the training-time forward over a clip) each
+    query sees the context only up to the end of its block.  Returns
+    dict(out=(Nq, H*d_h), y=(Nq, d), c, k_rope)."""
     tpf = s.tokens_per_frame
     times = context_times(window_ids, getattr(s, "rope_at_read", False))
     c, _, k_rope = cache_entries(s, w, x_window, window_ids, times)
     first = window_ids.index(chunk_ids[0])
     x_chunk = np.asarray(x_window[first * tpf:(first + len(chunk_ids)) * tpf], dtype=np.float64)
     _, q_nope, q_rope = query_parts(s, w, x_chunk, chunk_ids, times)
+    visible = visible_keys(s, window_ids, chunk_ids)
     if query_rows is not None:
         q_nope, q_rope = q_nope[query_rows], q_rope[query_rows]
-    out = attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope)
+        visible = visible[query_rows]
+    masked = bool(getattr(s, "causal_frames", 0))
+    out = attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope,
+                               visible=visible if masked else None)
     return {"out": out, "y": output_projection(w, out), "c": c, "k_rope": k_rope}

@@ -290,8 +290,49 @@ def pin_read_rotation(o):
         assert err < 1e-12, (token, err)
 
 
+def pin_chunk_causal(o):
+    """Chunk-causal forward over a clip (§3.3 trains with block masks; App. D.4:
+    tokens see their own chunk and earlier ones, never a later one).
+    (a) Block k of the clip pass equals the inference step whose chunk is block
+    k over a window of the frames before it and the block itself (no mask).
+    (b) Scalar loops over the truncated context give the same rows.
+    (c) Blocks as long as the chunk reduce to the unmasked step.
+    (d) Changing a later frame's tokens leaves every earlier block bit-identical
+    and changes the later block."""
+    s = small_wan(window_frames=6, chunk_frames=6, t0=0, n_valid_frames=6, causal_frames=2)
+    w, ids, x = layer_inputs(s)
+    assert ids == list(range(6))
+    tpf = s.tokens_per_frame
+    r = o.step(s, w, x, ids, s.chunk_frame_ids)
+    for k in range(3):
+        dk = s.with_(chunk_frames=2, t0=2 * k, n_valid_frames=2 * k + 2, causal_frames=0)
+        ids_k = dk.window_frame_ids
+        assert ids_k == list(range(2 * k + 2))
+        rk = o.step(dk, w, x[:len(ids_k) * tpf], ids_k, dk.chunk_frame_ids)
+        got = r["y"][2 * k * tpf:(2 * k + 2) * tpf]
+        assert np.abs(got - rk["y"]).max() < 1e-12 * np.abs(rk["y"]).max(), k
+    sb = tiny_brute_shape().with_(window_frames=4, chunk_frames=4, t0=0, n_valid_frames=4,
+                                  causal_frames=2)
+    wb, idb, xb = layer_inputs(sb, seed=4)
+    rb = o.step(sb, wb, xb, idb, sb.chunk_frame_ids)
+    tb = sb.tokens_per_frame
+    for token in (0, 7, 12, 23):
+        vis = (token // tb) // 2 * 2 + 2
+        yb = np.array(brute_force_y(sb, wb, xb[:vis * tb], idb[:vis], sb.chunk_frame_ids, token))
+        err = np.abs(yb - rb["y"][token]).max() / np.abs(yb).max()
+        assert err < 1e-12, (token, err)
+    full = o.step(s.with_(causal_frames=6), w, x, ids, s.chunk_frame_ids)
+    plain = o.step(s.with_(causal_frames=0), w, x, ids, s.chunk_frame_ids)
+    assert np.array_equal(full["y"], plain["y"])
+    x2 = x.copy()
+    x2[5 * tpf:] += 1.0
+    r2 = o.step(s, w, x2, ids, s.chunk_frame_ids)
+    assert np.array_equal(r2["y"][:4 * tpf], r["y"][:4 * tpf])
+    assert not np.allclose(r2["y"][4 * tpf:], r["y"][4 * tpf:])
+
+
 ALL_PINS = [pin_accounting, pin_absorbed, pin_sdpa, pin_bruteforce, pin_rope, pin_positions,
-            pin_sink_context, pin_read_rotation]
+            pin_sink_context, pin_read_rotation, pin_chunk_causal]
 
 
 # ---------------------------------------------------------------- the pins as tests
@@ -462,6 +503,26 @@ def test_read_time_rotation():
     pin_read_rotation(O)
 
 
+def test_chunk_causal_forward():
+    pin_chunk_causal(O)
+
+
+def test_chunk_causal_visible_keys():
+    """Prefix lengths of the block mask: a 21-frame clip in 3-frame blocks, and a
+    chunk that follows cached frames (the blocks start after them)."""
+    s = W.shape_by_name("wan1.3b-clip21-causal3")
+    v = O.visible_keys(s, s.window_frame_ids, s.chunk_frame_ids)
+    tpf = s.tokens_per_frame
+    assert v.shape == (21 * tpf,)
+    assert v[0] == v[3 * tpf - 1] == 3 * tpf and v[3 * tpf] == 6 * tpf and v[-1] == 21 * tpf
+    assert int(v.sum()) == W.attended_pairs(s) == tpf * tpf * 3 * 3 * (1 + 2 + 3 + 4 + 5 + 6 + 7)
+    t = small_wan(window_frames=6, chunk_frames=4, t0=2, n_valid_frames=6, causal_frames=2)
+    v = O.visible_keys(t, t.window_frame_ids, t.chunk_frame_ids)
+    tp = t.tokens_per_frame
+    assert list(v[::tp]) == [4 * tp, 4 * tp, 6 * tp, 6 * tp]
+    assert int(v.sum()) == W.attended_pairs(t)
+
+
 def test_expected_ring_with_sink_keeps_raw_keys():
     """With read-time rotation the ring keeps [c^KV | k^R] unrotated (§3.2); the sink
     frame sits in slot 0 for good and later frames go FIFO over slots 1..W."""
@@ -485,7 +546,7 @@ def test_expected_ring_with_sink_keeps_raw_keys():
 from oracle import mla_oracle as _M  # noqa: E402
 
 _ORIG = {k: getattr(_M, k) for k in ("rope3d", "rmsnorm", "reconstruct_kv",
-                                     "attention_unabsorbed", "rope_omegas")}
+                                     "attention_unabsorbed", "rope_omegas", "visible_keys")}
 
 
 def _mut_rope_sign(v, pos, omegas, axes):
@@ -508,13 +569,34 @@ def _mut_kv_head_order(s, w, c):
     return k_nope, v
 
 
-def _mut_drop_rope_term(s, w, q_nope, q_rope, c, k_rope, block=1024):
-    return _ORIG["attention_unabsorbed"](s, w, q_nope, np.zeros_like(q_rope), c, k_rope, block)
+def _mut_drop_rope_term(s, w, q_nope, q_rope, c, k_rope, block=1024, visible=None):
+    return _ORIG["attention_unabsorbed"](s, w, q_nope, np.zeros_like(q_rope), c, k_rope, block,
+                                         visible)
 
 
-def _mut_scale_nope_only(s, w, q_nope, q_rope, c, k_rope, block=1024):
+def _mut_scale_nope_only(s, w, q_nope, q_rope, c, k_rope, block=1024, visible=None):
     f = math.sqrt((s.d_nope + s.d_rope) / s.d_nope)
-    return _ORIG["attention_unabsorbed"](s, w, q_nope * f, q_rope * f, c, k_rope, block)
+    return _ORIG["attention_unabsorbed"](s, w, q_nope * f, q_rope * f, c, k_rope, block, visible)
+
+
+def _mut_mask_ignored(s, w, q_nope, q_rope, c, k_rope, block=1024, visible=None):
+    return _ORIG["attention_unabsorbed"](s, w, q_nope, q_rope, c, k_rope, block, None)
+
+
+def _mut_mask_per_frame(s, window_ids, chunk_ids):
+    v = _ORIG["visible_keys"](s, window_ids, chunk_ids)
+    if not getattr(s, "causal_frames", 0):
+        return v
+    tpf = s.tokens_per_frame
+    first = window_ids.index(chunk_ids[0])
+    return (first + np.arange(len(v)) // tpf + 1) * tpf
+
+
+def _mut_mask_one_block_late(s, window_ids, chunk_ids):
+    v = _ORIG["visible_keys"](s, window_ids, chunk_ids)
+    if not getattr(s, "causal_frames", 0):
+        return v
+    return np.minimum(v + s.causal_frames * s.tokens_per_frame, len(window_ids) * s.tokens_per_frame)
 
 
 def _mut_omega_lowband(d_head, pairs, theta=10000.0):
@@ -549,6 +631,9 @@ MUTANTS = {
     "absolute times at read": dict(context_times=_mut_times_absolute),
     "sink frame evicted": dict(ring_slot=_mut_sink_evicted),
     "sink after the local frames": dict(window_frames=_mut_sink_last),
+    "causal mask ignored": dict(attention_unabsorbed=_mut_mask_ignored),
+    "causal mask per frame, not per block": dict(visible_keys=_mut_mask_per_frame),
+    "causal mask one block late": dict(visible_keys=_mut_mask_one_block_late),
 }
 
 

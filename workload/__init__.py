@@ -4,9 +4,9 @@ This module only draws random numbers and describes shapes; it holds none of
 the method's arithmetic.  Both the HIP path (through the Python binding) and
 the CPU oracle receive exactly the arrays produced here.
 """
-from .shapes import MLAShape, SHAPES, shape_by_name
+from .shapes import MLAShape, SHAPES, shape_by_name, attended_pairs
 from .gen import (draw_weights, draw_frames, round_to_bf16_bits, bf16_bits_to_f32,
                   WEIGHT_NAMES)
 
-__all__ = ["MLAShape", "SHAPES", "shape_by_name", "draw_weights", "draw_frames",
+__all__ = ["MLAShape", "SHAPES", "shape_by_name", "attended_pairs", "draw_weights", "draw_frames",
            "round_to_bf16_bits", "bf16_bits_to_f32", "WEIGHT_NAMES"]

@@ -31,6 +31,7 @@ class MLAShape:
     batch: int = 1
     rope_at_read: bool = False # cache keeps k^R unrotated; rotation on window assembly
     sink_frames: int = 0       # leading frames kept for good (read-time rotation only)
+    causal_frames: int = 0     # chunk-causal blocks of this many chunk frames (0: no mask)
 
     @property
     def tokens_per_frame(self) -> int:
@@ -66,7 +67,7 @@ class MLAShape:
 
 
 def _wan(name, d_c=192, d_rope=32, window=21, chunk=3, t0=18, n_valid=None,
-         pairs=None, dtype="bf16", rope_at_read=False, sink=0):
+         pairs=None, dtype="bf16", rope_at_read=False, sink=0, causal=0):
     if pairs is None:
         pairs = (6, 5, 5) if d_rope == 32 else (12, 10, 10)
     return MLAShape(name=name, d_model=1536, n_heads=12, d_head=128,
@@ -74,7 +75,8 @@ def _wan(name, d_c=192, d_rope=32, window=21, chunk=3, t0=18, n_valid=None,
                     rope_pairs=pairs, grid_h=30, grid_w=52, window_frames=window,
                     chunk_frames=chunk, t0=t0,
                     n_valid_frames=window if n_valid is None else n_valid,
-                    dtype=dtype, rope_at_read=rope_at_read, sink_frames=sink)
+                    dtype=dtype, rope_at_read=rope_at_read, sink_frames=sink,
+                    causal_frames=causal)
 
 
 SHAPES = {
@@ -102,6 +104,27 @@ for _dc, _dr in ((128, 32), (256, 32), (192, 64)):
 SHAPES["wan1.3b-w21-read"] = _wan("wan1.3b-w21-read", rope_at_read=True)
 SHAPES["wan1.3b-sink1-w6-t240"] = _wan("wan1.3b-sink1-w6-t240", window=6, t0=238,
                                        rope_at_read=True, sink=1)
+
+# Training-time forward (§3.3, App. D.4): the whole 21-frame clip is the query
+# chunk, written to the cache in one call, with chunk-causal blocks of 3 frames.
+SHAPES["wan1.3b-clip21-causal3"] = _wan("wan1.3b-clip21-causal3", chunk=21, t0=0, causal=3)
+
+
+def attended_pairs(s: MLAShape) -> int:
+    """(query token, key token) pairs one request attends, per head: every chunk
+    token sees the whole window, or with causal blocks the context up to the end
+    of its block."""
+    tpf = s.tokens_per_frame
+    nk = s.window_tokens
+    if not s.causal_frames:
+        return s.chunk_tokens * nk
+    before = nk - s.chunk_tokens
+    blocks = -(-s.chunk_frames // s.causal_frames)
+    total = 0
+    for k in range(blocks):
+        frames = min(s.causal_frames, s.chunk_frames - k * s.causal_frames)
+        total += frames * tpf * min(before + (k + 1) * s.causal_frames * tpf, nk)
+    return total
 
 
 def shape_by_name(name: str) -> MLAShape:

@@ -26,7 +26,7 @@ def step_flops(s):
     """Algorithmic FLOP of one chunk step over the s.batch requests (each projection
     counted once, attention as one (d_c+d_rope)-wide score plus one d_c-wide latent
     value per (query, key, head))."""
-    tq, tw, nh = s.batch * s.chunk_tokens, s.window_tokens, s.n_heads
+    tq, nh = s.batch * s.chunk_tokens, s.n_heads
     write = 2 * tq * s.d_model * (s.d_c + s.d_rope)
     qprep = (2 * tq * s.d_model * s.d_q + 2 * tq * s.d_q * nh * (s.d_nope + s.d_rope)
              + 2 * tq * nh * s.d_nope * s.d_c)
@@ -38,7 +38,10 @@ def step_flops(s):
 
 
 def attention_flops(s):
-    return 2 * s.batch * s.chunk_tokens * s.n_heads * s.window_tokens * (2 * s.d_c + s.d_rope)
+    """Attended (query, key) pairs per head (the whole window, or with chunk-causal
+    blocks the context up to each block's end) x heads x the two contractions."""
+    from workload import attended_pairs
+    return 2 * s.batch * attended_pairs(s) * s.n_heads * (2 * s.d_c + s.d_rope)
 
 
 def cache_write_bytes(s):
@@ -109,7 +112,10 @@ def cpu_baseline(s, w_exact, x_window, n_tokens):
     t0 = time.perf_counter()
     O.step(s, w_exact, x_window, s.window_frame_ids, s.chunk_frame_ids, query_rows=rows)
     dt = time.perf_counter() - t0
-    flops = step_flops(s.with_(batch=1))["total"] * n_tokens / s.chunk_tokens
+    f1 = step_flops(s.with_(batch=1))
+    vis = O.visible_keys(s, s.window_frame_ids, s.chunk_frame_ids)[rows]
+    flops = ((f1["total"] - f1["attention"]) * n_tokens / s.chunk_tokens
+             + 2 * float(vis.sum()) * s.n_heads * (2 * s.d_c + s.d_rope))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n_tokens} of {s.chunk_tokens} query tokens (all {s.n_heads} heads) over "
                       f"the full {s.window_tokens}-token window, fp64 NumPy; "
@@ -161,7 +167,7 @@ def main():
         if f >= s.t0:
             break
         L.cache_write(L.chunk(1, f, 1), L.tokens(xs[:, i * tpf:(i + 1) * tpf]))
-    chunk = L.chunk(s.chunk_frames, s.t0, s.n_valid_frames)
+    chunk = L.chunk(s.chunk_frames, s.t0, s.n_valid_frames, s.causal_frames)
     x = L.tokens(xs[:, -s.chunk_frames * tpf:])
     y = L.new_out(chunk, s.d_model)
     ws = L.workspace(chunk)

@@ -107,6 +107,14 @@ typedef struct {
                           /* frame, n_valid <= W and covering every chunk frame   */
                           /* >= S.  The sink frames written so far (f < S) are    */
                           /* attended as well.                                    */
+  int32_t causal_frames;  /* 0: every chunk token attends the whole window (the   */
+                          /* inference step).  k > 0, dividing chunk_frames: the  */
+                          /* chunk-causal forward of training (§3.3 with the      */
+                          /* block masks of App. D.4): chunk frames form blocks   */
+                          /* of k, and a token of block j attends the context     */
+                          /* before the chunk plus blocks 0..j only.  Used by     */
+                          /* chunk_attention, step and latent_attention; the      */
+                          /* cache write ignores it.                              */
 } mla_chunk;
 
 /*

@@ -34,7 +34,8 @@ class Weights(ctypes.Structure):
 
 
 class Chunk(ctypes.Structure):
-    _fields_ = [("batch", _i32), ("chunk_frames", _i32), ("t0", _i64), ("n_valid_frames", _i32)]
+    _fields_ = [("batch", _i32), ("chunk_frames", _i32), ("t0", _i64), ("n_valid_frames", _i32),
+                ("causal_frames", _i32)]
 
 
 _P = ctypes.POINTER
@@ -104,8 +105,8 @@ def make_config(shape, dtype=None):
     return c
 
 
-def make_chunk(batch, chunk_frames, t0, n_valid_frames):
-    return Chunk(int(batch), int(chunk_frames), int(t0), int(n_valid_frames))
+def make_chunk(batch, chunk_frames, t0, n_valid_frames, causal_frames=0):
+    return Chunk(int(batch), int(chunk_frames), int(t0), int(n_valid_frames), int(causal_frames))
 
 
 def make_weights(tensors):

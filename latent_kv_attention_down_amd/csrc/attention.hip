@@ -47,17 +47,69 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: weights above it fall back
 constexpr float kSafeThreshold = 8.f;  // lazy rescale threshold of the safe kernel
 
+// Work of one launch.  The rows of a request form nblk blocks of blk_rows rows
+// (one block, all R rows, without a causal mask); block k attends the first
+// min(nk0 + (k+1) blk_keys, nk) keys.  Each block is cut into blk_rt row tiles of
+// RW rows (its last tile may be partial), and row tile rt has one step per key
+// tile it attends.  Steps are numbered request by request, block by block, row
+// tile by row tile: T in all, Tb per request.
 struct Sched {
   int B, R, RTb, RT;
   int nk, KT;
   int start0, len0;
   int64_t cache_rows;
-  int64_t T;
+  int64_t T, Tb;
   int G;
+  int RW;
+  int nblk, blk_rows, blk_rt, blk_keys, nk0;
 };
 
 __host__ __device__ __forceinline__ int wg_of(const Sched &s, int64_t flat) {
   return (int)(((flat + 1) * s.G - 1) / s.T);
+}
+
+__host__ __device__ __forceinline__ int blk_nk(const Sched &s, int k) {
+  const int v = s.nk0 + (k + 1) * s.blk_keys;
+  return v < s.nk ? v : s.nk;
+}
+
+__host__ __device__ __forceinline__ int blk_kt(const Sched &s, int k) {
+  return (blk_nk(s, k) + BN - 1) / BN;
+}
+
+// One row tile: its request, rows [row0, row_end), keys attended, key tiles and
+// the number of its first step.
+struct RowTile {
+  int b, row0, row_end, nk, KT;
+  int64_t f0;
+};
+
+__host__ __device__ __forceinline__ RowTile row_tile(const Sched &s, int rt) {
+  RowTile t;
+  t.b = rt / s.RTb;
+  const int j = rt - t.b * s.RTb, k = j / s.blk_rt, i = j - k * s.blk_rt;
+  int64_t f = (int64_t)t.b * s.Tb;
+  for (int q = 0; q < k; ++q) f += (int64_t)s.blk_rt * blk_kt(s, q);
+  t.nk = blk_nk(s, k);
+  t.KT = (t.nk + BN - 1) / BN;
+  t.f0 = f + (int64_t)i * t.KT;
+  t.row0 = k * s.blk_rows + i * s.RW;
+  const int lim = min((k + 1) * s.blk_rows, s.R);
+  t.row_end = min(t.row0 + s.RW, lim);
+  return t;
+}
+
+// The row tile that step f belongs to.
+__host__ __device__ __forceinline__ int rt_of(const Sched &s, int64_t f) {
+  const int b = (int)(f / s.Tb);
+  int64_t r = f - (int64_t)b * s.Tb;
+  int k = 0;
+  for (; k + 1 < s.nblk; ++k) {
+    const int64_t wk = (int64_t)s.blk_rt * blk_kt(s, k);
+    if (r < wk) break;
+    r -= wk;
+  }
+  return b * s.RTb + k * s.blk_rt + (int)(r / blk_kt(s, k));
 }
 
 // DC/DR: latent and RoPE widths; QT: 32-row query tiles per wave; NW: waves per
@@ -340,7 +392,6 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   Tile<C> tl;
   tl.base = (bf16 *)lds;
-  tl.nk = s.nk;
   tl.start0 = s.start0;
   tl.len0 = s.len0;
 
@@ -357,14 +408,13 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
   // Pieces are taken last row tile first: a range that crosses a row-tile boundary
   // then starts at key tile 0, so at step t nearly every workgroup reads key tile t
   // (or t + a fixed offset) and the workgroups of one XCD share their L2 lines.
-  const int rt_first = (int)(begin / s.KT), rt_last = (int)((end - 1) / s.KT);
-  const int kt_begin = (int)(begin - (int64_t)rt_first * s.KT);    // first key tile of rt_first
-  const int kt_end = (int)(end - (int64_t)rt_last * s.KT);         // end key tile of rt_last
+  const int rt_first = rt_of(s, begin), rt_last = rt_of(s, end - 1);
   for (int rt = rt_last; rt >= rt_first; --rt) {
-    const int kt0 = rt == rt_first ? kt_begin : 0;
-    const int kt1 = rt == rt_last ? kt_end : s.KT;
-    const int b = rt / s.RTb;
-    const int row0 = (rt % s.RTb) * RW;
+    const RowTile t = row_tile(s, rt);
+    const int kt0 = (int)((begin > t.f0 ? begin : t.f0) - t.f0);
+    const int kt1 = (int)((end < t.f0 + t.KT ? end : t.f0 + t.KT) - t.f0);
+    const int b = t.b, row0 = t.row0;
+    tl.nk = t.nk;
     tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
 
     load_queries<C::DK, QT, KB>(Qr, q, s, b, row0 + wave * QT * 32, l32, g);
@@ -434,7 +484,7 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
       }
     }
 
-    const bool whole = (kt0 == 0 && kt1 == s.KT);
+    const bool whole = (kt0 == 0 && kt1 == t.KT);
     unsigned char *rec = part + (size_t)(wg + rt) * C::REC;
     float *rec_m = (float *)(rec + (size_t)RW * DC * 2);
     float *rec_l = rec_m + RW;
@@ -448,7 +498,7 @@ void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
       if (!(lt <= kFastSumLimit)) flags[rt] = 1;
       const int lrow = wave * QT * 32 + qt * 32 + l32;
       const int row = row0 + lrow;
-      if (row < s.R) {
+      if (row < t.row_end) {
         bf16 *dst = whole ? o + ((int64_t)b * s.R + row) * DC : (bf16 *)rec + (int64_t)lrow * DC;
         store_rows<FT, QT>(dst, O, qt, 1.0f / lt, g);
         if (!whole && g == 0) {
@@ -684,7 +734,6 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
   const int l32 = lane & 31, g = lane >> 5;
   TileW<C> tl;
   tl.base = (bf16 *)lds;
-  tl.nk = s.nk;
   tl.start0 = s.start0;
   tl.len0 = s.len0;
   tl.init(lane, wave);
@@ -698,15 +747,14 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
   f32x16 S0[QT], S1[QT];
   float m[QT], l[QT], pend[QT];
 
-  const int rt_first = (int)(begin / s.KT), rt_last = (int)((end - 1) / s.KT);
-  const int kt_begin = (int)(begin - (int64_t)rt_first * s.KT);
-  const int kt_end = (int)(end - (int64_t)rt_last * s.KT);
-  const int last_kt = s.KT - 1;
+  const int rt_first = rt_of(s, begin), rt_last = rt_of(s, end - 1);
   for (int rt = rt_last; rt >= rt_first; --rt) {
-    const int kt0 = rt == rt_first ? kt_begin : 0;
-    const int kt1 = rt == rt_last ? kt_end : s.KT;
-    const int b = rt / s.RTb;
-    const int row0 = (rt % s.RTb) * RW;
+    const RowTile t = row_tile(s, rt);
+    const int kt0 = (int)((begin > t.f0 ? begin : t.f0) - t.f0);
+    const int kt1 = (int)((end < t.f0 + t.KT ? end : t.f0 + t.KT) - t.f0);
+    const int last_kt = t.KT - 1, nk = t.nk;
+    const int b = t.b, row0 = t.row0;
+    tl.nk = nk;
     tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
 
     tl.load(kt0, kt0 % NB);
@@ -727,8 +775,8 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     tl.template scores<0>(S0, Qr, kt0 % NB, l32, g, [](int) {});
     tl.template scores<1>(S1, Qr, kt0 % NB, l32, g, [](int) {});
     if (kt0 == last_kt) {
-      mask_half<QT>(S0, kt0 * BN, s.nk, g);
-      mask_half<QT>(S1, kt0 * BN + 32, s.nk, g);
+      mask_half<QT>(S0, kt0 * BN, nk, g);
+      mask_half<QT>(S1, kt0 * BN + 32, nk, g);
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -758,12 +806,12 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       // make the compiler wait for these loads before the value step.
       const bool more = kt + 2 < kt1;
       if (more) tl.load(kt + 2, (kt + 2) % NB);
-      if (kt == last_kt) mask_half<QT>(S0, kt * BN, s.nk, g);
+      if (kt == last_kt) mask_half<QT>(S0, kt * BN, nk, g);
       tl.template scores<1>(S1, Qr, cur, l32, g,
                             [&](int i) { exp_slot<0, QT, KB * QT>(i, S0, P, m, ls, pend); });
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
-      if (kt == last_kt) mask_half<QT>(S1, kt * BN + 32, s.nk, g);
+      if (kt == last_kt) mask_half<QT>(S1, kt * BN + 32, nk, g);
       if (more)
         wait_loads<C::LOADS>();
       else
@@ -774,7 +822,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     tl.values(O, P, (kt1 - 1) % NB, lane);
     __syncthreads();
 
-    const bool whole = (kt0 == 0 && kt1 == s.KT);
+    const bool whole = (kt0 == 0 && kt1 == t.KT);
     unsigned char *rec = part + (size_t)(wg + rt) * C::REC;
     float *rec_m = (float *)(rec + (size_t)RW * DC * 2);
     float *rec_l = rec_m + RW;
@@ -784,7 +832,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       if (!(lt <= kFastSumLimit)) flags[rt] = 1;
       const int lrow = wave * QT * 32 + qt * 32 + l32;
       const int row = row0 + lrow;
-      if (row < s.R) {
+      if (row < t.row_end) {
         bf16 *dst = whole ? o + ((int64_t)b * s.R + row) * DC : (bf16 *)rec + (int64_t)lrow * DC;
         store_rows<FT, QT>(dst, O, qt, 1.0f / lt, g);
         if (!whole && g == 0) {
@@ -805,12 +853,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
                                                     int blocks_per_tile) {
   constexpr int DC = C::DC, RW = C::RW, C8 = DC / 8;
   const int rt = blockIdx.x / blocks_per_tile;
-  const int g0 = wg_of(s, (int64_t)rt * s.KT), g1 = wg_of(s, (int64_t)rt * s.KT + s.KT - 1);
+  const RowTile t = row_tile(s, rt);
+  const int g0 = wg_of(s, t.f0), g1 = wg_of(s, t.f0 + t.KT - 1);
   if (g0 == g1) return;
   const int idx = (blockIdx.x % blocks_per_tile) * 256 + threadIdx.x;
   const int lrow = idx / C8, c8 = (idx % C8) * 8;
-  const int b = rt / s.RTb, row = (rt % s.RTb) * RW + lrow;
-  if (lrow >= RW || row >= s.R) return;
+  const int b = t.b, row = t.row0 + lrow;
+  if (lrow >= RW || row >= t.row_end) return;
   float mmax = -INFINITY;
   for (int gg = g0; gg <= g1; ++gg) {
     const float *rm = (const float *)(part + (size_t)(gg + rt) * C::REC + (size_t)RW * DC * 2);
@@ -841,16 +890,19 @@ __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
 template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_latent_attn_safe(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
-                        bf16 *__restrict__ o, const int *__restrict__ flags, Sched s,
-                        int fast_rw) {
+                        bf16 *__restrict__ o, const int *__restrict__ flags, Sched s) {
   constexpr int QT = C::QT, KB = C::KB, FT = C::FT, RW = C::RW;
-  const int RTb = (s.R + RW - 1) / RW;
-  const int b = blockIdx.x / RTb, row0 = (blockIdx.x % RTb) * RW;
-  if (!flags[b * s.RTb + row0 / fast_rw]) return;
+  // workgroup: one RW-row piece of a fast row tile (s.RW rows)
+  const int per = (s.RW + RW - 1) / RW;
+  const int rt = blockIdx.x / per;
+  if (!flags[rt]) return;
+  const RowTile t = row_tile(s, rt);
+  const int b = t.b, row0 = t.row0 + (blockIdx.x % per) * RW;
+  if (row0 >= t.row_end) return;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   Tile<C> tl;
   tl.base = (bf16 *)lds;
-  tl.nk = s.nk;
+  tl.nk = t.nk;
   tl.start0 = s.start0;
   tl.len0 = s.len0;
   tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
@@ -872,11 +924,11 @@ void k_latent_attn_safe(const bf16 *__restrict__ q, const bf16 *__restrict__ cac
       for (int r = 0; r < 16; ++r) O[ft][qt][r] = 0.f;
   }
   tl.load(0, tid);
-  for (int kt = 0; kt < s.KT; ++kt) {
+  for (int kt = 0; kt < t.KT; ++kt) {
     __syncthreads();
     tl.store(tid, 0);
     __syncthreads();
-    if (kt + 1 < s.KT) tl.load(kt + 1, tid);
+    if (kt + 1 < t.KT) tl.load(kt + 1, tid);
     f32x16 S[2][QT];
     tl.scores(S, Qr, kt, 0, l32, g);
 #pragma unroll
@@ -900,7 +952,8 @@ void k_latent_attn_safe(const bf16 *__restrict__ q, const bf16 *__restrict__ cac
   for (int qt = 0; qt < QT; ++qt) {
     const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
     const int row = row0 + wave * QT * 32 + qt * 32 + l32;
-    if (row < s.R) store_rows<FT, QT>(o + ((int64_t)b * s.R + row) * C::DC, O, qt, 1.0f / lt, g);
+    if (row < t.row_end)
+      store_rows<FT, QT>(o + ((int64_t)b * s.R + row) * C::DC, O, qt, 1.0f / lt, g);
   }
 }
 
@@ -929,7 +982,8 @@ __global__ __launch_bounds__(256) void k_latent_attn_f32(const float *__restrict
   }
   float m = -INFINITY, l = 0.f;
   const float *cb = cache + (int64_t)b * s.cache_rows * DK;
-  for (int kk = 0; kk < s.nk; ++kk) {
+  const int nk = blk_nk(s, (int)(row - (int64_t)b * s.R) / s.blk_rows);
+  for (int kk = 0; kk < nk; ++kk) {
     const int64_t kr = kk < s.len0 ? (int64_t)(s.start0 + kk) : (int64_t)(kk - s.len0);
     const float *k = cb + kr * DK;
     float sp = 0.f;
@@ -960,15 +1014,31 @@ Sched make_sched(const AttnArgs &a, int rows_per_wg, int grid) {
   Sched s;
   s.B = a.B;
   s.R = a.R;
-  s.RTb = (a.R + rows_per_wg - 1) / rows_per_wg;
-  s.RT = s.B * s.RTb;
+  s.RW = rows_per_wg;
   s.nk = a.nk;
   s.KT = (a.nk + BN - 1) / BN;
   s.start0 = a.start0;
   s.len0 = a.len0;
   s.cache_rows = a.cache_rows;
-  s.T = (int64_t)s.RT * s.KT;
+  if (a.nblk > 1) {
+    s.nblk = a.nblk;
+    s.blk_rows = a.blk_rows;
+    s.blk_keys = a.blk_keys;
+    s.nk0 = a.nk0;
+  } else {
+    s.nblk = 1;
+    s.blk_rows = a.R;
+    s.blk_keys = a.nk;
+    s.nk0 = 0;
+  }
+  s.blk_rt = (s.blk_rows + rows_per_wg - 1) / rows_per_wg;
+  s.RTb = s.nblk * s.blk_rt;
+  s.RT = s.B * s.RTb;
+  s.Tb = 0;
+  for (int k = 0; k < s.nblk; ++k) s.Tb += (int64_t)s.blk_rt * blk_kt(s, k);
+  s.T = (int64_t)s.B * s.Tb;
   s.G = (int)((int64_t)grid < s.T ? (int64_t)grid : s.T);
+  if (s.G < 1) s.G = 1;
   return s;
 }
 
@@ -1008,10 +1078,10 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
   hipLaunchKernelGGL(k_attn_merge<F>, dim3(s.RT * merge_blocks), dim3(256), 0, st, (bf16 *)a.o,
                      (const unsigned char *)a.part, s, merge_blocks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int safe_tiles = s.B * ((s.R + S::RW - 1) / S::RW);
-  hipLaunchKernelGGL(k_latent_attn_safe<S>, dim3(safe_tiles), dim3(S::NT), S::LDS, st,
+  const int safe_wgs = s.RT * ((F::RW + S::RW - 1) / S::RW);
+  hipLaunchKernelGGL(k_latent_attn_safe<S>, dim3(safe_wgs), dim3(S::NT), S::LDS, st,
                      (const bf16 *)a.q, (const bf16 *)a.cache, (bf16 *)a.o,
-                     (const int *)a.flags, s, F::RW);
+                     (const int *)a.flags, s);
   return hipGetLastError();
 }
 
@@ -1026,6 +1096,13 @@ AttnLayout layout() {
 bool latent_attention_bf16_supported(int dc, int dr) {
   return (dc == 192 && dr == 32) || (dc == 128 && dr == 32) || (dc == 256 && dr == 32) ||
          (dc == 192 && dr == 64);
+}
+
+AttnCounts latent_attention_counts(const AttnArgs &a) {
+  const AttnLayout al = latent_attention_layout(a.DC, a.DR);
+  if (al.rows_per_wg <= 0) return AttnCounts{0, 0};
+  const Sched s = make_sched(a, al.rows_per_wg, 1);
+  return AttnCounts{s.RT, s.T};
 }
 
 AttnLayout latent_attention_layout(int dc, int dr) {

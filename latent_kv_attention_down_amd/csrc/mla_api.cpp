@@ -51,6 +51,10 @@ struct Dims {
   int64_t start0;       // rotate-at-write: the window as (up to) two ring ranges,
   int64_t len0;         // [start0, start0 + len0) then [0, nk - len0)
   int64_t t0_q;         // temporal coordinate of the chunk's first frame for queries
+  int64_t nblk;         // chunk-causal blocks (1: no mask)
+  int64_t blk_rows;     // rows per block: causal_frames * tpf * n_h (R without a mask)
+  int64_t blk_keys;     // keys each block adds: causal_frames * tpf (nk without a mask)
+  int64_t nk0;          // keys before the chunk in context order (0 without a mask)
   size_t esz;
 };
 
@@ -80,6 +84,19 @@ Dims dims(const mla_config &c, const mla_chunk &k) {
     d.start0 = slot0 * d.tpf;
     d.len0 = run * d.tpf;
     d.t0_q = k.t0;
+  }
+  // the chunk's frames are the last C frames of the context (sinks included when
+  // the chunk starts inside them)
+  if (k.causal_frames > 0) {
+    d.nblk = k.chunk_frames / k.causal_frames;
+    d.blk_keys = (int64_t)k.causal_frames * d.tpf;
+    d.blk_rows = d.blk_keys * c.n_heads;
+    d.nk0 = d.nk - d.T_q;
+  } else {
+    d.nblk = 1;
+    d.blk_rows = d.R;
+    d.blk_keys = d.nk;
+    d.nk0 = 0;
   }
   d.esz = c.dtype == MLA_BF16 ? 2 : 4;
   return d;
@@ -141,6 +158,8 @@ int validate_chunk_write(const mla_config *c, const mla_chunk *k) {
   if (k->t0 < 0) return fail(MLA_ERR_INVALID_ARG, "t0 must be >= 0");
   if (local_chunk_frames(c, k) > c->window_frames)
     return fail(MLA_ERR_INVALID_ARG, "chunk_frames must fit the window_frames local slots");
+  if (k->causal_frames < 0 || (k->causal_frames > 0 && k->chunk_frames % k->causal_frames != 0))
+    return fail(MLA_ERR_INVALID_ARG, "causal_frames must be 0 or divide chunk_frames");
   const int64_t rows = (int64_t)k->batch * k->chunk_frames * c->grid_h * c->grid_w * c->n_heads;
   if (rows >= (int64_t)1 << 30) return fail(MLA_ERR_INVALID_ARG, "chunk too large");
   return MLA_OK;
@@ -211,6 +230,26 @@ int attn_grid_cus() {
   return cus < kMaxAttnGrid ? cus : kMaxAttnGrid;
 }
 
+// Attention geometry (no pointers): rows, keys, ring ranges and causal blocks.
+mla::AttnArgs attn_shape(const mla_config &c, const mla_chunk &k, const Dims &d) {
+  mla::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = k.batch;
+  a.R = (int)d.R;
+  a.DC = c.d_c;
+  a.DR = c.d_rope;
+  a.cache_rows = d.at_read ? d.nk : d.ring;
+  a.nk = (int)d.nk;
+  a.start0 = (int)d.start0;
+  a.len0 = (int)d.len0;
+  a.grid = 0;  // set at launch (a device query)
+  a.nblk = (int)d.nblk;
+  a.blk_rows = (int)d.blk_rows;
+  a.blk_keys = (int)d.blk_keys;
+  a.nk0 = (int)d.nk0;
+  return a;
+}
+
 // Workspace carving (offsets in bytes, each 256-aligned).
 struct Workspace {
   size_t u_q, c_q, q_nope, q_r, w_t, q_lat, o_lat, part, flags, out_heads, win, total;
@@ -236,8 +275,7 @@ Workspace carve(const mla_config &c, const mla_chunk &k) {
   if (c.dtype == MLA_BF16) {
     // split records are indexed (workgroup + row tile) < grid + row tiles
     const mla::AttnLayout al = mla::latent_attention_layout(c.d_c, c.d_rope);
-    const int64_t rw = al.rows_per_wg;
-    const int64_t rt = (int64_t)k.batch * ((d.R + rw - 1) / rw);
+    const int64_t rt = mla::latent_attention_counts(attn_shape(c, k, d)).row_tiles;
     part = (size_t)((int64_t)kMaxAttnGrid * al.wgs_per_cu + rt) * al.record_bytes;
     flags = (size_t)rt * sizeof(int);
   }
@@ -296,20 +334,12 @@ int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_
                          const void *keys, void *o_lat, unsigned char *ws, hipStream_t st) {
   const Dims d = dims(c, k);
   const Workspace L = carve(c, k);
-  mla::AttnArgs a;
+  mla::AttnArgs a = attn_shape(c, k, d);
   a.q = q_lat;
   a.cache = keys;
   a.o = o_lat;
   a.part = ws + L.part;
   a.flags = (int *)(ws + L.flags);
-  a.B = k.batch;
-  a.R = (int)d.R;
-  a.DC = c.d_c;
-  a.DR = c.d_rope;
-  a.cache_rows = d.at_read ? d.nk : d.ring;
-  a.nk = (int)d.nk;
-  a.start0 = (int)d.start0;
-  a.len0 = (int)d.len0;
   a.grid = attn_grid_cus();
   if (c.dtype == MLA_BF16)
     MLA_HIP(mla::latent_attention_bf16(a, g_ev_start, g_ev_stop, st), "latent attention");
@@ -542,9 +572,7 @@ int mla_attention_grid(const mla_config *cfg, const mla_chunk *chunk) {
   const Dims d = dims(*cfg, *chunk);
   if (cfg->dtype != MLA_BF16) return (int)((d.M * cfg->n_heads + 3) / 4);
   const mla::AttnLayout al = mla::latent_attention_layout(cfg->d_c, cfg->d_rope);
-  const int64_t rw = al.rows_per_wg;
-  const int64_t t = (int64_t)chunk->batch * ((d.R + rw - 1) / rw) *
-                    ((d.nk + mla::kAttnKeyTile - 1) / mla::kAttnKeyTile);
+  const int64_t t = mla::latent_attention_counts(attn_shape(*cfg, *chunk, d)).steps;
   const int64_t g = (int64_t)attn_grid_cus() * al.wgs_per_cu;
   return (int)(g < t ? g : t);
 }

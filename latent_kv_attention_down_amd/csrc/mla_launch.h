@@ -84,7 +84,18 @@ struct AttnArgs {
   int nk;              // valid keys
   int start0, len0;    // first contiguous row range of the window; the rest starts at row 0
   int grid;            // persistent workgroups
+  // Chunk-causal blocks: the R rows are nblk blocks of blk_rows rows; block k
+  // attends the first min(nk0 + (k + 1) * blk_keys, nk) keys.  No mask: nblk = 1,
+  // blk_rows = R, blk_keys = nk, nk0 = 0.
+  int nblk, blk_rows, blk_keys, nk0;
 };
+// Row tiles (with causal blocks, a block's last tile may be partial) and
+// (row tile, key tile) steps of the bf16 kernel for these arguments.
+struct AttnCounts {
+  int64_t row_tiles;
+  int64_t steps;
+};
+AttnCounts latent_attention_counts(const AttnArgs &a);
 hipError_t latent_attention_bf16(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1,
                                  hipStream_t st);
 hipError_t latent_attention_f32(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1,

@@ -43,8 +43,8 @@ class DeviceLayer:
         assert self.cache.numel() * self.cache.element_size() == _lib.cache_bytes(self.cfg, batch)
         self._ws = None
 
-    def chunk(self, chunk_frames, t0, n_valid_frames):
-        return _lib.make_chunk(self.batch, chunk_frames, t0, n_valid_frames)
+    def chunk(self, chunk_frames, t0, n_valid_frames, causal_frames=0):
+        return _lib.make_chunk(self.batch, chunk_frames, t0, n_valid_frames, causal_frames)
 
     def workspace(self, chunk):
         n = _lib.workspace_bytes(self.cfg, chunk)

@@ -83,7 +83,8 @@ class Run:
             self.L.cache_write(ch, xt)
 
     def chunk(self):
-        return self.L.chunk(self.s.chunk_frames, self.s.t0, self.s.n_valid_frames)
+        return self.L.chunk(self.s.chunk_frames, self.s.t0, self.s.n_valid_frames,
+                            self.s.causal_frames)
 
     def chunk_tokens(self):
         return self.L.tokens(self.x_store[:, self.chunk_slice])

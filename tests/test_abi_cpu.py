@@ -45,7 +45,8 @@ def cfg_of(name, **kw):
 
 
 def chunk_of(s, **kw):
-    d = dict(batch=1, chunk_frames=s.chunk_frames, t0=s.t0, n_valid_frames=s.n_valid_frames)
+    d = dict(batch=1, chunk_frames=s.chunk_frames, t0=s.t0, n_valid_frames=s.n_valid_frames,
+             causal_frames=s.causal_frames)
     d.update(kw)
     return mla.make_chunk(**d)
 
@@ -53,7 +54,8 @@ def chunk_of(s, **kw):
 @pytest.mark.parametrize("name", ["tiny-f32", "wan1.3b-w21", "wan1.3b-w42-t240",
                                   "wan1.3b-w21-t240-q1", "wan1.3b-w21-dc128-dr32",
                                   "wan1.3b-w21-dc256-dr32", "wan1.3b-w21-dc192-dr64",
-                                  "wan1.3b-w21-read", "wan1.3b-sink1-w6-t240"])
+                                  "wan1.3b-w21-read", "wan1.3b-sink1-w6-t240",
+                                  "wan1.3b-clip21-causal3"])
 def test_workload_shapes_validate(name):
     s = W.shape_by_name(name)
     assert mla.validate(mla.make_config(s), chunk_of(s)) == mla.MLA_OK, mla.last_error()
@@ -150,6 +152,25 @@ def test_cache_and_workspace_bytes_with_sink():
     a = mla.workspace_bytes(mla.make_config(w21), chunk_of(w21))
     b = mla.workspace_bytes(mla.make_config(w21.with_(rope_at_read=True)), chunk_of(w21))
     assert b - a >= 21 * 1560 * 224 * 2
+
+
+@pytest.mark.parametrize("causal,ok", [(0, True), (1, True), (3, True), (7, True), (21, True),
+                                       (2, False), (4, False), (-1, False)])
+def test_causal_blocks_must_divide_the_chunk(causal, ok):
+    """Chunk-causal blocks tile the 21-frame clip exactly or are refused."""
+    s = W.shape_by_name("wan1.3b-clip21-causal3")
+    st = mla.validate(mla.make_config(s), chunk_of(s, causal_frames=causal))
+    assert (st == mla.MLA_OK) == ok, (causal, st, mla.last_error())
+
+
+def test_causal_blocks_add_split_records():
+    """Each causal block starts a new row tile, so the clip pass needs a few more
+    row tiles (split records and flags) than the unmasked pass over the same rows."""
+    s = W.shape_by_name("wan1.3b-clip21-causal3")
+    cfg = mla.make_config(s)
+    a = mla.workspace_bytes(cfg, chunk_of(s, causal_frames=0))
+    b = mla.workspace_bytes(cfg, chunk_of(s))
+    assert 0 < a < b
 
 
 def test_latent_attention_refuses_read_rotation(lib):

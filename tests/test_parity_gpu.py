@@ -156,7 +156,11 @@ def test_attention_on_oracle_cache():
 def sample_rows(shape, n=48, seed=1):
     rng = np.random.default_rng(seed)
     t = shape.chunk_tokens
-    rows = np.unique(np.concatenate([rng.choice(t, n - 4, replace=False), [0, 1, t - 2, t - 1]]))
+    edges = [0, 1, t - 2, t - 1]
+    if shape.causal_frames:  # both sides of every block boundary
+        step = shape.causal_frames * shape.tokens_per_frame
+        edges += [e for k in range(step, t, step) for e in (k - 1, k)]
+    rows = np.unique(np.concatenate([rng.choice(t, n, replace=False), edges]))
     return rows
 
 

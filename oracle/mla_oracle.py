@@ -46,10 +46,9 @@ import numpy as np
 __all__ = [
     "rope_pair_split", "rope_omegas", "rope3d", "rmsnorm", "token_positions",
     "ring_slot", "window_frames", "ring_rows_for_window", "context_times", "visible_keys",
-    "cache_entries",
-    "expected_ring", "query_parts", "reconstruct_kv", "attention_unabsorbed",
-    "attention_absorbed", "output_projection", "step", "cache_scalars_per_token",
-    "dense_scalars_per_token",
+    "cache_entries", "expected_ring", "query_parts", "reconstruct_kv",
+    "attention_unabsorbed", "attention_absorbed", "value_absorbed_output",
+    "output_projection", "step", "cache_scalars_per_token", "dense_scalars_per_token",
 ]
 
 
@@ -264,6 +263,12 @@ def output_projection(w, out):
     return out @ w["w_o"].T
 
 
+def value_absorbed_output(s, w, h):
+    """B_h = W_O,h W_up,h^V (App. E Eq. 10-11): the columns of W_O that mix head h,
+    times that head's value up-projection; (d, d_c)."""
+    return w["w_o"][:, h * s.d_head:(h + 1) * s.d_head] @ _head_rows(w["w_v_up"], h, s.d_head)
+
+
 def attention_absorbed(s, w, c_q, q_rope, c, k_rope):
     """The inference reparameterisation of App. E, written as the paper states it:
     content score (c^Q)^T A_h c^KV with A_h = (W_up,h^Q)^T W_up,h^K (Eq. 8-9), the
@@ -274,7 +279,7 @@ def attention_absorbed(s, w, c_q, q_rope, c, k_rope):
     y = np.zeros((n, s.d_model))
     for h in range(s.n_heads):
         a_h = _head_rows(w["w_q_up"], h, s.d_nope).T @ _head_rows(w["w_k_up"], h, s.d_nope)
-        b_h = w["w_o"][:, h * s.d_head:(h + 1) * s.d_head] @ _head_rows(w["w_v_up"], h, s.d_head)
+        b_h = value_absorbed_output(s, w, h)
         sc = (c_q @ a_h @ c.T + q_rope[:, h, :] @ k_rope.T) * scale
         sc = sc - sc.max(axis=1, keepdims=True)
         a = np.exp(sc)

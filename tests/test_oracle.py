@@ -546,7 +546,8 @@ def test_expected_ring_with_sink_keeps_raw_keys():
 from oracle import mla_oracle as _M  # noqa: E402
 
 _ORIG = {k: getattr(_M, k) for k in ("rope3d", "rmsnorm", "reconstruct_kv",
-                                     "attention_unabsorbed", "rope_omegas", "visible_keys")}
+                                     "attention_unabsorbed", "rope_omegas", "visible_keys",
+                                     "value_absorbed_output")}
 
 
 def _mut_rope_sign(v, pos, omegas, axes):
@@ -620,6 +621,16 @@ def _mut_sink_last(t0, chunk_frames, n_valid_frames, sink_frames=0):
     return list(range(last - n_valid_frames + 1, last + 1)) + list(range(min(sink_frames, last + 1)))
 
 
+def _mut_b_transposed_head(s, w, h):
+    wo = w["w_o"][:, h * s.d_head:(h + 1) * s.d_head]
+    wv = w["w_v_up"][h * s.d_head:(h + 1) * s.d_head]
+    return wo[:, ::-1] @ wv
+
+
+def _mut_b_next_head(s, w, h):
+    return _ORIG["value_absorbed_output"](s, w, (h + 1) % s.n_heads)
+
+
 MUTANTS = {
     "rope rotation sign": dict(rope3d=_mut_rope_sign),
     "rope axis order": dict(rope3d=_mut_rope_axes),
@@ -634,6 +645,8 @@ MUTANTS = {
     "causal mask ignored": dict(attention_unabsorbed=_mut_mask_ignored),
     "causal mask per frame, not per block": dict(visible_keys=_mut_mask_per_frame),
     "causal mask one block late": dict(visible_keys=_mut_mask_one_block_late),
+    "B_h with W_O columns reversed": dict(value_absorbed_output=_mut_b_transposed_head),
+    "B_h of the next head": dict(value_absorbed_output=_mut_b_next_head),
 }
 
 

@@ -95,6 +95,11 @@ typedef struct {
   const void *w_k_up;    /* W^K_up     (n_h*d_nope) x d_c   (Eq. 2)                */
   const void *w_v_up;    /* W^V_up     (n_h*d_head) x d_c   (Eq. 2)                */
   const void *w_o;       /* W_O        d x (n_h*d_head)                            */
+  const void *w_b;       /* optional: B = [B_1 .. B_nh], d x (n_h*d_c), B_h =       */
+                         /* W_O[:, h*d_h:(h+1)*d_h] W^V_up,h (App. E Eq. 10-11),    */
+                         /* as written by mla_value_absorbed_weights.  When set,    */
+                         /* mla_step computes y = sum_h B_h O_lat,h in one GEMM     */
+                         /* and needs neither w_v_up nor w_o; NULL: W^V_up then W_O */
 } mla_weights;
 
 /* The chunk being generated and the window it sees.                             */
@@ -165,7 +170,8 @@ int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk
  *   out_heads (B, C * tpf, n_h * d_head): head outputs o_h = W^V_up,h sum_j a_j c_j,
  *             concatenated over heads (before W_O).
  *   workspace device scratch of at least mla_workspace_bytes(cfg, chunk).
- * Every query attends to every valid cached token (no mask inside the window).
+ * Every query attends to every valid cached token (no mask inside the window),
+ * unless chunk->causal_frames cuts the chunk into causal blocks (see mla_chunk).
  * Under MLA_ROPE_AT_READ the attended frames are first gathered into the
  * workspace in context order with k^R rotated at window-local positions.
  */
@@ -175,12 +181,27 @@ int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_c
 
 /*
  * One layer's chunk step: mla_cache_write, then mla_chunk_attention, then the
- * output projection y = W_O out_heads (§3.3).
+ * output projection y = W_O out_heads (§3.3).  With w->w_b set, the value
+ * up-projection and W_O are replaced by y = sum_h B_h O_lat,h (App. E Eq. 10-11),
+ * one GEMM over the n_h * d_c latent outputs; the result is the same up to
+ * rounding.
  *   y  (B, C * tpf, d).
  */
 int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
              const void *x, void *cache, void *y, void *workspace, size_t ws_bytes,
              void *stream);
+
+/*
+ * Value absorption into the output projection (App. E Eq. 10-11), a weight
+ * preparation done once per weight set:
+ *   w_b (d, n_h * d_c) cfg->dtype, written: column h*d_c + c of row n is
+ *       sum_k W_O[n][h*d_head + k] * W^V_up[h*d_head + k][c], summed in fp32
+ *       and rounded once.  16-byte aligned, caller-owned.
+ * Needs w->w_v_up and w->w_o.  Asynchronous on `stream`; INVALID_ARG or
+ * ALIGNMENT before any launch, MLA_ERR_HIP if the launch fails.
+ */
+int mla_value_absorbed_weights(const mla_config *cfg, const mla_weights *w, void *w_b,
+                               void *stream);
 
 /*
  * The latent attention loop on its own (App. E Eq. 8, 12 and 16): the inner call

@@ -186,15 +186,20 @@ int validate(const mla_config *c, const mla_chunk *k) {
   return validate_chunk(c, k);
 }
 
+// write: the cache-write weights; attend: the query side and W^K_up; heads: the
+// per-head outputs (W^V_up); project: y, either through w_b or through W^V_up
+// and W_O.
 int validate_weights(const mla_config &c, const mla_weights *w, bool write, bool attend,
-                     bool project) {
+                     bool heads, bool project) {
   if (!w) return fail(MLA_ERR_INVALID_ARG, "weights is NULL");
   if (write && (!w->w_kv_down || !w->w_kr)) return fail(MLA_ERR_INVALID_ARG, "w_kv_down/w_kr NULL");
-  if (attend && (!w->w_q_down || !w->w_q_up || !w->w_qr || !w->w_k_up || !w->w_v_up))
-    return fail(MLA_ERR_INVALID_ARG, "a query/up-projection weight is NULL");
-  if (project && !w->w_o) return fail(MLA_ERR_INVALID_ARG, "w_o is NULL");
+  if (attend && (!w->w_q_down || !w->w_q_up || !w->w_qr || !w->w_k_up))
+    return fail(MLA_ERR_INVALID_ARG, "a query projection or w_k_up is NULL");
+  if (heads && !w->w_v_up) return fail(MLA_ERR_INVALID_ARG, "w_v_up is NULL");
+  if (project && !w->w_b && (!w->w_v_up || !w->w_o))
+    return fail(MLA_ERR_INVALID_ARG, "need w_b, or w_v_up and w_o");
   const void *ptrs[] = {w->w_kv_down, w->w_kr, w->w_q_down, w->w_q_up, w->w_qr,
-                        w->w_k_up,    w->w_v_up, w->w_o};
+                        w->w_k_up,    w->w_v_up, w->w_o,    w->w_b};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "weights must be 16-byte aligned");
   (void)c;
@@ -383,7 +388,8 @@ int run_gemm(const mla_config &c, const mla::GemmArgs &g, bool out_f32, hipStrea
     if (s_ != MLA_OK) return s_; \
   } while (0)
 
-// Query preparation, latent attention and per-head value up-projection.
+// Query preparation, latent attention and, when out_heads is given, the per-head
+// value up-projection.
 int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chunk &k,
                         const void *x, const void *cache, void *out_heads, unsigned char *ws,
                         hipStream_t st) {
@@ -454,6 +460,7 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
   }
   // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16)
   MLA_TRY(run_latent_attention(c, k, q_lat, keys, o_lat, ws, st));
+  if (!out_heads) return MLA_OK;  // O_lat stays in the workspace
   // o_h = W^V_up,h O_lat,h  (Eq. 2)
   MLA_TRY(run_gemm(c, gemm(o_lat, (int64_t)nh * c.d_c, c.d_c, w.w_v_up, c.d_c,
                            (int64_t)c.d_head * c.d_c, out_heads, (int64_t)nh * c.d_head, c.d_head,
@@ -496,7 +503,7 @@ int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk
   g_last_error.clear();
   MLA_TRY(validate_config(cfg));
   MLA_TRY(validate_chunk_write(cfg, chunk));
-  MLA_TRY(validate_weights(*cfg, w, true, false, false));
+  MLA_TRY(validate_weights(*cfg, w, true, false, false, false));
   if (!x || !cache) return fail(MLA_ERR_INVALID_ARG, "x or cache is NULL");
   if (!aligned16(x) || !aligned16(cache)) return fail(MLA_ERR_ALIGNMENT, "x and cache must be 16-byte aligned");
   return run_cache_write(*cfg, *w, *chunk, x, cache, (hipStream_t)stream);
@@ -507,7 +514,7 @@ int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_c
                         size_t ws_bytes, void *stream) {
   g_last_error.clear();
   MLA_TRY(validate(cfg, chunk));
-  MLA_TRY(validate_weights(*cfg, w, false, true, false));
+  MLA_TRY(validate_weights(*cfg, w, false, true, true, false));
   if (!x || !cache || !out_heads) return fail(MLA_ERR_INVALID_ARG, "x, cache or out_heads is NULL");
   if (!aligned16(x) || !aligned16(cache) || !aligned16(out_heads))
     return fail(MLA_ERR_ALIGNMENT, "x, cache and out_heads must be 16-byte aligned");
@@ -520,7 +527,7 @@ int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk
              void *cache, void *y, void *workspace, size_t ws_bytes, void *stream) {
   g_last_error.clear();
   MLA_TRY(validate(cfg, chunk));
-  MLA_TRY(validate_weights(*cfg, w, true, true, true));
+  MLA_TRY(validate_weights(*cfg, w, true, true, false, true));
   if (!x || !cache || !y) return fail(MLA_ERR_INVALID_ARG, "x, cache or y is NULL");
   if (!aligned16(x) || !aligned16(cache) || !aligned16(y))
     return fail(MLA_ERR_ALIGNMENT, "x, cache and y must be 16-byte aligned");
@@ -532,12 +539,35 @@ int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk
   const Workspace L = carve(c, k);
   const Dims d = dims(c, k);
   MLA_TRY(run_cache_write(c, *w, k, x, cache, st));
+  if (w->w_b) {
+    MLA_TRY(run_chunk_attention(c, *w, k, x, cache, nullptr, ws, st));
+    // y = sum_h B_h O_lat,h  (App. E Eq. 10-11): row (token) of O_lat is n_h * d_c wide
+    const int64_t kb = (int64_t)c.n_heads * c.d_c;
+    MLA_TRY(run_gemm(c, gemm(ws + L.o_lat, kb, 0, w->w_b, kb, 0, y, c.d_model, 0, d.M, c.d_model,
+                             (int)kb, 1, 1.f),
+                     false, st, "value-absorbed output projection"));
+    return MLA_OK;
+  }
   MLA_TRY(run_chunk_attention(c, *w, k, x, cache, ws + L.out_heads, ws, st));
   // y = W_O out  (§3.3)
   MLA_TRY(run_gemm(c, gemm(ws + L.out_heads, (int64_t)c.n_heads * c.d_head, 0, w->w_o,
                            (int64_t)c.n_heads * c.d_head, 0, y, c.d_model, 0, d.M, c.d_model,
                            c.n_heads * c.d_head, 1, 1.f),
                    false, st, "output projection"));
+  return MLA_OK;
+}
+
+int mla_value_absorbed_weights(const mla_config *cfg, const mla_weights *w, void *w_b,
+                               void *stream) {
+  g_last_error.clear();
+  MLA_TRY(validate_config(cfg));
+  if (!w || !w->w_v_up || !w->w_o) return fail(MLA_ERR_INVALID_ARG, "need w_v_up and w_o");
+  if (!w_b) return fail(MLA_ERR_INVALID_ARG, "w_b is NULL");
+  if (!aligned16(w->w_v_up) || !aligned16(w->w_o) || !aligned16(w_b))
+    return fail(MLA_ERR_ALIGNMENT, "w_v_up, w_o and w_b must be 16-byte aligned");
+  MLA_HIP(mla::absorb_value(w->w_o, w->w_v_up, w_b, cfg->d_model, cfg->n_heads, cfg->d_head,
+                            cfg->d_c, cfg->dtype == MLA_BF16, (hipStream_t)stream),
+          "value absorption");
   return MLA_OK;
 }
 

@@ -72,6 +72,10 @@ hipError_t assemble_window(const AssembleArgs &a, bool bf16, hipStream_t st);
 hipError_t transpose_heads(const void *w, void *w_t, int n_h, int d_nope, int d_c, int esz,
                            hipStream_t st);
 
+// B = [B_1 .. B_nh], B_h = W_O[:, h*d_h:(h+1)*d_h] W^V_up,h, stored [d][n_h*d_c].
+hipError_t absorb_value(const void *w_o, const void *w_v, void *w_b, int d, int n_h, int d_h,
+                        int d_c, bool bf16_io, hipStream_t st);
+
 // Latent attention over the ring window.
 struct AttnArgs {
   const void *q;       // (B, R, DK)

@@ -43,6 +43,16 @@ class DeviceLayer:
         assert self.cache.numel() * self.cache.element_size() == _lib.cache_bytes(self.cfg, batch)
         self._ws = None
 
+    def absorb_value(self):
+        """Compute B = [B_1 .. B_nh] (B_h = W_O,h W^V_up,h) on the device and make
+        step() project the latent attention output with it."""
+        s = self.shape
+        w_b = torch.empty((s.d_model, s.n_heads * s.d_c), dtype=self.tdtype, device=self.device)
+        _lib.value_absorbed_weights(self.cfg, self.weights, w_b)
+        self.tensors["w_b"] = w_b
+        self.weights = _lib.make_weights(self.tensors)
+        return w_b
+
     def chunk(self, chunk_frames, t0, n_valid_frames, causal_frames=0):
         return _lib.make_chunk(self.batch, chunk_frames, t0, n_valid_frames, causal_frames)
 

@@ -206,6 +206,30 @@ def test_null_arguments_fail_before_any_launch(lib):
                                     None) == mla.MLA_ERR_WORKSPACE
 
 
+def test_value_absorbed_weights_checks_before_launch(lib):
+    """mla_value_absorbed_weights needs W^V_up, W_O and an aligned output; it refuses
+    anything else on the host.  mla_step accepts w_b in place of W^V_up and W_O."""
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    fake = {n: 4096 for n, _ in mla.Weights._fields_}
+    assert lib.mla_value_absorbed_weights(ctypes.byref(cfg), ctypes.byref(mla.Weights(**fake)),
+                                          None, None) == mla.MLA_ERR_INVALID_ARG
+    no_o = mla.Weights(**dict(fake, w_o=None))
+    assert lib.mla_value_absorbed_weights(ctypes.byref(cfg), ctypes.byref(no_o), 4096,
+                                          None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_value_absorbed_weights(ctypes.byref(cfg), ctypes.byref(mla.Weights(**fake)),
+                                          4100, None) == mla.MLA_ERR_ALIGNMENT
+    ch = chunk_of(s)
+    n = mla.workspace_bytes(cfg, ch)
+    # no w_b and no w_o: refused; a misaligned w_b: refused (both before any launch)
+    wt = mla.Weights(**dict(fake, w_o=None, w_b=None))
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
+                        4096, n, None) == mla.MLA_ERR_INVALID_ARG
+    wt = mla.Weights(**dict(fake, w_o=None, w_v_up=None, w_b=4100))
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
+                        4096, n, None) == mla.MLA_ERR_ALIGNMENT
+
+
 def test_status_strings(lib):
     for code, name in ((0, "MLA_OK"), (-1, "MLA_ERR_INVALID_ARG"), (-2, "MLA_ERR_UNSUPPORTED"),
                        (-3, "MLA_ERR_ALIGNMENT"), (-4, "MLA_ERR_WORKSPACE"), (-5, "MLA_ERR_HIP")):

@@ -45,6 +45,9 @@ constexpr int BN = kAttnKeyTile;       // keys per tile
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: weights above it fall back
+// Word 3 of a gfx9 buffer descriptor for raw byte-addressed loads (no format
+// conversion, stride 0).
+constexpr int kBufferConfig = 0x00020000;
 constexpr float kSafeThreshold = 8.f;  // lazy rescale threshold of the safe kernel
 
 // Work of one launch.  The rows of a request form nblk blocks of blk_rows rows
@@ -155,6 +158,9 @@ struct CfgW {
   static constexpr size_t LDS = (size_t)STAGE * 2 * NBUF;
   static constexpr size_t REC = (size_t)RW * DC * 2 + (size_t)RW * 8;
   static constexpr int WAVES_PER_SIMD = 1;
+  // After a row tile's first key tile, its reference max enters the score MFMAs as
+  // their initial accumulator (-m), so the exponentials need no subtraction.
+  static constexpr bool FOLD_MAX = true;
   static_assert(CPR % 4 == 0 && LOADS * NW * 64 == BN * CPR, "tile does not split into loads");
   static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
 };
@@ -525,15 +531,15 @@ struct TileW {
   bf16 *base;
   const bf16 *cb;
   int nk, start0, len0;
-  int goff[LOADS];  // element offset, within the tile's rows, of this lane's chunks
-  int dst0;         // element offset of this wave's first load in a stage
+  unsigned boff[LOADS];  // byte offset, within the tile's rows, of this lane's chunks
+  int dst0;              // element offset of this wave's first load in a stage
 
   __device__ __forceinline__ void init(int lane, int wave) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int p = (wave * LOADS + i) * 64 + lane;
       const int r = p / C::CPR;
-      goff[i] = r * DK + (((p % C::CPR) ^ swz4(r)) * 8);
+      boff[i] = (unsigned)(r * DK + (((p % C::CPR) ^ swz4(r)) * 8)) * 2u;
     }
     dst0 = wave * LOADS * 64 * 8;
   }
@@ -544,34 +550,31 @@ struct TileW {
     return kk < len0 ? (int64_t)(start0 + kk) : (int64_t)(kk - len0);
   }
 
-  // Loads of tile kt into stage buf: plan once, then issue the LOADS pieces one at
-  // a time (completion: vmcnt).  Keys past nk repeat key nk-1, a finite row whose
-  // probability is zero.
-  struct Plan {
-    const bf16 *tb;  // first row of a tile that is contiguous in the ring, else null
-    int k0;
-    bf16 *dst;
-  };
-  __device__ __forceinline__ Plan plan(int kt, int buf) const {
-    const int k0 = kt * BN;
-    const bool contiguous = (k0 + BN <= nk) && (k0 + BN <= len0 || k0 >= len0);
-    return Plan{contiguous ? cb + key_row(k0) * DK : nullptr, k0, Ks(buf) + dst0};
-  }
-  __device__ __forceinline__ void issue(const Plan &pl, int i) const {
+  // Loads of tile kt into stage buf (completion: vmcnt; LOADS per wave either way),
+  // as buffer loads into LDS through rs, a descriptor of this request's ring
+  // (byte offsets; anything past its end reads as zero).  A tile that is one run of
+  // consecutive ring rows takes a uniform offset plus each lane's fixed offset, no
+  // per-lane address arithmetic.  Otherwise (the window's last tile, or the tile
+  // where the ring wraps) each lane finds its own row; keys past nk repeat key nk-1,
+  // a finite row whose probability is zero.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int kt, int buf) const {
     typedef __attribute__((address_space(3))) void lds_void;
-    const bf16 *src;
-    if (pl.tb) {
-      src = pl.tb + goff[i];
-    } else {
-      const int r = goff[i] / DK;
-      src = cb + key_row(min(pl.k0 + r, nk - 1)) * DK + (goff[i] - r * DK);
-    }
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(pl.dst + i * 512), 16, 0, 0);
-  }
-  __device__ __forceinline__ void load(int kt, int buf) const {
-    const Plan pl = plan(kt, buf);
+    const int k0 = kt * BN;
+    bf16 *dst = Ks(buf) + dst0;
+    if ((k0 + BN <= nk) && (k0 + BN <= len0 || k0 >= len0)) {
+      const int tile_off = (int)(key_row(k0) * (DK * 2));
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) issue(pl, i);
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + i * 512), 16, (int)boff[i],
+                                                 tile_off, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int e = (int)(boff[i] / 2u), r = e / DK;
+        const int off = (int)(key_row(min(k0 + r, nk - 1)) * (DK * 2)) + (e - r * DK) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + i * 512), 16, off, 0, 0, 0);
+      }
+    }
   }
 
   // S^T of one 32-key half T of the tile for both query tiles.  K fragments run
@@ -579,8 +582,9 @@ struct TileW {
   // qt) the caller's work(2kb + qt) is emitted, each group fenced so the order
   // stays MFMA / VALU / MFMA / VALU.
   template <int T, class Work>
-  __device__ __forceinline__ void scores(f32x16 (&S)[QT], const bf16x8 (&Qr)[QT][KB], int buf,
-                                         int l32, int g, Work &&work) const {
+  __device__ __forceinline__ void scores(f32x16 (&S)[QT], const bf16x8 (&Qr)[QT][KB],
+                                         const f32x16 (&init)[QT], int buf, int l32, int g,
+                                         Work &&work) const {
     // k-block kb is chunk 2kb + g of row T*32 + l32; the swizzle only flips the low
     // two chunk bits, so even and odd k-blocks each have one base address.
     const int sw = swz4(l32);
@@ -591,14 +595,13 @@ struct TileW {
     bf16x8 fr[D + 1];
 #pragma unroll
     for (int kb = 0; kb < D; ++kb) fr[kb] = kfrag(kb);
-    const f32x16 zero = {};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       __builtin_amdgcn_sched_barrier(0);
       if (kb + D < KB) fr[(kb + D) % (D + 1)] = kfrag(kb + D);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        S[qt] = mfma32(fr[kb % (D + 1)], Qr[qt][kb], kb == 0 ? zero : S[qt]);
+        S[qt] = mfma32(fr[kb % (D + 1)], Qr[qt][kb], kb == 0 ? init[qt] : S[qt]);
         work(kb * QT + qt);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -660,9 +663,11 @@ __device__ __forceinline__ void pin(T &v) {
 // the MFMAs of another step: slot i takes elements [i*16QT/NS, (i+1)*16QT/NS),
 // element j being row j % 16 of query tile j / 16.  Block 2T + h of P takes S
 // elements 8h..8h+7 (keys T*32 + 16h + 4g + e and T*32 + 16h + 8 + 4g + e) as
-// packed bf16 pairs, as the V^T fragments expect.  Row sums go to two partial sums
-// per query tile; pend carries an even element to the slot that completes its pair.
-template <int T, int QT, int NS>
+// packed bf16 pairs, as the V^T fragments expect.  SUB: S still holds raw scores
+// (subtract the reference max), else the max was folded into the scores.  Row
+// sums go to two partial sums per query tile; pend carries an even element to the
+// slot that completes its pair.
+template <int T, int QT, int NS, bool SUB>
 __device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], u32x4 (&P)[BN / 16][QT],
                                          const float (&m)[QT], float (&ls)[QT][2],
                                          float (&pend)[QT]) {
@@ -670,7 +675,7 @@ __device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], u32x4 
 #pragma unroll
   for (int j = slot * NE / NS; j < (slot + 1) * NE / NS; ++j) {
     const int qt = j / 16, r = j % 16;
-    float p = fast_exp2(S[qt][r] - m[qt]);
+    float p = fast_exp2(SUB ? S[qt][r] - m[qt] : S[qt][r]);
     ls[qt][r & 1] += p;
     pin(p);
     pin(ls[qt][r & 1]);
@@ -685,11 +690,11 @@ __device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], u32x4 
   }
 }
 
-template <int T, int QT>
+template <int T, int QT, bool SUB>
 __device__ __forceinline__ void exp_half(const f32x16 (&S)[QT], u32x4 (&P)[BN / 16][QT],
                                          const float (&m)[QT], float (&l)[QT]) {
   float ls[QT][2] = {}, pend[QT];
-  exp_slot<T, QT, 1>(0, S, P, m, ls, pend);
+  exp_slot<T, QT, 1, SUB>(0, S, P, m, ls, pend);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
 }
@@ -756,8 +761,10 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     const int b = t.b, row0 = t.row0;
     tl.nk = nk;
     tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)tl.cb, (short)0, (int)(s.cache_rows * C::DK * 2), kBufferConfig);
 
-    tl.load(kt0, kt0 % NB);
+    tl.load(rs, kt0, kt0 % NB);
     load_queries<C::DK, QT, KB>(Qr, q, s, b, row0 + wave * QT * 32, l32, g);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -769,11 +776,13 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     }
     wait_loads<0>();
     __syncthreads();
-    if (kt0 + 1 < kt1) tl.load(kt0 + 1, (kt0 + 1) % NB);
+    if (kt0 + 1 < kt1) tl.load(rs, kt0 + 1, (kt0 + 1) % NB);
 
     // first tile: both halves, the fixed reference max, probabilities of keys 0-31
-    tl.template scores<0>(S0, Qr, kt0 % NB, l32, g, [](int) {});
-    tl.template scores<1>(S1, Qr, kt0 % NB, l32, g, [](int) {});
+    constexpr bool FOLD = C::FOLD_MAX;
+    f32x16 init[QT] = {};
+    tl.template scores<0>(S0, Qr, init, kt0 % NB, l32, g, [](int) {});
+    tl.template scores<1>(S1, Qr, init, kt0 % NB, l32, g, [](int) {});
     if (kt0 == last_kt) {
       mask_half<QT>(S0, kt0 * BN, nk, g);
       mask_half<QT>(S1, kt0 * BN + 32, nk, g);
@@ -785,9 +794,19 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[qt][r], S1[qt][r]));
       m[qt] = fmaxf(mx, __shfl_xor(mx, 32, 64));
     }
-    exp_half<0, QT>(S0, P, m, l);
+    exp_half<0, QT, true>(S0, P, m, l);
+    if (FOLD) {
+      // later tiles start their scores at -m; keys 32-63 of this tile catch up here
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          init[qt][r] = -m[qt];
+          S1[qt][r] -= m[qt];
+        }
+    }
     if (kt0 + 2 < kt1) {
-      tl.load(kt0 + 2, (kt0 + 2) % NB);
+      tl.load(rs, kt0 + 2, (kt0 + 2) % NB);
       wait_loads<C::LOADS>();
     } else {
       wait_loads<0>();
@@ -797,18 +816,20 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     for (int kt = kt0 + 1; kt < kt1; ++kt) {
       const int cur = kt % NB, prev = (kt + NB - 1) % NB;
       float ls[QT][2] = {};
-      tl.template scores<0>(S0, Qr, cur, l32, g,
-                            [&](int i) { exp_slot<1, QT, KB * QT>(i, S1, P, m, ls, pend); });
+      tl.template scores<0>(S0, Qr, init, cur, l32, g, [&](int i) {
+        exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend);
+      });
       tl.values(O, P, prev, lane);
       order_values_step<FT * (BN / 16)>();
       __builtin_amdgcn_sched_barrier(0);
       // Tile kt+2 is requested only now: the transpose reads above would otherwise
       // make the compiler wait for these loads before the value step.
       const bool more = kt + 2 < kt1;
-      if (more) tl.load(kt + 2, (kt + 2) % NB);
+      if (more) tl.load(rs, kt + 2, (kt + 2) % NB);
       if (kt == last_kt) mask_half<QT>(S0, kt * BN, nk, g);
-      tl.template scores<1>(S1, Qr, cur, l32, g,
-                            [&](int i) { exp_slot<0, QT, KB * QT>(i, S0, P, m, ls, pend); });
+      tl.template scores<1>(S1, Qr, init, cur, l32, g, [&](int i) {
+        exp_slot<0, QT, KB * QT, !FOLD>(i, S0, P, m, ls, pend);
+      });
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
       if (kt == last_kt) mask_half<QT>(S1, kt * BN + 32, nk, g);
@@ -818,7 +839,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
         wait_loads<0>();
       __syncthreads();
     }
-    exp_half<1, QT>(S1, P, m, l);
+    exp_half<1, QT, !FOLD>(S1, P, m, l);
     tl.values(O, P, (kt1 - 1) % NB, lane);
     __syncthreads();
 

@@ -135,6 +135,10 @@ int validate_config(const mla_config *c) {
       return fail(MLA_ERR_UNSUPPORTED,
                   "bf16 path needs d_model, d_q, d_c, d_nope, n_heads*d_head % 32 == 0 and "
                   "d_rope % 16 == 0");
+    // the attention kernel addresses one request's ring (or assembled window) with
+    // 32-bit byte offsets
+    if (ring * (c->d_c + c->d_rope) * 2 >= ((int64_t)1 << 31))
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 path needs a ring of under 2 GiB per request");
     if (!mla::latent_attention_bf16_supported(c->d_c, c->d_rope))
       return fail(MLA_ERR_UNSUPPORTED,
                   "bf16 path is built for (d_c, d_rope) in {(128,32), (192,32), (256,32), (192,64)}");

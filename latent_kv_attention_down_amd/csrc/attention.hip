@@ -1088,8 +1088,10 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
   hipError_t e = allow_lds(fast, F::LDS);
   if (e == hipSuccess) e = allow_lds(k_latent_attn_safe<S>, S::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_fill_i32, dim3((s.RT + 255) / 256), dim3(256), 0, st, a.flags, s.RT, 0);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.flags_zeroed) {
+    hipLaunchKernelGGL(k_fill_i32, dim3((s.RT + 255) / 256), dim3(256), 0, st, a.flags, s.RT, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(fast, dim3(s.G), dim3(F::NT), F::LDS, st, (const bf16 *)a.q,
                      (const bf16 *)a.cache, (bf16 *)a.o, (unsigned char *)a.part, a.flags, s);

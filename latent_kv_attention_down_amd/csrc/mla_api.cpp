@@ -262,6 +262,7 @@ mla::AttnArgs attn_shape(const mla_config &c, const mla_chunk &k, const Dims &d)
 // Workspace carving (offsets in bytes, each 256-aligned).
 struct Workspace {
   size_t u_q, c_q, q_nope, q_r, w_t, q_lat, o_lat, part, flags, out_heads, win, total;
+  int64_t n_flags;  // overflow flags of the bf16 attention (one per row tile)
 };
 
 Workspace carve(const mla_config &c, const mla_chunk &k) {
@@ -281,12 +282,14 @@ Workspace carve(const mla_config &c, const mla_chunk &k) {
   w.q_lat = take((size_t)k.batch * d.R * d.DK * d.esz);
   w.o_lat = take((size_t)k.batch * d.R * c.d_c * d.esz);
   size_t part = 0, flags = 0;
+  w.n_flags = 0;
   if (c.dtype == MLA_BF16) {
     // split records are indexed (workgroup + row tile) < grid + row tiles
     const mla::AttnLayout al = mla::latent_attention_layout(c.d_c, c.d_rope);
     const int64_t rt = mla::latent_attention_counts(attn_shape(c, k, d)).row_tiles;
     part = (size_t)((int64_t)kMaxAttnGrid * al.wgs_per_cu + rt) * al.record_bytes;
     flags = (size_t)rt * sizeof(int);
+    w.n_flags = rt;
   }
   w.part = take(part);
   w.flags = take(flags);
@@ -340,7 +343,8 @@ int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &
 // Latent attention over `keys`: the ring itself (rotate-at-write), or the window
 // assembled in context order in the workspace (read-time rotation).
 int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_lat,
-                         const void *keys, void *o_lat, unsigned char *ws, hipStream_t st) {
+                         const void *keys, void *o_lat, unsigned char *ws, bool flags_zeroed,
+                         hipStream_t st) {
   const Dims d = dims(c, k);
   const Workspace L = carve(c, k);
   mla::AttnArgs a = attn_shape(c, k, d);
@@ -349,6 +353,7 @@ int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_
   a.o = o_lat;
   a.part = ws + L.part;
   a.flags = (int *)(ws + L.flags);
+  a.flags_zeroed = flags_zeroed;
   a.grid = attn_grid_cus();
   if (c.dtype == MLA_BF16)
     MLA_HIP(mla::latent_attention_bf16(a, g_ev_start, g_ev_stop, st), "latent attention");
@@ -439,6 +444,8 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
   rq.t0 = d.t0_q;  // absolute, or the chunk's place in the re-indexed context (App. D.5)
   rq.scale = scale;
   rq.rope = rope_table(c);
+  rq.zero = (int *)(ws + L.flags);  // the attention's overflow flags (bf16 path)
+  rq.n_zero = (int)L.n_flags;
   MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
   // read-time rotation: gather the sink and local frames in context order and
   // rotate k^R at window-local positions (§3.2 Eq. 5, App. D.4-D.5)
@@ -463,7 +470,7 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
     keys = ws + L.win;
   }
   // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16)
-  MLA_TRY(run_latent_attention(c, k, q_lat, keys, o_lat, ws, st));
+  MLA_TRY(run_latent_attention(c, k, q_lat, keys, o_lat, ws, true, st));
   if (!out_heads) return MLA_OK;  // O_lat stays in the workspace
   // o_h = W^V_up,h O_lat,h  (Eq. 2)
   MLA_TRY(run_gemm(c, gemm(o_lat, (int64_t)nh * c.d_c, c.d_c, w.w_v_up, c.d_c,
@@ -588,7 +595,7 @@ int mla_latent_attention(const mla_config *cfg, const mla_chunk *chunk, const vo
     return fail(MLA_ERR_ALIGNMENT, "q_lat, cache and o_lat must be 16-byte aligned");
   MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
   return run_latent_attention(*cfg, *chunk, q_lat, cache, o_lat, (unsigned char *)workspace,
-                              (hipStream_t)stream);
+                              false, (hipStream_t)stream);
 }
 
 void mla_set_timing_events(void *ev_start, void *ev_stop) {

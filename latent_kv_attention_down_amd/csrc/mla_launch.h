@@ -51,6 +51,8 @@ struct RopeQArgs {
   int64_t t0;
   float scale;
   RopeTable rope;
+  int *zero;   // n_zero ints set to 0 on the way (the attention's overflow flags), or null
+  int n_zero;
 };
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st);
 
@@ -88,6 +90,7 @@ struct AttnArgs {
   int nk;              // valid keys
   int start0, len0;    // first contiguous row range of the window; the rest starts at row 0
   int grid;            // persistent workgroups
+  bool flags_zeroed;   // flags already cleared by an earlier kernel on the stream
   // Chunk-causal blocks: the R rows are nblk blocks of blk_rows rows; block k
   // attends the first min(nk0 + (k + 1) * blk_keys, nk) keys.  No mask: nblk = 1,
   // blk_rows = R, blk_keys = nk, nk0 = 0.

@@ -2,7 +2,8 @@
 // §3.2 Eq. 6, App. D.2, App. E Eq. 8-9):
 //  * RMSNorm of the query latent c^Q (one wave per row);
 //  * rotation of the per-head positional query and its store, pre-scaled, into the
-//    rope columns of the absorbed query rows;
+//    rope columns of the absorbed query rows (the same launch clears the attention's
+//    overflow flags, saving a launch of its own);
 //  * the per-head transpose of W^K_up used by the absorption GEMM
 //    q~_h = (W^K_up,h)^T q^nope_h.
 #include "mla_device.h"
@@ -30,6 +31,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *in, const GT 
 template <typename OutT>
 __global__ __launch_bounds__(256) void k_rope_q(RopeQArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one pair per thread
+  if (idx < a.n_zero) a.zero[idx] = 0;
   const int P = a.d_rope / 2;
   const int64_t total = (int64_t)a.M * a.n_h * P;
   if (idx >= total) return;
@@ -75,7 +77,8 @@ hipError_t rmsnorm_rows(const float *in, const void *g, void *out, int rows, int
 }
 
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st) {
-  const int64_t total = (int64_t)a.M * a.n_h * (a.d_rope / 2);
+  int64_t total = (int64_t)a.M * a.n_h * (a.d_rope / 2);
+  if (a.n_zero > total) total = a.n_zero;
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
   if (bf16_out)

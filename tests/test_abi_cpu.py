@@ -173,6 +173,19 @@ def test_causal_blocks_add_split_records():
     assert 0 < a < b
 
 
+def test_bf16_ring_over_2gib_is_refused():
+    """The attention kernel addresses one request's ring with 32-bit byte offsets, so
+    the bf16 path refuses rings of 2 GiB or more per request; fp32 has no such limit."""
+    s = W.shape_by_name("wan1.3b-w21")
+    frames = (1 << 31) // (1560 * 224 * 2)  # 3072 frames of 1560 tokens: just over 2 GiB
+    big = mla.make_config(s.with_(window_frames=frames + 1))
+    assert mla.validate(big, chunk_of(s)) == mla.MLA_ERR_UNSUPPORTED
+    ok = mla.make_config(s.with_(window_frames=frames - 1))
+    assert mla.validate(ok, chunk_of(s)) == mla.MLA_OK, mla.last_error()
+    assert mla.validate(mla.make_config(s.with_(window_frames=frames + 1, dtype="f32")),
+                        chunk_of(s)) == mla.MLA_OK
+
+
 def test_latent_attention_refuses_read_rotation(lib):
     s = W.shape_by_name("wan1.3b-w21-read")
     cfg = mla.make_config(s)

@@ -194,3 +194,11 @@ def test_batched_requests_full_size_sampled(name, batch):
 @pytest.mark.parametrize("name", ["wan1.3b-w6-t240", "wan1.3b-w42-t240", "wan1.3b-w21-t240-q1"])
 def test_window_sweep_sampled(name):
     sampled_full(W.shape_by_name(name))
+
+
+@pytest.mark.parametrize("name", ["wan1.3b-w21-dc128-dr32", "wan1.3b-w21-dc256-dr32",
+                                  "wan1.3b-w21-dc192-dr64"])
+def test_latent_width_variants_full_size_sampled(name):
+    """The (d_c, d_rope) variants at full Wan-1.3B size, in the launch the sweep times
+    (d_c = 256 runs the two-waves-per-SIMD kernel)."""
+    sampled_full(W.shape_by_name(name))

@@ -865,18 +865,25 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
   }
 }
 
-// Merge the pieces of every row tile that more than one workgroup worked on.  One
-// thread per (row, 8 latent columns): it weighs each piece's normalised partial by
-// l_p * 2^(m_p - max m) and renormalises.  Workgroups of unsplit tiles exit at once.
+// Merge the pieces of every row tile that more than one workgroup worked on.  The
+// grid walks the workgroup boundaries: boundary w (the first step of workgroup w)
+// falls inside at most one row tile, and a split tile is taken at the first
+// boundary inside it, so every split tile is merged exactly once and the launch
+// stays small however many row tiles there are.  One thread per (row, 8 latent
+// columns): it weighs each piece's normalised partial by l_p * 2^(m_p - max m) and
+// renormalises.
 template <class C>
 __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
                                                     const unsigned char *__restrict__ part, Sched s,
                                                     int blocks_per_tile) {
   constexpr int DC = C::DC, RW = C::RW, C8 = DC / 8;
-  const int rt = blockIdx.x / blocks_per_tile;
+  const int wb = blockIdx.x / blocks_per_tile;
+  if (wb == 0) return;
+  const int64_t f = (int64_t)wb * s.T / s.G;
+  const int rt = rt_of(s, f);
   const RowTile t = row_tile(s, rt);
-  const int g0 = wg_of(s, t.f0), g1 = wg_of(s, t.f0 + t.KT - 1);
-  if (g0 == g1) return;
+  if (f == t.f0 || wg_of(s, t.f0) != wb - 1) return;
+  const int g0 = wb - 1, g1 = wg_of(s, t.f0 + t.KT - 1);
   const int idx = (blockIdx.x % blocks_per_tile) * 256 + threadIdx.x;
   const int lrow = idx / C8, c8 = (idx % C8) * 8;
   const int b = t.b, row = t.row0 + lrow;
@@ -1098,7 +1105,7 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   const int merge_blocks = (F::RW * (DC / 8) + 255) / 256;
-  hipLaunchKernelGGL(k_attn_merge<F>, dim3(s.RT * merge_blocks), dim3(256), 0, st, (bf16 *)a.o,
+  hipLaunchKernelGGL(k_attn_merge<F>, dim3(s.G * merge_blocks), dim3(256), 0, st, (bf16 *)a.o,
                      (const unsigned char *)a.part, s, merge_blocks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int safe_wgs = s.RT * ((F::RW + S::RW - 1) / S::RW);

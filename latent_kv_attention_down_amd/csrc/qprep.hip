@@ -12,41 +12,77 @@
 namespace mla {
 namespace {
 
+// One wave per row; four columns per lane and step when cols % 4 == 0 (16-byte
+// loads, the gains read the same way), one otherwise.
 template <typename OutT, typename GT>
 __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *in, const GT *g, OutT *out,
                                                       int rows, int cols, float eps) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float *r = in + (int64_t)row * cols;
+  OutT *o = out + (int64_t)row * cols;
   float ss = 0.f;
+  if (cols % 4 == 0) {
+    const float4 *r4 = (const float4 *)r;
+    for (int c = lane; c < cols / 4; c += 64) {
+      const float4 v = r4[c];
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)cols + eps);
+    for (int c = lane; c < cols / 4; c += 64) {
+      const float4 v = r4[c];
+      float gn[4] = {1.f, 1.f, 1.f, 1.f};
+      if (g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gn[e] = to_f32(g[4 * c + e]);
+      o[4 * c + 0] = from_f32<OutT>(v.x * inv * gn[0]);
+      o[4 * c + 1] = from_f32<OutT>(v.y * inv * gn[1]);
+      o[4 * c + 2] = from_f32<OutT>(v.z * inv * gn[2]);
+      o[4 * c + 3] = from_f32<OutT>(v.w * inv * gn[3]);
+    }
+    return;
+  }
   for (int c = lane; c < cols; c += 64) ss += r[c] * r[c];
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)cols + eps);
   for (int c = lane; c < cols; c += 64) {
     float gain = g ? to_f32(g[c]) : 1.0f;
-    out[(int64_t)row * cols + c] = from_f32<OutT>(r[c] * inv * gain);
+    o[c] = from_f32<OutT>(r[c] * inv * gain);
   }
 }
 
-template <typename OutT>
+// PG pairs per thread (4 when the pair count allows: 32-byte reads of q^R).
+template <typename OutT, int PG>
 __global__ __launch_bounds__(256) void k_rope_q(RopeQArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one pair per thread
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx < a.n_zero) a.zero[idx] = 0;
-  const int P = a.d_rope / 2;
-  const int64_t total = (int64_t)a.M * a.n_h * P;
+  const int P = a.d_rope / 2, NG = P / PG;
+  const int64_t total = (int64_t)a.M * a.n_h * NG;
   if (idx >= total) return;
-  const int p = idx % P;
-  const int64_t mh = idx / P;
+  const int p0 = (int)(idx % NG) * PG;
+  const int64_t mh = idx / NG;
   const int h = mh % a.n_h;
   const int m = mh / a.n_h;
   const int i = m % a.T_q, n = i % a.tpf;
   const float pos[3] = {(float)(a.t0 + i / a.tpf), (float)(n / a.grid_w), (float)(n % a.grid_w)};
-  const float *src = a.q_r + (int64_t)m * a.n_h * a.d_rope + h * a.d_rope + 2 * p;
-  float re = src[0], im = src[1];
-  rope_rotate(re, im, pos[a.rope.axis[p]], a.rope.omega[p]);
-  OutT *dst = (OutT *)a.q_lat + mh * (a.d_c + a.d_rope) + a.d_c + 2 * p;
-  dst[0] = from_f32<OutT>(re * a.scale);
-  dst[1] = from_f32<OutT>(im * a.scale);
+  const float *src = a.q_r + (int64_t)m * a.n_h * a.d_rope + h * a.d_rope + 2 * p0;
+  float v[2 * PG];
+  if (PG == 4) {
+    const float4 lo = *(const float4 *)src, hi = *(const float4 *)(src + 4);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 2 * PG; ++e) v[e] = src[e];
+  }
+  OutT *dst = (OutT *)a.q_lat + mh * (a.d_c + a.d_rope) + a.d_c + 2 * p0;
+#pragma unroll
+  for (int q = 0; q < PG; ++q) {
+    rope_rotate(v[2 * q], v[2 * q + 1], pos[a.rope.axis[p0 + q]], a.rope.omega[p0 + q]);
+    dst[2 * q] = from_f32<OutT>(v[2 * q] * a.scale);
+    dst[2 * q + 1] = from_f32<OutT>(v[2 * q + 1] * a.scale);
+  }
 }
 
 template <typename T>
@@ -77,14 +113,20 @@ hipError_t rmsnorm_rows(const float *in, const void *g, void *out, int rows, int
 }
 
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st) {
-  int64_t total = (int64_t)a.M * a.n_h * (a.d_rope / 2);
+  const int P = a.d_rope / 2;
+  const bool by4 = P % 4 == 0;  // q^R rows are 16-byte aligned when d_rope % 8 == 0
+  int64_t total = (int64_t)a.M * a.n_h * (by4 ? P / 4 : P);
   if (a.n_zero > total) total = a.n_zero;
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
-  if (bf16_out)
-    hipLaunchKernelGGL(k_rope_q<bf16>, grid, dim3(256), 0, st, a);
+  if (bf16_out && by4)
+    hipLaunchKernelGGL((k_rope_q<bf16, 4>), grid, dim3(256), 0, st, a);
+  else if (bf16_out)
+    hipLaunchKernelGGL((k_rope_q<bf16, 1>), grid, dim3(256), 0, st, a);
+  else if (by4)
+    hipLaunchKernelGGL((k_rope_q<float, 4>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_rope_q<float>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_rope_q<float, 1>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 // Projection GEMMs of the MLA chunk step: C = alpha * A * B^T with both operands
 // K-contiguous (x W^T for row-major [out][in] weights).
 //  * bf16, direct loads (K a multiple of 32, 16-byte aligned rows): BM x BN tiles,
-//    waves of WTM x WTN built from 32x32x16 MFMAs.  KC-wide k chunks of A and B go
+//    waves of WTM x WTN built from 32x32x16 MFMAs (256x256 tiles of 128x64 waves for
+//    large problems, 256x128 / 128x128 / 128x64 tiles of 64x64 or 64x32 waves else).  KC-wide k chunks of A and B go
 //    through an NS-stage LDS ring filled by global_load_lds_dwordx4 (vector loads
 //    into registers top out near 34 GB/s per CU, the direct path near 100 GB/s for
 //    L2-resident operands).  16-byte chunk c of stage row r sits at chunk
@@ -127,7 +128,10 @@ struct GemmDma {
   static constexpr int A_LOADS = BM / RPL, B_LOADS = BN / RPL;
   static constexpr int LPW = (A_LOADS + B_LOADS) / NW;  // loads per wave per stage
   static constexpr int SB = (BM + BN) * ROWB;          // stage bytes
-  static constexpr size_t LDS = (size_t)SB * NS;
+  // the epilogue reuses the stages as a BM x (BN + one 16-byte piece) output tile
+  static constexpr int OUT_B = OUT_F32 ? 4 : 2;
+  static constexpr size_t EPI = (size_t)BM * (BN + 16 / OUT_B) * OUT_B;
+  static constexpr size_t LDS = (size_t)SB * NS > EPI ? (size_t)SB * NS : EPI;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(LPW * NW == A_LOADS + B_LOADS, "loads do not split over the waves");
   static_assert(NS >= 2 && NS <= 4, "stage count");
@@ -137,7 +141,9 @@ template <int KC>
 __device__ __forceinline__ int gswz(int row) { return (row >> 1) & (KC / 8 - 1); }
 
 template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32>
-__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm_dma(GemmArgs g) {
+__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64)
+__attribute__((amdgpu_waves_per_eu(WTM * WTN >= 128 * 64 ? 2 : 4, 8)))
+void k_gemm_dma(GemmArgs g) {
   using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32>;
   constexpr int TM = D::TM, TN = D::TN, LPW = D::LPW, RPL = D::RPL, CPR = KC / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -272,12 +278,11 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void k_gemm_dma(GemmA
   }
 }
 
-template <int BM, int BN, int WTM, int WTN, int KC, int NS>
-hipError_t launch_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
+template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32>
+hipError_t launch_dma(const GemmArgs &g, hipStream_t st) {
+  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32>;
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.batch);
-  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, false>;
-  const auto kern = out_f32 ? k_gemm_dma<BM, BN, WTM, WTN, KC, NS, true>
-                            : k_gemm_dma<BM, BN, WTM, WTN, KC, NS, false>;
+  const auto kern = k_gemm_dma<BM, BN, WTM, WTN, KC, NS, OUT_F32>;
   if (D::LDS > 65536) {
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)D::LDS);
@@ -287,9 +292,23 @@ hipError_t launch_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WTM, int WTN, int KC, int NS>
+hipError_t launch_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
+  return out_f32 ? launch_dma<BM, BN, WTM, WTN, KC, NS, true>(g, st)
+                 : launch_dma<BM, BN, WTM, WTN, KC, NS, false>(g, st);
+}
+
 template <int KC>
 hipError_t gemm_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
   const int64_t mt128 = (g.M + 127) / 128;
+  // Large problems (the 21-frame clip, batched requests): 256x256 tiles of eight
+  // 128x64 waves, two per SIMD, read 0.75 KB of LDS per MFMA instead of 1 KB and
+  // fetch 128 FLOP per byte instead of 85; bf16 output only (an fp32 output tile
+  // of that size does not fit the LDS).  Two 64-wide k stages measured faster than
+  // four 32-wide ones.
+  const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  if (!out_f32 && g.N >= 512 && tiles256 >= 512)
+    return launch_dma<256, 256, 128, 64, 64, 2, false>(g, st);
   if (g.N >= 1024) return launch_dma<256, 128, 64, 64, KC, 3>(g, out_f32, st);
   if (g.N % 128 == 0 && mt128 * (g.N / 128) * g.batch >= 200)
     return launch_dma<128, 128, 64, 64, KC, 4>(g, out_f32, st);

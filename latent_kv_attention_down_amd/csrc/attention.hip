@@ -14,12 +14,10 @@
 //    only: the score contraction S^T = K Q^T reads 16-byte K fragments, and the
 //    value contraction O^T = V^T P^T reads V^T fragments of the same rows with the
 //    LDS transpose load ds_read_b64_tr_b16, so no transposed copy is written;
-//  * k_latent_attn_w1 (the fast kernel where its registers fit): one wave per
-//    SIMD with 64 query rows, tiles brought in by direct global->LDS loads into an
-//    unpadded swizzled four-stage ring, and the softmax of one half tile
-//    interleaved with the score MFMAs of the next;  k_latent_attn: two waves per
-//    SIMD with 32 rows each, register-staged loads, waves skewed so one wave's
-//    softmax runs beside the other's MFMAs;
+//  * k_latent_attn_w1 (the fast kernel): one wave per SIMD with 64 query rows (32
+//    at d_c = 256, whose 64-row accumulators would not fit), tiles brought in by
+//    direct global->LDS loads into an unpadded swizzled four-stage ring, and the
+//    softmax of one half tile interleaved with the score MFMAs of the next;
 //  * S^T comes out of v_mfma_f32_32x32x16_bf16 with one query per lane column, so
 //    the row max needs one cross-lane step (lane l and l^32) and the bf16
 //    probabilities feed the next MFMA as its B operand without a shuffle;
@@ -115,14 +113,13 @@ __host__ __device__ __forceinline__ int rt_of(const Sched &s, int64_t f) {
   return b * s.RTb + k * s.blk_rt + (int)(r / blk_kt(s, k));
 }
 
-// DC/DR: latent and RoPE widths; QT: 32-row query tiles per wave; NW: waves per
-// workgroup; PIPE: 0 = one LDS stage (two barriers per tile), 1 = two stages,
-// 2 = three stages with skewed waves; WPC: workgroups resident per CU.
-template <int DC_, int DR_, int QT_, int NW_, int PIPE_, int WPC_, int PAD_ = 8>
+// Configuration of the safe kernel: DC/DR latent and RoPE widths, QT 32-row query
+// tiles per wave, NW waves per workgroup, one padded LDS stage of one key tile
+// (rows padded by PAD_ elements), filled through registers.
+template <int DC_, int DR_, int QT_, int NW_, int PAD_ = 8>
 struct Cfg {
-  static constexpr bool DIRECT = false;
-  static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_, WPC = WPC_, PIPE = PIPE_;
-  static constexpr int NBUF = PIPE == 2 ? 3 : (PIPE == 1 ? 2 : 1);
+  static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_;
+  static constexpr int NBUF = 1;
   static constexpr int NT = NW * 64;
   static constexpr int DK = DC + DR;
   static constexpr int KB = DK / 16;
@@ -135,18 +132,15 @@ struct Cfg {
   static constexpr int CH_PER_T = (CHUNKS + NT - 1) / NT;
   static constexpr int STAGE = BN * KS;       // elements per LDS stage
   static constexpr size_t LDS = (size_t)STAGE * 2 * NBUF;
-  static constexpr size_t REC = (size_t)RW * DC * 2 + (size_t)RW * 8;
-  static constexpr int WAVES_PER_SIMD = (NW / 4) * WPC;
   static_assert(NW % 4 == 0, "whole waves per SIMD");
   static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
 };
 
-// One wave per SIMD, 64 query rows per wave, key tiles brought into an unpadded
+// One wave per SIMD, QT x 32 query rows per wave, key tiles brought into an unpadded
 // swizzled four-stage LDS ring by direct global->LDS loads (k_latent_attn_w1).
-template <int DC_, int DR_>
+template <int DC_, int DR_, int QT_ = 2>
 struct CfgW {
-  static constexpr bool DIRECT = true;
-  static constexpr int DC = DC_, DR = DR_, QT = 2, NW = 4, WPC = 1, NBUF = 4;
+  static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = 4, WPC = 1, NBUF = 4;
   static constexpr int NT = NW * 64;
   static constexpr int DK = DC + DR;
   static constexpr int KB = DK / 16;
@@ -157,7 +151,6 @@ struct CfgW {
   static constexpr int STAGE = BN * DK;       // elements per LDS stage (no padding)
   static constexpr size_t LDS = (size_t)STAGE * 2 * NBUF;
   static constexpr size_t REC = (size_t)RW * DC * 2 + (size_t)RW * 8;
-  static constexpr int WAVES_PER_SIMD = 1;
   // After a row tile's first key tile, its reference max enters the score MFMAs as
   // their initial accumulator (-m), so the exponentials need no subtraction.
   static constexpr bool FOLD_MAX = true;
@@ -169,14 +162,14 @@ struct CfgW {
 template <int DC, int DR>
 struct Choice {
   using Fast = CfgW<DC, DR>;
-  using Safe = Cfg<DC, DR, 1, 4, 0, 1>;
+  using Safe = Cfg<DC, DR, 1, 4>;
 };
 // At d_c = 256 the 64-row O^T alone needs all 256 accumulation registers, so the
-// one-wave kernel would spill; two waves per SIMD with 32 rows each fit.
+// one-wave kernel takes 32 rows per wave there.
 template <>
 struct Choice<256, 32> {
-  using Fast = Cfg<256, 32, 1, 8, 2, 1, 56>;
-  using Safe = Cfg<256, 32, 1, 4, 0, 1>;
+  using Fast = CfgW<256, 32, 1>;
+  using Safe = Cfg<256, 32, 1, 4>;
 };
 
 // One workgroup's view of the ring: global -> registers -> LDS (one key-major tile
@@ -388,134 +381,6 @@ __device__ __forceinline__ void store_rows(bf16 *dst, const f32x16 (&O)[FT][QT],
     }
 }
 
-template <class C>
-__global__ __launch_bounds__(C::NT)
-__attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD)))
-void k_latent_attn(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
-                   bf16 *__restrict__ o, unsigned char *__restrict__ part, int *__restrict__ flags,
-                   Sched s) {
-  constexpr int DC = C::DC, QT = C::QT, KB = C::KB, FT = C::FT, RW = C::RW;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  Tile<C> tl;
-  tl.base = (bf16 *)lds;
-  tl.start0 = s.start0;
-  tl.len0 = s.len0;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int wg = blockIdx.x;
-  const int64_t begin = (int64_t)wg * s.T / s.G, end = (int64_t)(wg + 1) * s.T / s.G;
-
-  bf16x8 Qr[QT][KB];
-  f32x16 O[FT][QT];
-  bf16x8 P[BN / 16][QT];
-  float m[QT], l[QT];
-
-  // Pieces are taken last row tile first: a range that crosses a row-tile boundary
-  // then starts at key tile 0, so at step t nearly every workgroup reads key tile t
-  // (or t + a fixed offset) and the workgroups of one XCD share their L2 lines.
-  const int rt_first = rt_of(s, begin), rt_last = rt_of(s, end - 1);
-  for (int rt = rt_last; rt >= rt_first; --rt) {
-    const RowTile t = row_tile(s, rt);
-    const int kt0 = (int)((begin > t.f0 ? begin : t.f0) - t.f0);
-    const int kt1 = (int)((end < t.f0 + t.KT ? end : t.f0 + t.KT) - t.f0);
-    const int b = t.b, row0 = t.row0;
-    tl.nk = t.nk;
-    tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
-
-    load_queries<C::DK, QT, KB>(Qr, q, s, b, row0 + wave * QT * 32, l32, g);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      l[qt] = 0.f;
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[ft][qt][r] = 0.f;
-    }
-
-    // scores and probabilities of tile kt (into P)
-    auto softmax_tile = [&](int kt, int buf) {
-      f32x16 S[2][QT];
-      tl.scores(S, Qr, kt, buf, l32, g);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if (kt == kt0) m[qt] = tile_max<QT>(S, qt);  // fixed reference for this piece
-        l[qt] += exp_and_pack<QT>(S, P, qt, m[qt]);
-      }
-    };
-    auto compute = [&](int kt, int buf) {
-      softmax_tile(kt, buf);
-      tl.values(O, P, buf, lane);
-    };
-
-    tl.load(kt0, tid);
-    if (C::PIPE == 2) {
-      // Skewed waves: the second half of the workgroup (one wave per SIMD) takes
-      // its value MFMAs one tile late, so on every SIMD one wave's softmax VALU
-      // work runs beside the other wave's MFMAs.  Three LDS stages: tile kt+1 is
-      // written while tiles kt and kt-1 are read.
-      const bool lag = wave >= C::NW / 2;
-      tl.store(tid, kt0 % 3);
-      __syncthreads();
-      for (int kt = kt0; kt < kt1; ++kt) {
-        if (kt + 1 < kt1) tl.load(kt + 1, tid);
-        if (!lag) {
-          compute(kt, kt % 3);
-        } else {
-          if (kt > kt0) tl.values(O, P, (kt - 1) % 3, lane);
-          softmax_tile(kt, kt % 3);
-        }
-        if (kt + 1 < kt1) tl.store(tid, (kt + 1) % 3);
-        __syncthreads();
-      }
-      if (lag) tl.values(O, P, (kt1 - 1) % 3, lane);
-      __syncthreads();
-    } else if (C::PIPE == 1) {
-      tl.store(tid, 0);
-      __syncthreads();
-      for (int kt = kt0; kt < kt1; ++kt) {
-        const int cur = (kt - kt0) & 1;
-        if (kt + 1 < kt1) tl.load(kt + 1, tid);
-        compute(kt, cur);
-        if (kt + 1 < kt1) tl.store(tid, cur ^ 1);
-        __syncthreads();
-      }
-    } else {
-      for (int kt = kt0; kt < kt1; ++kt) {
-        __syncthreads();
-        tl.store(tid, 0);
-        __syncthreads();
-        if (kt + 1 < kt1) tl.load(kt + 1, tid);
-        compute(kt, 0);
-      }
-    }
-
-    const bool whole = (kt0 == 0 && kt1 == t.KT);
-    unsigned char *rec = part + (size_t)(wg + rt) * C::REC;
-    float *rec_m = (float *)(rec + (size_t)RW * DC * 2);
-    float *rec_l = rec_m + RW;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
-      // The reference key of the first tile has weight 1, so lt >= 1.  Any weight
-      // above 2^64 (a score more than 64 above the reference) makes lt exceed
-      // 2^64, as does inf or NaN: such a row tile is recomputed by the safe kernel.
-      // Sums above 2^64 made only of smaller weights are flagged too (harmless).
-      if (!(lt <= kFastSumLimit)) flags[rt] = 1;
-      const int lrow = wave * QT * 32 + qt * 32 + l32;
-      const int row = row0 + lrow;
-      if (row < t.row_end) {
-        bf16 *dst = whole ? o + ((int64_t)b * s.R + row) * DC : (bf16 *)rec + (int64_t)lrow * DC;
-        store_rows<FT, QT>(dst, O, qt, 1.0f / lt, g);
-        if (!whole && g == 0) {
-          rec_m[lrow] = m[qt];
-          rec_l[lrow] = lt;
-        }
-      }
-    }
-  }
-}
-
 // Chunk swizzle of the unpadded key tile: 16-byte chunk c of tile row r sits at
 // chunk position c ^ swz4(r) of that row.  With it the 32-row K fragment reads and
 // the V^T transpose reads below touch every LDS bank equally often.
@@ -707,26 +572,28 @@ __device__ __forceinline__ void wait_loads() {
 }
 
 // Instruction order of the value step: three V^T fragments (two reads each) in
-// flight, then per fragment its two MFMAs and the next fragment's reads.
-template <int NF>
+// flight, then per fragment its QT MFMAs and the next fragment's reads.
+template <int NF, int QT>
 __device__ __forceinline__ void order_values_step() {
   __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 }
 
-// Fast latent attention, one wave per SIMD.  Each wave owns 64 query rows (two
-// 32-row MFMA tiles) whose q_lat stays in registers; O^T (DC x 64 fp32) lives in
+// Fast latent attention, one wave per SIMD.  Each wave owns QT x 32 query rows
+// (64 at d_c <= 192, 32 at d_c = 256) whose q_lat stays in registers; O^T lives in
 // the accumulation registers.  Key tile kt is handled in three steps:
 //   1. S^T of keys 0-31 of kt, beside the softmax VALU work of keys 32-63 of kt-1;
 //   2. O^T += V^T P^T of tile kt-1, then the loads of tile kt+2 are issued;
 //   3. S^T of keys 32-63 of kt, beside the softmax VALU work of keys 0-31 of kt,
 // so the wave's own MFMAs cover its exponentials.  Four LDS stages: at the end of
 // step 3 tile kt+1 has landed (tile kt+2 may still be in flight), one barrier per
-// tile.  Reference max, flags, pieces and records are as in k_latent_attn.
+// tile.  A row tile whose piece covers all its key tiles is written directly; a
+// piece of a split tile goes to its record (normalised bf16 rows plus m and l)
+// for k_attn_merge.
 template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
@@ -820,7 +687,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
         exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend);
       });
       tl.values(O, P, prev, lane);
-      order_values_step<FT * (BN / 16)>();
+      order_values_step<FT * (BN / 16), QT>();
       __builtin_amdgcn_sched_barrier(0);
       // Tile kt+2 is requested only now: the transpose reads above would otherwise
       // make the compiler wait for these loads before the value step.
@@ -850,6 +717,10 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+      // The reference key of the first tile has weight 1, so lt >= 1.  Any weight
+      // above 2^64 (a score more than 64 above the reference) makes lt exceed 2^64,
+      // as does inf or NaN: such a row tile is recomputed by the safe kernel.
+      // Sums above 2^64 made only of smaller weights are flagged too (harmless).
       if (!(lt <= kFastSumLimit)) flags[rt] = 1;
       const int lrow = wave * QT * 32 + qt * 32 + l32;
       const int row = row0 + lrow;
@@ -1077,21 +948,13 @@ hipError_t allow_lds(K kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <class F>
-auto fast_kernel() {
-  if constexpr (F::DIRECT)
-    return k_latent_attn_w1<F>;
-  else
-    return k_latent_attn<F>;
-}
-
 template <int DC, int DR>
 hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   using F = typename Choice<DC, DR>::Fast;
   using S = typename Choice<DC, DR>::Safe;
   Sched s = make_sched(a, F::RW, a.grid * F::WPC);
   if (s.T <= 0) return hipSuccess;
-  const auto fast = fast_kernel<F>();
+  const auto fast = k_latent_attn_w1<F>;
   hipError_t e = allow_lds(fast, F::LDS);
   if (e == hipSuccess) e = allow_lds(k_latent_attn_safe<S>, S::LDS);
   if (e != hipSuccess) return e;

@@ -737,24 +737,37 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
 }
 
 // Merge the pieces of every row tile that more than one workgroup worked on.  The
-// grid walks the workgroup boundaries: boundary w (the first step of workgroup w)
-// falls inside at most one row tile, and a split tile is taken at the first
-// boundary inside it, so every split tile is merged exactly once and the launch
-// stays small however many row tiles there are.  One thread per (row, 8 latent
-// columns): it weighs each piece's normalised partial by l_p * 2^(m_p - max m) and
-// renormalises.
+// grid walks either the row tiles (unsplit ones exit at once) or, when there are
+// more row tiles than workgroups, the workgroup boundaries: boundary w (the first
+// step of workgroup w) falls inside at most one row tile, and a split tile is taken
+// at the first boundary inside it, so every split tile is merged exactly once and
+// the launch does not grow with the number of row tiles.  One thread per (row, 8
+// latent columns): it weighs each piece's normalised partial by l_p * 2^(m_p - max
+// m) and renormalises.
 template <class C>
 __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
                                                     const unsigned char *__restrict__ part, Sched s,
-                                                    int blocks_per_tile) {
+                                                    int blocks_per_tile, int by_boundary) {
   constexpr int DC = C::DC, RW = C::RW, C8 = DC / 8;
-  const int wb = blockIdx.x / blocks_per_tile;
-  if (wb == 0) return;
-  const int64_t f = (int64_t)wb * s.T / s.G;
-  const int rt = rt_of(s, f);
+  const int unit = blockIdx.x / blocks_per_tile;
+  int rt, g0;
+  if (by_boundary) {
+    if (unit == 0) return;
+    const int64_t f = (int64_t)unit * s.T / s.G;
+    rt = rt_of(s, f);
+    g0 = unit - 1;
+  } else {
+    rt = unit;
+    g0 = -1;
+  }
   const RowTile t = row_tile(s, rt);
-  if (f == t.f0 || wg_of(s, t.f0) != wb - 1) return;
-  const int g0 = wb - 1, g1 = wg_of(s, t.f0 + t.KT - 1);
+  if (by_boundary) {
+    if ((int64_t)unit * s.T / s.G == t.f0 || wg_of(s, t.f0) != g0) return;
+  } else {
+    g0 = wg_of(s, t.f0);
+  }
+  const int g1 = wg_of(s, t.f0 + t.KT - 1);
+  if (g0 == g1) return;
   const int idx = (blockIdx.x % blocks_per_tile) * 256 + threadIdx.x;
   const int lrow = idx / C8, c8 = (idx % C8) * 8;
   const int b = t.b, row = t.row0 + lrow;
@@ -968,8 +981,9 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   const int merge_blocks = (F::RW * (DC / 8) + 255) / 256;
-  hipLaunchKernelGGL(k_attn_merge<F>, dim3(s.G * merge_blocks), dim3(256), 0, st, (bf16 *)a.o,
-                     (const unsigned char *)a.part, s, merge_blocks);
+  const int by_boundary = s.RT > s.G;
+  hipLaunchKernelGGL(k_attn_merge<F>, dim3((by_boundary ? s.G : s.RT) * merge_blocks), dim3(256), 0,
+                     st, (bf16 *)a.o, (const unsigned char *)a.part, s, merge_blocks, by_boundary);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int safe_wgs = s.RT * ((F::RW + S::RW - 1) / S::RW);
   hipLaunchKernelGGL(k_latent_attn_safe<S>, dim3(safe_wgs), dim3(S::NT), S::LDS, st,

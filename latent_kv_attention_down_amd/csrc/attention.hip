@@ -16,7 +16,7 @@
 //    LDS transpose load ds_read_b64_tr_b16, so no transposed copy is written;
 //  * k_latent_attn_w1 (the fast kernel): one wave per SIMD with 64 query rows (32
 //    at d_c = 256, whose 64-row accumulators would not fit), tiles brought in by
-//    direct global->LDS loads into an unpadded swizzled four-stage ring, and the
+//    buffer loads straight into an unpadded swizzled four-stage LDS ring, and the
 //    softmax of one half tile interleaved with the score MFMAs of the next;
 //  * S^T comes out of v_mfma_f32_32x32x16_bf16 with one query per lane column, so
 //    the row max needs one cross-lane step (lane l and l^32) and the bf16
@@ -137,7 +137,7 @@ struct Cfg {
 };
 
 // One wave per SIMD, QT x 32 query rows per wave, key tiles brought into an unpadded
-// swizzled four-stage LDS ring by direct global->LDS loads (k_latent_attn_w1).
+// swizzled four-stage LDS ring by buffer loads into LDS (k_latent_attn_w1).
 template <int DC_, int DR_, int QT_ = 2>
 struct CfgW {
   static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = 4, WPC = 1, NBUF = 4;
@@ -387,9 +387,9 @@ __device__ __forceinline__ void store_rows(bf16 *dst, const f32x16 (&O)[FT][QT],
 __device__ __forceinline__ int swz4(int r) { return (r ^ (r >> 2)) & 3; }
 
 // Key tiles of the one-wave-per-SIMD kernel.  A tile is 64 ring rows of DK bf16,
-// unpadded and swizzled, brought in by global_load_lds_dwordx4: each load puts 64
-// lanes' 16 bytes at consecutive LDS chunk positions, so the swizzle is applied on
-// the global side (lane p of the tile fetches the chunk that belongs at position p).
+// unpadded and swizzled, brought in by buffer_load_dwordx4 ... lds: each load puts
+// 64 lanes' 16 bytes at consecutive LDS chunk positions, so the swizzle is applied
+// on the global side (lane p of the tile fetches the chunk that belongs at position p).
 template <class C>
 struct TileW {
   static constexpr int DK = C::DK, KB = C::KB, FT = C::FT, QT = C::QT, LOADS = C::LOADS;

@@ -97,6 +97,63 @@ def traffic_from_profiles(kernel_src, summary):
     return d.get("hbm_bytes_per_launch")
 
 
+def spread(v):
+    """mean, median, 10th and 90th percentile of a list of timings."""
+    v = sorted(v)
+    n = len(v)
+
+    def q(p):
+        return v[min(n - 1, max(0, int(round(p * (n - 1)))))]
+    return {"mean": round(sum(v) / n, 4), "median": round(q(0.5), 4), "p10": round(q(0.1), 4),
+            "p90": round(q(0.9), 4)}
+
+
+def ceilings(hip, stream):
+    """What this device sustains, next to the rated peaks the roofline uses: a loop of
+    independent bf16 MFMAs (libmla_probe.so, not the MLA path) and a 1 GiB device
+    copy (read + write bytes)."""
+    import torch
+    out = {}
+    path = os.path.join(ROOT, "latent_kv_attention_down_amd", "libmla_probe.so")
+    if os.path.exists(path):
+        probe = ctypes.CDLL(path)
+        probe.mla_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        probe.mla_probe_mfma_bf16_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+        probe.mla_probe_mfma_bf16_flop.restype = ctypes.c_double
+        blocks = torch.cuda.get_device_properties(0).multi_processor_count
+        iters = 4096
+        buf = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+        a, b = hip.event(), hip.event()
+        best = None
+        for _ in range(3):
+            hip.record(a, stream)
+            assert probe.mla_probe_mfma_bf16(blocks, iters, buf.data_ptr(), stream) == 0
+            hip.record(b, stream)
+            torch.cuda.synchronize()
+            t = hip.ms(a, b)
+            best = t if best is None else min(best, t)
+        out["mfma_bf16_tflops"] = round(probe.mla_probe_mfma_bf16_flop(blocks, iters) / (best * 1e-3)
+                                        / 1e12, 1)
+        hip.destroy(a)
+        hip.destroy(b)
+    else:
+        print(f"[bench] {path} missing: no MFMA ceiling", file=sys.stderr)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["hbm_copy_gbs"] = round(2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    out["note"] = "measured here; roofline fractions use the rated 2.5 PF bf16 and 8 TB/s"
+    return out
+
+
 def cpu_baseline(s, w_exact, x_window, n_tokens):
     """The oracle (fp64 NumPy, unabsorbed) on a bounded sample: n_tokens evenly
     spaced query tokens of the chunk, all heads, the full window (cache entries and
@@ -216,6 +273,25 @@ def main():
     hip.record(t_stop, stream)
     torch.cuda.synchronize()
     write_ms = hip.ms(t_start, t_stop) / nw
+    device_bytes = {"cache_per_request": L.cache[0].numel() * L.cache.element_size(),
+                    "workspace": int(ws.numel()),
+                    "peak_allocated": int(torch.cuda.max_memory_allocated())}
+
+    # cold cache write: 1 GiB written before each launch evicts the 256 MB last-level
+    # cache, so x and the weights come from HBM
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold_ev = [(hip.event(), hip.event()) for _ in range(10)]
+    for a, b in cold_ev:
+        flush.fill_(1)
+        hip.record(a, stream)
+        mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    cold_us = [1e3 * hip.ms(a, b) for a, b in cold_ev]
+    for a, b in cold_ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    del flush
 
     fl = step_flops(s)
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
@@ -250,6 +326,10 @@ def main():
         "chunk_attention_tflops": round(attn_tflops, 2),
         "cache_write_gbs": round(write_gbs, 1),
         "cache_write_us": round(write_ms * 1e3, 2),
+        "attention_ms": spread(attn_ms),
+        "window_read_gbs": round(s.batch * s.window_tokens * (s.d_c + s.d_rope) * 2
+                                 / (attn_avg * 1e-3) / 1e9, 1),
+        "cache_write_cold_us": spread(cold_us),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
@@ -262,9 +342,8 @@ def main():
                                  "traffic": cw_traffic,
                                  "kernel": "k_cache_write_dma (cache write)",
                                  "bytes_per_launch": wbytes},
-        "device_bytes": {"cache_per_request": L.cache[0].numel() * L.cache.element_size(),
-                         "workspace": int(ws.numel()),
-                         "peak_allocated": int(torch.cuda.max_memory_allocated())},
+        "device_bytes": device_bytes,
+        "ceilings": ceilings(hip, stream),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)

@@ -40,6 +40,21 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(fns) == set(mla.SIGNATURES), "binding and header disagree"
 
 
+def test_probe_library_exports_its_header():
+    """The ceiling probe (a library of its own, not the MLA path) exports what
+    include/mla_probe.h declares, and libmla.so does not carry it."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mla_probe.h")).read(),
+                  flags=re.S)
+    fns = sorted(set(re.findall(r"\b(mla_probe_[a-z0-9_]+)\s*\(", text)))
+    assert fns == ["mla_probe_mfma_bf16", "mla_probe_mfma_bf16_flop"]
+    probe = ctypes.CDLL(os.path.join(ROOT, "latent_kv_attention_down_amd", "libmla_probe.so"))
+    for name in fns:
+        assert hasattr(probe, name), name
+    assert not hasattr(mla.load(), "mla_probe_mfma_bf16")
+    probe.mla_probe_mfma_bf16_flop.restype = ctypes.c_double
+    assert probe.mla_probe_mfma_bf16_flop(2, 3) == 2 * 8 * 3 * 4 * 2 * 32 * 32 * 16
+
+
 def cfg_of(name, **kw):
     return mla.make_config(W.shape_by_name(name).with_(**kw))
 

@@ -195,7 +195,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4680)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (a known-size kernel "
-                         "for scaling FETCH_SIZE/WRITE_SIZE counters)")
+                         "for scaling FETCH_SIZE/WRITE_SIZE counters); the run then makes no "
+                         "other copies (no ceilings, no cold cache write)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured MFMA and copy ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -278,20 +281,23 @@ def main():
                     "peak_allocated": int(torch.cuda.max_memory_allocated())}
 
     # cold cache write: 1 GiB written before each launch evicts the 256 MB last-level
-    # cache, so x and the weights come from HBM
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cold_ev = [(hip.event(), hip.event()) for _ in range(10)]
-    for a, b in cold_ev:
-        flush.fill_(1)
-        hip.record(a, stream)
-        mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
-        hip.record(b, stream)
-    torch.cuda.synchronize()
-    cold_us = [1e3 * hip.ms(a, b) for a, b in cold_ev]
-    for a, b in cold_ev:
-        hip.destroy(a)
-        hip.destroy(b)
-    del flush
+    # cache, so x and the weights come from HBM (skipped in counter-calibration runs,
+    # whose only large copy must be the calibration one)
+    cold_us = None
+    if args.copy_calibration <= 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold_ev = [(hip.event(), hip.event()) for _ in range(10)]
+        for a, b in cold_ev:
+            flush.fill_(1)
+            hip.record(a, stream)
+            mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
+            hip.record(b, stream)
+        torch.cuda.synchronize()
+        cold_us = [1e3 * hip.ms(a, b) for a, b in cold_ev]
+        for a, b in cold_ev:
+            hip.destroy(a)
+            hip.destroy(b)
+        del flush
 
     fl = step_flops(s)
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
@@ -329,7 +335,7 @@ def main():
         "attention_ms": spread(attn_ms),
         "window_read_gbs": round(s.batch * s.window_tokens * (s.d_c + s.d_rope) * 2
                                  / (attn_avg * 1e-3) / 1e9, 1),
-        "cache_write_cold_us": spread(cold_us),
+        "cache_write_cold_us": spread(cold_us) if cold_us else None,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
@@ -343,7 +349,8 @@ def main():
                                  "kernel": "k_cache_write_dma (cache write)",
                                  "bytes_per_launch": wbytes},
         "device_bytes": device_bytes,
-        "ceilings": ceilings(hip, stream),
+        "ceilings": (None if args.no_ceilings or args.copy_calibration > 0
+                     else ceilings(hip, stream)),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)

@@ -12,7 +12,10 @@
  *     (§3.3 Eq. 7), evaluated in the absorbed latent form of App. E
  *     (Eq. 8-9 and 12), softmax over the window, value sum accumulated in
  *     latent space and up-projected per head through W^V_up (Eq. 2);
- *   - heads are mixed by W_O (§3.3).
+ *   - heads are mixed by W_O (§3.3), or, with the value up-projection absorbed,
+ *     by B_h = W_O,h W^V_up,h applied to the latent output (App. E Eq. 10-11);
+ *   - a chunk may also be a whole clip attended with chunk-causal blocks, the
+ *     training-time forward (§3.3 with the block masks of App. D.4).
  *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage).
@@ -28,7 +31,8 @@
  *     returns MLA_ERR_HIP and mla_last_error() gives the HIP message.  Device
  *     faults surface at the caller's next synchronisation.  No C++ exception
  *     crosses this boundary.
- *   - Two calls that write the same cache must not run concurrently.
+ *   - Two calls that write the same cache, or share a workspace, must not run
+ *     concurrently.
  */
 #ifndef MLA_H
 #define MLA_H

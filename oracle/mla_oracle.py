@@ -47,7 +47,7 @@ __all__ = [
     "rope_pair_split", "rope_omegas", "rope3d", "rmsnorm", "token_positions",
     "ring_slot", "window_frames", "ring_rows_for_window", "context_times", "visible_keys",
     "cache_entries", "expected_ring", "query_parts", "reconstruct_kv",
-    "attention_unabsorbed", "attention_absorbed", "value_absorbed_output",
+    "attention_unabsorbed", "attention_absorbed", "query_absorbed", "value_absorbed_output",
     "output_projection", "step", "cache_scalars_per_token", "dense_scalars_per_token",
 ]
 
@@ -269,6 +269,12 @@ def value_absorbed_output(s, w, h):
     return w["w_o"][:, h * s.d_head:(h + 1) * s.d_head] @ _head_rows(w["w_v_up"], h, s.d_head)
 
 
+def query_absorbed(s, w, h):
+    """A_h = (W_up,h^Q)^T W_up,h^K (App. E Eq. 8-9): the query-side absorption, so
+    that the content score is (c^Q)^T A_h c^KV; (d_q, d_c)."""
+    return _head_rows(w["w_q_up"], h, s.d_nope).T @ _head_rows(w["w_k_up"], h, s.d_nope)
+
+
 def attention_absorbed(s, w, c_q, q_rope, c, k_rope):
     """The inference reparameterisation of App. E, written as the paper states it:
     content score (c^Q)^T A_h c^KV with A_h = (W_up,h^Q)^T W_up,h^K (Eq. 8-9), the
@@ -278,7 +284,7 @@ def attention_absorbed(s, w, c_q, q_rope, c, k_rope):
     scale = 1.0 / np.sqrt(s.d_nope + s.d_rope)
     y = np.zeros((n, s.d_model))
     for h in range(s.n_heads):
-        a_h = _head_rows(w["w_q_up"], h, s.d_nope).T @ _head_rows(w["w_k_up"], h, s.d_nope)
+        a_h = query_absorbed(s, w, h)
         b_h = value_absorbed_output(s, w, h)
         sc = (c_q @ a_h @ c.T + q_rope[:, h, :] @ k_rope.T) * scale
         sc = sc - sc.max(axis=1, keepdims=True)

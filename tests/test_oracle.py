@@ -547,7 +547,7 @@ from oracle import mla_oracle as _M  # noqa: E402
 
 _ORIG = {k: getattr(_M, k) for k in ("rope3d", "rmsnorm", "reconstruct_kv",
                                      "attention_unabsorbed", "rope_omegas", "visible_keys",
-                                     "value_absorbed_output")}
+                                     "value_absorbed_output", "query_absorbed")}
 
 
 def _mut_rope_sign(v, pos, omegas, axes):
@@ -631,6 +631,16 @@ def _mut_b_next_head(s, w, h):
     return _ORIG["value_absorbed_output"](s, w, (h + 1) % s.n_heads)
 
 
+def _mut_a_transposed_query(s, w, h):
+    return _ORIG["query_absorbed"](s, w, h)[::-1]
+
+
+def _mut_a_other_head_keys(s, w, h):
+    wq = w["w_q_up"][h * s.d_nope:(h + 1) * s.d_nope]
+    g = (h + 1) % s.n_heads
+    return wq.T @ w["w_k_up"][g * s.d_nope:(g + 1) * s.d_nope]
+
+
 MUTANTS = {
     "rope rotation sign": dict(rope3d=_mut_rope_sign),
     "rope axis order": dict(rope3d=_mut_rope_axes),
@@ -647,6 +657,8 @@ MUTANTS = {
     "causal mask one block late": dict(visible_keys=_mut_mask_one_block_late),
     "B_h with W_O columns reversed": dict(value_absorbed_output=_mut_b_transposed_head),
     "B_h of the next head": dict(value_absorbed_output=_mut_b_next_head),
+    "A_h with the query latent reversed": dict(query_absorbed=_mut_a_transposed_query),
+    "A_h with another head's keys": dict(query_absorbed=_mut_a_other_head_keys),
 }
 
 

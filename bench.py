@@ -191,6 +191,11 @@ def main():
                     help="two-stage: per-head W^V_up then W_O; absorbed: y = sum_h B_h O_lat,h "
                          "with B_h = W_O,h W^V_up,h prepared once (FLOPs are counted as "
                          "two-stage either way)")
+    ap.add_argument("--query", choices=("direct", "absorbed"), default="absorbed",
+                    help="direct: W^Q_up, then (W^K_up,h)^T per head, and W^Q_R apart; "
+                         "absorbed: each query row from c^Q in one GEMM with [(W^K_up,h)^T "
+                         "W^Q_up,h ; W^Q_R,h] prepared once (FLOPs are counted as direct "
+                         "either way)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4680)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -228,6 +233,8 @@ def main():
     L = DeviceLayer(s, stored, batch=s.batch)
     if args.epilogue == "absorbed":
         L.absorb_value()  # weight preparation, once, outside the timed region
+    if args.query == "absorbed":
+        L.absorb_query()  # likewise
     tpf = s.tokens_per_frame
     for i, f in enumerate(ids):
         if f >= s.t0:
@@ -324,6 +331,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights; no trained model)",
         "config": {"workload": s.name, "batch": s.batch, "epilogue": args.epilogue,
+                   "query": args.query,
                    "query_tokens": s.chunk_tokens,
                    "window_tokens": s.window_tokens, "chunk_frames": s.chunk_frames,
                    "window_frames": s.window_frames, "heads": s.n_heads, "d_c": s.d_c,

@@ -104,6 +104,14 @@ typedef struct {
                          /* as written by mla_value_absorbed_weights.  When set,    */
                          /* mla_step computes y = sum_h B_h O_lat,h in one GEMM     */
                          /* and needs neither w_v_up nor w_o; NULL: W^V_up then W_O */
+  const void *w_qlat;    /* optional: the latent query projection, (n_h*(d_c +     */
+                         /* d_rope)) x d_q: rows h*(d_c+d_rope) .. +d_c-1 hold     */
+                         /* W_qk,h = (W^K_up,h)^T W^Q_up,h (App. E Eq. 8-9), the  */
+                         /* next d_rope rows W^Q_R,h, as written by                */
+                         /* mla_query_absorbed_weights.  When set, every absorbed  */
+                         /* query row comes from c^Q in one GEMM, its RoPE part     */
+                         /* rotated in place (then w_q_up, w_k_up and w_qr are not */
+                         /* needed); NULL: W^Q_up, (W^K_up,h)^T and W^Q_R apart     */
 } mla_weights;
 
 /* The chunk being generated and the window it sees.                             */
@@ -205,6 +213,20 @@ int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk
  * ALIGNMENT before any launch, MLA_ERR_HIP if the launch fails.
  */
 int mla_value_absorbed_weights(const mla_config *cfg, const mla_weights *w, void *w_b,
+                               void *stream);
+
+/*
+ * Query-side absorption (App. E Eq. 8-9), a weight preparation done once per
+ * weight set:
+ *   w_qlat ((n_h * (d_c + d_rope)), d_q) cfg->dtype, written: for head h, row
+ *        h*(d_c+d_rope) + c (c < d_c) column k is sum_n W^K_up[h*d_nope + n][c] *
+ *        W^Q_up[h*d_nope + n][k], summed in fp32 and rounded once; rows
+ *        h*(d_c+d_rope) + d_c + r copy W^Q_R[h*d_rope + r].  16-byte aligned,
+ *        caller-owned.
+ * Needs w->w_k_up, w->w_q_up and w->w_qr.  Asynchronous on `stream`; INVALID_ARG or
+ * ALIGNMENT before any launch, MLA_ERR_HIP if the launch fails.
+ */
+int mla_query_absorbed_weights(const mla_config *cfg, const mla_weights *w, void *w_qlat,
                                void *stream);
 
 /*

@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGNMENT, MLA_ERR_WORKSPACE,
     MLA_ERR_HIP, MLA_BF16, MLA_F32, MLA_ROPE_AT_WRITE, MLA_ROPE_AT_READ, Config, Weights, Chunk,
     MLAError, load, make_config, make_chunk, make_weights, validate, workspace_bytes, cache_bytes, cache_write,
-    chunk_attention, step, value_absorbed_weights, latent_attention, set_timing_events, attention_grid, status_string,
+    chunk_attention, step, value_absorbed_weights, query_absorbed_weights, latent_attention,
+    set_timing_events, attention_grid, status_string,
     last_error, SIGNATURES, LIB_PATH,
 )

@@ -30,7 +30,7 @@ class Config(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("w_kv_down", "w_kr", "g_kv", "w_q_down", "g_q", "w_q_up",
-                                   "w_qr", "w_k_up", "w_v_up", "w_o", "w_b")]
+                                   "w_qr", "w_k_up", "w_v_up", "w_o", "w_b", "w_qlat")]
 
 
 class Chunk(ctypes.Structure):
@@ -49,6 +49,7 @@ SIGNATURES = {
     "mla_step": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_latent_attention": (ctypes.c_int, [_P(Config), _P(Chunk), _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_value_absorbed_weights": (ctypes.c_int, [_P(Config), _P(Weights), _vp, _vp]),
+    "mla_query_absorbed_weights": (ctypes.c_int, [_P(Config), _P(Weights), _vp, _vp]),
     "mla_set_timing_events": (None, [_vp, _vp]),
     "mla_attention_grid": (ctypes.c_int, [_P(Config), _P(Chunk)]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -164,6 +165,12 @@ def step(cfg, weights, chunk, x, cache, y, workspace, stream=None):
 def value_absorbed_weights(cfg, weights, w_b, stream=None):
     _check(load().mla_value_absorbed_weights(ctypes.byref(cfg), ctypes.byref(weights), _ptr(w_b),
                                              _stream(stream)), "mla_value_absorbed_weights")
+
+
+def query_absorbed_weights(cfg, weights, w_qlat, stream=None):
+    _check(load().mla_query_absorbed_weights(ctypes.byref(cfg), ctypes.byref(weights),
+                                             _ptr(w_qlat), _stream(stream)),
+           "mla_query_absorbed_weights")
 
 
 def latent_attention(cfg, chunk, q_lat, cache, o_lat, workspace, stream=None):

@@ -197,13 +197,13 @@ int validate_weights(const mla_config &c, const mla_weights *w, bool write, bool
                      bool heads, bool project) {
   if (!w) return fail(MLA_ERR_INVALID_ARG, "weights is NULL");
   if (write && (!w->w_kv_down || !w->w_kr)) return fail(MLA_ERR_INVALID_ARG, "w_kv_down/w_kr NULL");
-  if (attend && (!w->w_q_down || !w->w_q_up || !w->w_qr || !w->w_k_up))
-    return fail(MLA_ERR_INVALID_ARG, "a query projection or w_k_up is NULL");
+  if (attend && (!w->w_q_down || (!w->w_qlat && (!w->w_q_up || !w->w_k_up || !w->w_qr))))
+    return fail(MLA_ERR_INVALID_ARG, "need w_q_down, and w_qlat or all of w_q_up, w_k_up, w_qr");
   if (heads && !w->w_v_up) return fail(MLA_ERR_INVALID_ARG, "w_v_up is NULL");
   if (project && !w->w_b && (!w->w_v_up || !w->w_o))
     return fail(MLA_ERR_INVALID_ARG, "need w_b, or w_v_up and w_o");
   const void *ptrs[] = {w->w_kv_down, w->w_kr, w->w_q_down, w->w_q_up, w->w_qr,
-                        w->w_k_up,    w->w_v_up, w->w_o,    w->w_b};
+                        w->w_k_up,    w->w_v_up, w->w_o,    w->w_b, w->w_qlat};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "weights must be 16-byte aligned");
   (void)c;
@@ -417,19 +417,28 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
                            c.d_model, 1, 1.f),
                    true, st, "query down-projection"));
   MLA_HIP(mla::rmsnorm_rows(u_q, w.g_q, c_q, (int)d.M, c.d_q, c.rms_eps, bf, st), "query rmsnorm");
-  // q^nope = W^Q_up c^Q (Eq. 4), q^R = W^Q_R c^Q (Eq. 6)
-  MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_q_up, c.d_q, 0, q_nope, (int64_t)nh * c.d_nope, 0,
-                           d.M, nh * c.d_nope, c.d_q, 1, 1.f),
-                   false, st, "query up-projection"));
-  MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qr, c.d_q, 0, q_r, (int64_t)nh * c.d_rope, 0, d.M,
-                           nh * c.d_rope, c.d_q, 1, 1.f),
-                   true, st, "positional query projection"));
-  // q~_h = (W^K_up,h)^T q^nope_h, scaled (App. E Eq. 8-9 applied to the query)
-  MLA_HIP(mla::transpose_heads(w.w_k_up, w_t, nh, c.d_nope, c.d_c, (int)d.esz, st), "key up transpose");
-  MLA_TRY(run_gemm(c, gemm(q_nope, (int64_t)nh * c.d_nope, c.d_nope, w_t, c.d_nope,
-                           (int64_t)c.d_c * c.d_nope, q_lat, (int64_t)nh * d.DK, d.DK, d.M, c.d_c,
-                           c.d_nope, nh, scale),
-                   false, st, "key absorption"));
+  if (w.w_qlat) {
+    // every absorbed query row [q~_h | q^R_h] = W_qlat,h c^Q, scaled, in one GEMM:
+    // W_qlat,h = [(W^K_up,h)^T W^Q_up,h ; W^Q_R,h] prepared once (App. E Eq. 8-9)
+    MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qlat, c.d_q, 0, q_lat, (int64_t)nh * d.DK, 0, d.M,
+                             (int)(nh * d.DK), c.d_q, 1, scale),
+                     false, st, "absorbed query projection"));
+  } else {
+    // q^R = W^Q_R c^Q (Eq. 6); q^nope = W^Q_up c^Q (Eq. 4), then q~_h =
+    // (W^K_up,h)^T q^nope_h, scaled (App. E Eq. 8-9 applied to the query)
+    MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qr, c.d_q, 0, q_r, (int64_t)nh * c.d_rope, 0, d.M,
+                             nh * c.d_rope, c.d_q, 1, 1.f),
+                     true, st, "positional query projection"));
+    MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_q_up, c.d_q, 0, q_nope, (int64_t)nh * c.d_nope, 0,
+                             d.M, nh * c.d_nope, c.d_q, 1, 1.f),
+                     false, st, "query up-projection"));
+    MLA_HIP(mla::transpose_heads(w.w_k_up, w_t, nh, c.d_nope, c.d_c, (int)d.esz, st),
+            "key up transpose");
+    MLA_TRY(run_gemm(c, gemm(q_nope, (int64_t)nh * c.d_nope, c.d_nope, w_t, c.d_nope,
+                             (int64_t)c.d_c * c.d_nope, q_lat, (int64_t)nh * d.DK, d.DK, d.M, c.d_c,
+                             c.d_nope, nh, scale),
+                     false, st, "key absorption"));
+  }
   // RoPE3D(q^R_h) into the last d_rope columns, same scale (Eq. 6, 12)
   mla::RopeQArgs rq;
   rq.q_r = q_r;
@@ -446,6 +455,8 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
   rq.rope = rope_table(c);
   rq.zero = (int *)(ws + L.flags);  // the attention's overflow flags (bf16 path)
   rq.n_zero = (int)L.n_flags;
+  rq.in_place = w.w_qlat != nullptr;
+  if (rq.in_place) rq.q_r = nullptr;
   MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
   // read-time rotation: gather the sink and local frames in context order and
   // rotate k^R at window-local positions (§3.2 Eq. 5, App. D.4-D.5)
@@ -565,6 +576,22 @@ int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk
                            (int64_t)c.n_heads * c.d_head, 0, y, c.d_model, 0, d.M, c.d_model,
                            c.n_heads * c.d_head, 1, 1.f),
                    false, st, "output projection"));
+  return MLA_OK;
+}
+
+int mla_query_absorbed_weights(const mla_config *cfg, const mla_weights *w, void *w_qlat,
+                               void *stream) {
+  g_last_error.clear();
+  MLA_TRY(validate_config(cfg));
+  if (!w || !w->w_k_up || !w->w_q_up || !w->w_qr)
+    return fail(MLA_ERR_INVALID_ARG, "need w_k_up, w_q_up and w_qr");
+  if (!w_qlat) return fail(MLA_ERR_INVALID_ARG, "w_qlat is NULL");
+  if (!aligned16(w->w_k_up) || !aligned16(w->w_q_up) || !aligned16(w->w_qr) || !aligned16(w_qlat))
+    return fail(MLA_ERR_ALIGNMENT, "w_k_up, w_q_up, w_qr and w_qlat must be 16-byte aligned");
+  MLA_HIP(mla::absorb_query(w->w_k_up, w->w_q_up, w->w_qr, w_qlat, cfg->n_heads, cfg->d_nope,
+                            cfg->d_c, cfg->d_rope, cfg->d_q, cfg->dtype == MLA_BF16,
+                            (hipStream_t)stream),
+          "query absorption");
   return MLA_OK;
 }
 

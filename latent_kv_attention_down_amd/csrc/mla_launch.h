@@ -53,6 +53,7 @@ struct RopeQArgs {
   RopeTable rope;
   int *zero;   // n_zero ints set to 0 on the way (the attention's overflow flags), or null
   int n_zero;
+  bool in_place;  // q_r is null: rotate the (already scaled) RoPE columns of q_lat in place
 };
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st);
 
@@ -73,6 +74,11 @@ hipError_t assemble_window(const AssembleArgs &a, bool bf16, hipStream_t st);
 // w_t[h][c][n] = w_k_up[h*d_nope + n][c]  (per-head transpose, element size esz).
 hipError_t transpose_heads(const void *w, void *w_t, int n_h, int d_nope, int d_c, int esz,
                            hipStream_t st);
+
+// Latent query projection [n_h*(d_c+d_rope)][d_q]: per head W_qk,h = (W^K_up,h)^T
+// W^Q_up,h, then the head's W^Q_R rows.
+hipError_t absorb_query(const void *w_k, const void *w_q, const void *w_r, void *w_out, int n_h,
+                        int d_nope, int d_c, int d_rope, int d_q, bool bf16_io, hipStream_t st);
 
 // B = [B_1 .. B_nh], B_h = W_O[:, h*d_h:(h+1)*d_h] W^V_up,h, stored [d][n_h*d_c].
 hipError_t absorb_value(const void *w_o, const void *w_v, void *w_b, int d, int n_h, int d_h,

@@ -66,22 +66,28 @@ __global__ __launch_bounds__(256) void k_rope_q(RopeQArgs a) {
   const int m = mh / a.n_h;
   const int i = m % a.T_q, n = i % a.tpf;
   const float pos[3] = {(float)(a.t0 + i / a.tpf), (float)(n / a.grid_w), (float)(n % a.grid_w)};
-  const float *src = a.q_r + (int64_t)m * a.n_h * a.d_rope + h * a.d_rope + 2 * p0;
+  OutT *dst = (OutT *)a.q_lat + mh * (a.d_c + a.d_rope) + a.d_c + 2 * p0;
   float v[2 * PG];
-  if (PG == 4) {
+  float scale = a.scale;
+  if (a.in_place) {  // the GEMM already wrote scale * q^R here
+#pragma unroll
+    for (int e = 0; e < 2 * PG; ++e) v[e] = to_f32(dst[e]);
+    scale = 1.f;
+  } else if (PG == 4) {
+    const float *src = a.q_r + (int64_t)m * a.n_h * a.d_rope + h * a.d_rope + 2 * p0;
     const float4 lo = *(const float4 *)src, hi = *(const float4 *)(src + 4);
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   } else {
+    const float *src = a.q_r + (int64_t)m * a.n_h * a.d_rope + h * a.d_rope + 2 * p0;
 #pragma unroll
     for (int e = 0; e < 2 * PG; ++e) v[e] = src[e];
   }
-  OutT *dst = (OutT *)a.q_lat + mh * (a.d_c + a.d_rope) + a.d_c + 2 * p0;
 #pragma unroll
   for (int q = 0; q < PG; ++q) {
     rope_rotate(v[2 * q], v[2 * q + 1], pos[a.rope.axis[p0 + q]], a.rope.omega[p0 + q]);
-    dst[2 * q] = from_f32<OutT>(v[2 * q] * a.scale);
-    dst[2 * q + 1] = from_f32<OutT>(v[2 * q + 1] * a.scale);
+    dst[2 * q] = from_f32<OutT>(v[2 * q] * scale);
+    dst[2 * q + 1] = from_f32<OutT>(v[2 * q + 1] * scale);
   }
 }
 

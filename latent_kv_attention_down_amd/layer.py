@@ -53,6 +53,17 @@ class DeviceLayer:
         self.weights = _lib.make_weights(self.tensors)
         return w_b
 
+    def absorb_query(self):
+        """Compute the latent query projection (per head (W^K_up,h)^T W^Q_up,h, then
+        W^Q_R,h) on the device and make the step build the absorbed query with it."""
+        s = self.shape
+        w_qlat = torch.empty((s.n_heads * (s.d_c + s.d_rope), s.d_q), dtype=self.tdtype,
+                             device=self.device)
+        _lib.query_absorbed_weights(self.cfg, self.weights, w_qlat)
+        self.tensors["w_qlat"] = w_qlat
+        self.weights = _lib.make_weights(self.tensors)
+        return w_qlat
+
     def chunk(self, chunk_frames, t0, n_valid_frames, causal_frames=0):
         return _lib.make_chunk(self.batch, chunk_frames, t0, n_valid_frames, causal_frames)
 

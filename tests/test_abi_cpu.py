@@ -258,6 +258,28 @@ def test_value_absorbed_weights_checks_before_launch(lib):
                         4096, n, None) == mla.MLA_ERR_ALIGNMENT
 
 
+def test_query_absorbed_weights_checks_before_launch(lib):
+    """mla_query_absorbed_weights needs W^K_up, W^Q_up, W^Q_R and an aligned output; a
+    step accepts w_qlat in place of all three."""
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    fake = {n: 4096 for n, _ in mla.Weights._fields_}
+    assert lib.mla_query_absorbed_weights(ctypes.byref(cfg), ctypes.byref(mla.Weights(**fake)),
+                                          None, None) == mla.MLA_ERR_INVALID_ARG
+    for missing in ("w_k_up", "w_q_up", "w_qr"):
+        w = mla.Weights(**dict(fake, **{missing: None}))
+        assert lib.mla_query_absorbed_weights(ctypes.byref(cfg), ctypes.byref(w), 4096,
+                                              None) == mla.MLA_ERR_INVALID_ARG, missing
+    ch = chunk_of(s)
+    n = mla.workspace_bytes(cfg, ch)
+    wt = mla.Weights(**dict(fake, w_qr=None, w_qlat=None))
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
+                        4096, n, None) == mla.MLA_ERR_INVALID_ARG
+    wt = mla.Weights(**dict(fake, w_q_up=None, w_k_up=None, w_qr=None, w_qlat=4100))
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
+                        4096, n, None) == mla.MLA_ERR_ALIGNMENT
+
+
 def test_status_strings(lib):
     for code, name in ((0, "MLA_OK"), (-1, "MLA_ERR_INVALID_ARG"), (-2, "MLA_ERR_UNSUPPORTED"),
                        (-3, "MLA_ERR_ALIGNMENT"), (-4, "MLA_ERR_WORKSPACE"), (-5, "MLA_ERR_HIP")):

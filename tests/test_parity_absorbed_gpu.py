@@ -1,8 +1,9 @@
-"""GPU parity of the value-absorbed output (VideoMLA App. E Eq. 10-11): the device
-computes B_h = W_O,h W^V_up,h once per weight set, and mla_step then maps the
-latent attention output to the model width with one GEMM.  B against the oracle's
-B_h, and the step's y against the oracle's unabsorbed step, at the usual
-tolerances, through the C ABI."""
+"""GPU parity of the absorbed weight forms of VideoMLA App. E: B_h = W_O,h W^V_up,h
+(Eq. 10-11), with which mla_step maps the latent attention output to the model width
+in one GEMM, and W_qk,h = (W^K_up,h)^T W^Q_up,h (Eq. 8-9), stacked with W^Q_R,h so
+that each absorbed query row is one GEMM from c^Q.  Each prepared weight against the oracle's, and the
+steps' y against the oracle's unabsorbed step, at the usual tolerances, through the
+C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -31,9 +32,55 @@ def test_absorbed_weights(name):
     assert_close(to_host(w_b), oracle_b(run), TOL[s.dtype], "B")
 
 
-def absorbed(run):
+def oracle_wqlat(run):
+    """Per head: A_h^T (the oracle's A_h of App. E Eq. 8-9, transposed), then W^Q_R,h."""
+    s = run.s
+    parts = []
+    for h in range(s.n_heads):
+        parts.append(O.query_absorbed(s, run.w, h).T)
+        parts.append(run.w["w_qr"][h * s.d_rope:(h + 1) * s.d_rope])
+    return np.concatenate(parts, axis=0)
+
+
+@pytest.mark.parametrize("name", ["tiny-f32", "wan1.3b-w21"])
+def test_query_absorbed_weights(name):
+    run = Run(W.shape_by_name(name))
+    w_qlat = run.L.absorb_query()
+    torch.cuda.synchronize()
+    s = run.s
+    assert tuple(w_qlat.shape) == (s.n_heads * (s.d_c + s.d_rope), s.d_q)
+    assert_close(to_host(w_qlat), oracle_wqlat(run), TOL[s.dtype], "W_qlat")
+
+
+def absorbed(run, query=False):
     run.L.absorb_value()
+    if query:
+        run.L.absorb_query()
     return run
+
+
+def query_absorbed(run):
+    run.L.absorb_query()
+    return run
+
+
+def test_query_absorbed_step_small_bf16():
+    full_step(query_absorbed(Run(small_wan(), random_gains=True)))
+
+
+def test_both_absorbed_step_fp32():
+    full_step(absorbed(Run(W.shape_by_name("tiny-f32"), random_gains=True), query=True))
+
+
+def test_both_absorbed_step_causal_sink():
+    s = small_wan(rope_at_read=True, sink_frames=1, window_frames=4, chunk_frames=4, t0=8,
+                  n_valid_frames=4, causal_frames=2)
+    full_step(absorbed(Run(s, batch=2), query=True))
+
+
+def test_both_absorbed_step_full_size_sampled():
+    s = W.shape_by_name("wan1.3b-w21")
+    full_step(absorbed(Run(s), query=True), check_cache=False, sample=sample_rows(s))
 
 
 def test_absorbed_step_small_bf16():

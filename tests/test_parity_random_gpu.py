@@ -41,13 +41,15 @@ def draw_case(seed):
         ch = mla.make_chunk(1, s.chunk_frames, s.t0, s.n_valid_frames, s.causal_frames)
         if mla.validate(mla.make_config(s), ch) != mla.MLA_OK:
             continue
-        return s, int(rng.integers(1, 3)), bool(rng.integers(2))
+        return s, int(rng.integers(1, 3)), bool(rng.integers(2)), bool(rng.integers(2))
 
 
 @pytest.mark.parametrize("seed", range(24))
 def test_random_configuration(seed):
-    s, batch, absorbed = draw_case(seed)
+    s, batch, absorbed, query = draw_case(seed)
     run = Run(s, batch=batch, random_gains=True, seed=seed)
     if absorbed:
         run.L.absorb_value()
+    if query:
+        run.L.absorb_query()
     full_step(run)

@@ -21,6 +21,12 @@
 //  * S^T comes out of v_mfma_f32_32x32x16_bf16 with one query per lane column, so
 //    the row max needs one cross-lane step (lane l and l^32) and the bf16
 //    probabilities feed the next MFMA as its B operand without a shuffle;
+//  * the fast kernel issues its score MFMAs as inline asm with architectural VGPR
+//    destinations: O fills the accumulation registers, and with S there as well
+//    the compiler moved every score in and out of them (two register moves per
+//    score element, in blocks the matrix unit could not hide).  The compiler
+//    cannot see these MFMAs, so each score half ends with an explicit wait for
+//    their results before any VALU instruction reads them;
 //  * fast path: each row's softmax reference is the max of the first key tile the
 //    workgroup sees for it and is never moved, so O is never rescaled inside the
 //    loop (a rescale would drag the AGPR-resident accumulators through VGPRs).
@@ -33,6 +39,8 @@
 //    the same work.  A row tile finished by one workgroup is written directly; one
 //    split across workgroups leaves normalised bf16 partials plus (m, l) per row,
 //    merged by k_attn_merge in a fixed order (deterministic, no atomics).
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_launch.h"
 
@@ -154,6 +162,11 @@ struct CfgW {
   // After a row tile's first key tile, its reference max enters the score MFMAs as
   // their initial accumulator (-m), so the exponentials need no subtraction.
   static constexpr bool FOLD_MAX = true;
+  // LDS fragments read ahead of their MFMAs in the score and value contractions.
+  static constexpr int DS = 3, DV = 3;
+  // Score MFMAs issued so that S stays in architectural VGPRs (see TileW::scores),
+  // where q_lat takes at most 112 of them (more would spill).
+  static constexpr bool ASM_SCORES = DK * QT <= 448;
   static_assert(CPR % 4 == 0 && LOADS * NW * 64 == BN * CPR, "tile does not split into loads");
   static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
 };
@@ -443,10 +456,10 @@ struct TileW {
   }
 
   // S^T of one 32-key half T of the tile for both query tiles.  K fragments run
-  // three k-blocks ahead of their MFMAs; after the MFMA of (k-block kb, query tile
+  // C::DS k-blocks ahead of their MFMAs; after the MFMA of (k-block kb, query tile
   // qt) the caller's work(2kb + qt) is emitted, each group fenced so the order
   // stays MFMA / VALU / MFMA / VALU.
-  template <int T, class Work>
+  template <int T, bool ZERO = false, class Work>
   __device__ __forceinline__ void scores(f32x16 (&S)[QT], const bf16x8 (&Qr)[QT][KB],
                                          const f32x16 (&init)[QT], int buf, int l32, int g,
                                          Work &&work) const {
@@ -456,7 +469,7 @@ struct TileW {
     const bf16 *rb = Ks(buf) + (T * 32 + l32) * DK;
     const bf16 *kr[2] = {rb + ((g ^ sw) * 8), rb + (((2 + g) ^ sw) * 8)};
     auto kfrag = [&](int kb) { return *(const bf16x8 *)(kr[kb & 1] + (kb >> 1) * 32); };
-    constexpr int D = 3;  // fragments in flight
+    constexpr int D = C::DS;  // fragments in flight
     bf16x8 fr[D + 1];
 #pragma unroll
     for (int kb = 0; kb < D; ++kb) fr[kb] = kfrag(kb);
@@ -466,44 +479,84 @@ struct TileW {
       if (kb + D < KB) fr[(kb + D) % (D + 1)] = kfrag(kb + D);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        S[qt] = mfma32(fr[kb % (D + 1)], Qr[qt][kb], kb == 0 ? init[qt] : S[qt]);
+        if constexpr (C::ASM_SCORES) {
+          if (kb == 0 && ZERO)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                         : "=&v"(S[qt])
+                         : "v"(fr[kb % (D + 1)]), "v"(Qr[qt][kb]));
+          else if (kb == 0)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
+                         : "=&v"(S[qt])
+                         : "v"(fr[kb % (D + 1)]), "v"(Qr[qt][kb]), "v"(init[qt]));
+          else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+v"(S[qt])
+                         : "v"(fr[kb % (D + 1)]), "v"(Qr[qt][kb]));
+        } else {
+          S[qt] = mfma32(fr[kb % (D + 1)], Qr[qt][kb], kb == 0 ? init[qt] : S[qt]);
+        }
         work(kb * QT + qt);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
-
-  // O^T += V^T P^T over the tile's four 16-key blocks (fragment mapping as in
-  // Tile::values, addresses through the swizzle); P holds packed bf16 pairs.
-  __device__ __forceinline__ void values(f32x16 (&O)[FT][QT], const u32x4 (&P)[BN / 16][QT],
-                                         int buf, int lane) const {
-    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-    const int G = lane >> 4, r = lane & 15, g = lane >> 5;
-    const bf16 *vt[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 8 * h + 4 * g + (r >> 2);
-      const int chunk = (2 * (G & 1) + ((r & 3) >> 1)) ^ swz4(row);
-      vt[h] = Ks(buf) + row * DK + chunk * 8 + (r & 1) * 4;
-    }
-#pragma unroll
-    for (int i = 0; i < FT * (BN / 16); ++i) {
-      const int off = (i % (BN / 16)) * 16 * DK + (i / (BN / 16)) * 32;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(vt[0] + off));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(vt[1] + off));
-      const bf16x8 f =
-          __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        O[i / (BN / 16)][qt] = mfma32(f, __builtin_bit_cast(bf16x8, P[i % (BN / 16)][qt]),
-                                      O[i / (BN / 16)][qt]);
+    if constexpr (C::ASM_SCORES) {
+      // The compiler does not see the MFMAs above, so it cannot space their
+      // consumers: wait out the VGPR write latency of the last ones here (24 wait
+      // states, tied to S so that no read of S moves above it).
+      static_assert(QT == 1 || QT == 2, "drain covers one or two query tiles");
+      if constexpr (QT == 2)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
+      else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]));
     }
   }
 };
+
+// O^T += V^T P^T over key blocks KB0 .. KB0+NKB-1 (16 keys each) of the tile, V^T
+// fragments read with ds_read_b64_tr_b16 as in Tile::values (addresses through the
+// swizzle) C::DV ahead of their MFMAs; P holds packed bf16 pairs.  The caller's
+// work(i) follows the MFMA of (fragment i / QT, query tile i % QT), each group fenced.
+template <class C, int KB0, int NKB, class Work>
+__device__ __forceinline__ void values_part(const TileW<C> &tl, f32x16 (&O)[C::FT][C::QT],
+                                            const u32x4 (&P)[BN / 16][C::QT], int buf, int lane,
+                                            Work &&work) {
+  typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+  constexpr int DK = C::DK, FT = C::FT, QT = C::QT, NF = FT * NKB, D = C::DV;
+  const int G = lane >> 4, r = lane & 15, g = lane >> 5;
+  const bf16 *vt[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * h + 4 * g + (r >> 2);
+    const int chunk = (2 * (G & 1) + ((r & 3) >> 1)) ^ swz4(row);
+    vt[h] = tl.Ks(buf) + row * DK + chunk * 8 + (r & 1) * 4;
+  }
+  auto vfrag = [&](int i) {
+    const int off = (KB0 + i % NKB) * 16 * DK + (i / NKB) * 32;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(vt[0] + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(vt[1] + off));
+    return __builtin_bit_cast(bf16x8,
+                              (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8 fr[D + 1];
+#pragma unroll
+  for (int i = 0; i < D; ++i) fr[i] = vfrag(i);
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + D < NF) fr[(i + D) % (D + 1)] = vfrag(i + D);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      O[i / NKB][qt] = mfma32(fr[i % (D + 1)],
+                              __builtin_bit_cast(bf16x8, P[KB0 + i % NKB][qt]), O[i / NKB][qt]);
+      work(i * QT + qt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
 
 // Keys of half T past nk get -inf (only the window's last tile has any).
 template <int QT>
@@ -571,18 +624,6 @@ __device__ __forceinline__ void wait_loads() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Instruction order of the value step: three V^T fragments (two reads each) in
-// flight, then per fragment its QT MFMAs and the next fragment's reads.
-template <int NF, int QT>
-__device__ __forceinline__ void order_values_step() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-}
-
 // Fast latent attention, one wave per SIMD.  Each wave owns QT x 32 query rows
 // (64 at d_c <= 192, 32 at d_c = 256) whose q_lat stays in registers; O^T lives in
 // the accumulation registers.  Key tile kt is handled in three steps:
@@ -648,8 +689,8 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     // first tile: both halves, the fixed reference max, probabilities of keys 0-31
     constexpr bool FOLD = C::FOLD_MAX;
     f32x16 init[QT] = {};
-    tl.template scores<0>(S0, Qr, init, kt0 % NB, l32, g, [](int) {});
-    tl.template scores<1>(S1, Qr, init, kt0 % NB, l32, g, [](int) {});
+    tl.template scores<0, true>(S0, Qr, init, kt0 % NB, l32, g, [](int) {});
+    tl.template scores<1, true>(S1, Qr, init, kt0 % NB, l32, g, [](int) {});
     if (kt0 == last_kt) {
       mask_half<QT>(S0, kt0 * BN, nk, g);
       mask_half<QT>(S1, kt0 * BN + 32, nk, g);
@@ -680,34 +721,46 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     }
     __syncthreads();
 
-    for (int kt = kt0 + 1; kt < kt1; ++kt) {
+    // One tile step.  Keys past nk exist only in the window's last key tile: MASK 1
+    // masks them, 0 knows kt is not that tile, 2 checks.  Where registers allow,
+    // the last tile is a step of its own, so that no branch splits the scores of
+    // the others.
+    auto tile_step = [&](const int kt, auto mask_tag) {
+      constexpr int MASK = decltype(mask_tag)::value;
+      const bool LAST = MASK == 1 || (MASK == 2 && kt == last_kt);
       const int cur = kt % NB, prev = (kt + NB - 1) % NB;
       float ls[QT][2] = {};
+      const bool more = kt + 2 < kt1;
       tl.template scores<0>(S0, Qr, init, cur, l32, g, [&](int i) {
         exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend);
       });
-      tl.values(O, P, prev, lane);
-      order_values_step<FT * (BN / 16), QT>();
+      values_part<C, 0, BN / 16>(tl, O, P, prev, lane, [](int) {});
       __builtin_amdgcn_sched_barrier(0);
       // Tile kt+2 is requested only now: the transpose reads above would otherwise
       // make the compiler wait for these loads before the value step.
-      const bool more = kt + 2 < kt1;
       if (more) tl.load(rs, kt + 2, (kt + 2) % NB);
-      if (kt == last_kt) mask_half<QT>(S0, kt * BN, nk, g);
+      if (LAST) mask_half<QT>(S0, kt * BN, nk, g);
       tl.template scores<1>(S1, Qr, init, cur, l32, g, [&](int i) {
         exp_slot<0, QT, KB * QT, !FOLD>(i, S0, P, m, ls, pend);
       });
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
-      if (kt == last_kt) mask_half<QT>(S1, kt * BN + 32, nk, g);
+      if (LAST) mask_half<QT>(S1, kt * BN + 32, nk, g);
       if (more)
         wait_loads<C::LOADS>();
       else
         wait_loads<0>();
       __syncthreads();
+    };
+    if constexpr (C::ASM_SCORES) {
+      const int kt_mid = kt1 == t.KT ? kt1 - 1 : kt1;  // steps before the last key tile
+      for (int kt = kt0 + 1; kt < kt_mid; ++kt) tile_step(kt, std::integral_constant<int, 0>{});
+      if (kt_mid < kt1 && kt_mid > kt0) tile_step(kt_mid, std::integral_constant<int, 1>{});
+    } else {
+      for (int kt = kt0 + 1; kt < kt1; ++kt) tile_step(kt, std::integral_constant<int, 2>{});
     }
     exp_half<1, QT, !FOLD>(S1, P, m, l);
-    tl.values(O, P, (kt1 - 1) % NB, lane);
+    values_part<C, 0, BN / 16>(tl, O, P, (kt1 - 1) % NB, lane, [](int) {});
     __syncthreads();
 
     const bool whole = (kt0 == 0 && kt1 == t.KT);

@@ -301,13 +301,15 @@ hipError_t launch_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
 template <int KC>
 hipError_t gemm_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
   const int64_t mt128 = (g.M + 127) / 128;
-  // Large problems (the 21-frame clip, batched requests): 256x256 tiles of eight
-  // 128x64 waves, two per SIMD, read 0.75 KB of LDS per MFMA instead of 1 KB and
-  // fetch 128 FLOP per byte instead of 85; bf16 output only (an fp32 output tile
-  // of that size does not fit the LDS).  Two 64-wide k stages measured faster than
-  // four 32-wide ones.
+  // 256x256 tiles of eight 128x64 waves, two per SIMD, read 0.75 KB of LDS per MFMA
+  // instead of 1 KB and fetch 128 FLOP per byte instead of 85; bf16 output only (an
+  // fp32 output tile of that size does not fit the LDS).  Two 64-wide k stages
+  // measured faster than four 32-wide ones.  Taken when there are enough of them to
+  // cover most of the 256 CUs: the 21-frame clip and batched requests, and at the
+  // 3-frame chunk the 2688-wide query GEMM (209 tiles in one round, against 399 of
+  // 256x128 in two); the chunk's output projection (114 tiles) stays at 256x128.
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-  if (!out_f32 && g.N >= 512 && tiles256 >= 512)
+  if (!out_f32 && g.N >= 512 && tiles256 >= 200)
     return launch_dma<256, 256, 128, 64, 64, 2, false>(g, st);
   if (g.N >= 1024) return launch_dma<256, 128, 64, 64, KC, 3>(g, out_f32, st);
   if (g.N % 128 == 0 && mt128 * (g.N / 128) * g.batch >= 200)

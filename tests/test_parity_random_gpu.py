@@ -4,6 +4,8 @@ placements, sink frames, partial windows, wrapped rings, causal blocks, batches 
 requests and both output epilogues, each checked through the C ABI against the fp64
 oracle at the usual tolerances.  Invalid draws (as the library's own validation
 judges them) are redrawn, so every case is one the ABI accepts."""
+import os
+
 import numpy as np
 import pytest
 
@@ -44,7 +46,11 @@ def draw_case(seed):
         return s, int(rng.integers(1, 3)), bool(rng.integers(2)), bool(rng.integers(2))
 
 
-@pytest.mark.parametrize("seed", range(24))
+# MLA_RANDOM_CASES widens the sweep for a one-off longer run; 24 by default.
+CASES = int(os.environ.get("MLA_RANDOM_CASES", "24"))
+
+
+@pytest.mark.parametrize("seed", range(CASES))
 def test_random_configuration(seed):
     s, batch, absorbed, query = draw_case(seed)
     run = Run(s, batch=batch, random_gains=True, seed=seed)

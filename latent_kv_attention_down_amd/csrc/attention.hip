@@ -584,18 +584,16 @@ __device__ __forceinline__ void pin(T &v) {
 // packed bf16 pairs, as the V^T fragments expect.  SUB: S still holds raw scores
 // (subtract the reference max), else the max was folded into the scores.  Row
 // sums go to two partial sums per query tile; pend carries an even element to the
-// slot that completes its pair.
+// element that completes its pair.  Each element's sum and packing run one element
+// late (prev carries it), so no instruction waits on the exponential just issued.
 template <int T, int QT, int NS, bool SUB>
 __device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], u32x4 (&P)[BN / 16][QT],
                                          const float (&m)[QT], float (&ls)[QT][2],
-                                         float (&pend)[QT]) {
+                                         float (&pend)[QT], float &prev) {
   constexpr int NE = 16 * QT;
-#pragma unroll
-  for (int j = slot * NE / NS; j < (slot + 1) * NE / NS; ++j) {
+  auto finish = [&](int j, float p) {
     const int qt = j / 16, r = j % 16;
-    float p = fast_exp2(SUB ? S[qt][r] - m[qt] : S[qt][r]);
     ls[qt][r & 1] += p;
-    pin(p);
     pin(ls[qt][r & 1]);
     if (r & 1) {
       bf16x2 w2 = {(bf16)pend[qt], (bf16)p};
@@ -605,14 +603,23 @@ __device__ __forceinline__ void exp_slot(int slot, const f32x16 (&S)[QT], u32x4 
     } else {
       pend[qt] = p;
     }
+  };
+#pragma unroll
+  for (int j = slot * NE / NS; j < (slot + 1) * NE / NS; ++j) {
+    const int qt = j / 16, r = j % 16;
+    float p = fast_exp2(SUB ? S[qt][r] - m[qt] : S[qt][r]);
+    pin(p);
+    if (j > 0) finish(j - 1, prev);
+    prev = p;
+    if (j == NE - 1) finish(j, p);
   }
 }
 
 template <int T, int QT, bool SUB>
 __device__ __forceinline__ void exp_half(const f32x16 (&S)[QT], u32x4 (&P)[BN / 16][QT],
                                          const float (&m)[QT], float (&l)[QT]) {
-  float ls[QT][2] = {}, pend[QT];
-  exp_slot<T, QT, 1, SUB>(0, S, P, m, ls, pend);
+  float ls[QT][2] = {}, pend[QT], prev = 0.f;
+  exp_slot<T, QT, 1, SUB>(0, S, P, m, ls, pend, prev);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
 }
@@ -729,10 +736,10 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       constexpr int MASK = decltype(mask_tag)::value;
       const bool LAST = MASK == 1 || (MASK == 2 && kt == last_kt);
       const int cur = kt % NB, prev = (kt + NB - 1) % NB;
-      float ls[QT][2] = {};
+      float ls[QT][2] = {}, late = 0.f;
       const bool more = kt + 2 < kt1;
       tl.template scores<0>(S0, Qr, init, cur, l32, g, [&](int i) {
-        exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend);
+        exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend, late);
       });
       values_part<C, 0, BN / 16>(tl, O, P, prev, lane, [](int) {});
       __builtin_amdgcn_sched_barrier(0);
@@ -741,7 +748,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       if (more) tl.load(rs, kt + 2, (kt + 2) % NB);
       if (LAST) mask_half<QT>(S0, kt * BN, nk, g);
       tl.template scores<1>(S1, Qr, init, cur, l32, g, [&](int i) {
-        exp_slot<0, QT, KB * QT, !FOLD>(i, S0, P, m, ls, pend);
+        exp_slot<0, QT, KB * QT, !FOLD>(i, S0, P, m, ls, pend, late);
       });
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];

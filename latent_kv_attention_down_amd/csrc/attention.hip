@@ -399,6 +399,22 @@ __device__ __forceinline__ void store_rows(bf16 *dst, const f32x16 (&O)[FT][QT],
 // the V^T transpose reads below touch every LDS bank equally often.
 __device__ __forceinline__ int swz4(int r) { return (r ^ (r >> 2)) & 3; }
 
+// The compiler does not see the inline-asm score MFMAs, so it cannot space their
+// consumers: where a VALU instruction may read S right after them, wait out their
+// VGPR write latency first (24 wait states, tied to S so that no read of S moves
+// above it).  Elsewhere the next read of S comes after a whole value step, or after
+// a barrier and an LDS read wait, far more than that.
+template <class C>
+__device__ __forceinline__ void drain_scores(f32x16 (&S)[C::QT]) {
+  if constexpr (C::ASM_SCORES) {
+    static_assert(C::QT == 1 || C::QT == 2, "drain covers one or two query tiles");
+    if constexpr (C::QT == 2)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
+    else
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]));
+  }
+}
+
 // Key tiles of the one-wave-per-SIMD kernel.  A tile is 64 ring rows of DK bf16,
 // unpadded and swizzled, brought in by buffer_load_dwordx4 ... lds: each load puts
 // 64 lanes' 16 bytes at consecutive LDS chunk positions, so the swizzle is applied
@@ -459,7 +475,7 @@ struct TileW {
   // C::DS k-blocks ahead of their MFMAs; after the MFMA of (k-block kb, query tile
   // qt) the caller's work(2kb + qt) is emitted, each group fenced so the order
   // stays MFMA / VALU / MFMA / VALU.
-  template <int T, bool ZERO = false, class Work>
+  template <int T, bool ZERO = false, bool DRAIN = true, class Work>
   __device__ __forceinline__ void scores(f32x16 (&S)[QT], const bf16x8 (&Qr)[QT][KB],
                                          const f32x16 (&init)[QT], int buf, int l32, int g,
                                          Work &&work) const {
@@ -499,16 +515,7 @@ struct TileW {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if constexpr (C::ASM_SCORES) {
-      // The compiler does not see the MFMAs above, so it cannot space their
-      // consumers: wait out the VGPR write latency of the last ones here (24 wait
-      // states, tied to S so that no read of S moves above it).
-      static_assert(QT == 1 || QT == 2, "drain covers one or two query tiles");
-      if constexpr (QT == 2)
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
-      else
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]));
-    }
+    if constexpr (DRAIN) drain_scores<C>(S);
   }
 };
 
@@ -738,7 +745,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       const int cur = kt % NB, prev = (kt + NB - 1) % NB;
       float ls[QT][2] = {}, late = 0.f;
       const bool more = kt + 2 < kt1;
-      tl.template scores<0>(S0, Qr, init, cur, l32, g, [&](int i) {
+      tl.template scores<0, false, false>(S0, Qr, init, cur, l32, g, [&](int i) {
         exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend, late);
       });
       values_part<C, 0, BN / 16>(tl, O, P, prev, lane, [](int) {});
@@ -747,7 +754,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       // make the compiler wait for these loads before the value step.
       if (more) tl.load(rs, kt + 2, (kt + 2) % NB);
       if (LAST) mask_half<QT>(S0, kt * BN, nk, g);
-      tl.template scores<1>(S1, Qr, init, cur, l32, g, [&](int i) {
+      tl.template scores<1, false, MASK != 0>(S1, Qr, init, cur, l32, g, [&](int i) {
         exp_slot<0, QT, KB * QT, !FOLD>(i, S0, P, m, ls, pend, late);
       });
 #pragma unroll
@@ -766,6 +773,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     } else {
       for (int kt = kt0 + 1; kt < kt1; ++kt) tile_step(kt, std::integral_constant<int, 2>{});
     }
+    drain_scores<C>(S1);  // the last step may have ended right after its scores
     exp_half<1, QT, !FOLD>(S1, P, m, l);
     values_part<C, 0, BN / 16>(tl, O, P, (kt1 - 1) % NB, lane, [](int) {});
     __syncthreads();

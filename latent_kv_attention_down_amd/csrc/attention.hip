@@ -471,45 +471,59 @@ struct TileW {
     }
   }
 
+  // K fragment kb of half T of stage buf (lane: key l32, features 8g..8g+7 of k-block
+  // kb); the swizzle only flips the low two chunk bits.
+  __device__ __forceinline__ bf16x8 kfrag_at(int buf, int T, int l32, int g, int kb) const {
+    const bf16 *rb = Ks(buf) + (T * 32 + l32) * DK;
+    return *(const bf16x8 *)(rb + ((2 * (kb & 1) + g) ^ swz4(l32)) * 8 + (kb >> 1) * 32);
+  }
+
   // S^T of one 32-key half T of the tile for both query tiles.  K fragments run
-  // C::DS k-blocks ahead of their MFMAs; after the MFMA of (k-block kb, query tile
-  // qt) the caller's work(2kb + qt) is emitted, each group fenced so the order
-  // stays MFMA / VALU / MFMA / VALU.
-  template <int T, bool ZERO = false, bool DRAIN = true, class Work>
+  // C::DS k-blocks ahead of their MFMAs in the ring fr, fragment kb in slot
+  // (BASE + kb) % (DS + 1); with PRE the first DS are already there.  After the MFMA
+  // of (k-block kb, query tile qt) the caller's work(2kb + qt) is emitted, each group
+  // fenced so the order stays MFMA / VALU / MFMA / VALU; where no fragment of this
+  // half is left to fetch, tail(i) fetches fragment i of the next step instead.
+  template <int T, bool ZERO, bool DRAIN, int BASE, bool PRE, class Work, class Tail>
   __device__ __forceinline__ void scores(f32x16 (&S)[QT], const bf16x8 (&Qr)[QT][KB],
                                          const f32x16 (&init)[QT], int buf, int l32, int g,
-                                         Work &&work) const {
-    // k-block kb is chunk 2kb + g of row T*32 + l32; the swizzle only flips the low
-    // two chunk bits, so even and odd k-blocks each have one base address.
+                                         bf16x8 (&fr)[C::DS + 1], Work &&work,
+                                         Tail &&tail) const {
+    // k-block kb is chunk 2kb + g of row T*32 + l32: even and odd k-blocks each have
+    // one base address
     const int sw = swz4(l32);
     const bf16 *rb = Ks(buf) + (T * 32 + l32) * DK;
     const bf16 *kr[2] = {rb + ((g ^ sw) * 8), rb + (((2 + g) ^ sw) * 8)};
     auto kfrag = [&](int kb) { return *(const bf16x8 *)(kr[kb & 1] + (kb >> 1) * 32); };
-    constexpr int D = C::DS;  // fragments in flight
-    bf16x8 fr[D + 1];
+    constexpr int D = C::DS, R = D + 1;
+    if constexpr (!PRE) {
 #pragma unroll
-    for (int kb = 0; kb < D; ++kb) fr[kb] = kfrag(kb);
+      for (int kb = 0; kb < D; ++kb) fr[(BASE + kb) % R] = kfrag(kb);
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       __builtin_amdgcn_sched_barrier(0);
-      if (kb + D < KB) fr[(kb + D) % (D + 1)] = kfrag(kb + D);
+      if (kb + D < KB)
+        fr[(BASE + kb + D) % R] = kfrag(kb + D);
+      else
+        tail(kb + D - KB);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         if constexpr (C::ASM_SCORES) {
           if (kb == 0 && ZERO)
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                          : "=&v"(S[qt])
-                         : "v"(fr[kb % (D + 1)]), "v"(Qr[qt][kb]));
+                         : "v"(fr[(BASE + kb) % R]), "v"(Qr[qt][kb]));
           else if (kb == 0)
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
                          : "=&v"(S[qt])
-                         : "v"(fr[kb % (D + 1)]), "v"(Qr[qt][kb]), "v"(init[qt]));
+                         : "v"(fr[(BASE + kb) % R]), "v"(Qr[qt][kb]), "v"(init[qt]));
           else
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                          : "+v"(S[qt])
-                         : "v"(fr[kb % (D + 1)]), "v"(Qr[qt][kb]));
+                         : "v"(fr[(BASE + kb) % R]), "v"(Qr[qt][kb]));
         } else {
-          S[qt] = mfma32(fr[kb % (D + 1)], Qr[qt][kb], kb == 0 ? init[qt] : S[qt]);
+          S[qt] = mfma32(fr[(BASE + kb) % R], Qr[qt][kb], kb == 0 ? init[qt] : S[qt]);
         }
         work(kb * QT + qt);
         __builtin_amdgcn_sched_barrier(0);
@@ -517,20 +531,56 @@ struct TileW {
     }
     if constexpr (DRAIN) drain_scores<C>(S);
   }
+
+  // The same with a ring of its own and nothing fetched for a next step.
+  template <int T, bool ZERO = false, bool DRAIN = true, class Work>
+  __device__ __forceinline__ void scores(f32x16 (&S)[QT], const bf16x8 (&Qr)[QT][KB],
+                                         const f32x16 (&init)[QT], int buf, int l32, int g,
+                                         Work &&work) const {
+    bf16x8 fr[C::DS + 1];
+    scores<T, ZERO, DRAIN, 0, false>(S, Qr, init, buf, l32, g, fr, work, [](int) {});
+  }
 };
 
-// O^T += V^T P^T over key blocks KB0 .. KB0+NKB-1 (16 keys each) of the tile, V^T
-// fragments read with ds_read_b64_tr_b16 as in Tile::values (addresses through the
-// swizzle) C::DV ahead of their MFMAs; P holds packed bf16 pairs.  The caller's
-// work(i) follows the MFMA of (fragment i / QT, query tile i % QT), each group fenced.
-template <class C, int KB0, int NKB, class Work>
-__device__ __forceinline__ void values_part(const TileW<C> &tl, f32x16 (&O)[C::FT][C::QT],
-                                            const u32x4 (&P)[BN / 16][C::QT], int buf, int lane,
-                                            Work &&work) {
+// V^T fragment i of key blocks KB0 .. KB0+NKB-1 of stage buf (fragment i: key block
+// KB0 + i % NKB, features 32 (i / NKB) .. +31).
+template <class C, int KB0, int NKB>
+__device__ __forceinline__ bf16x8 vfrag_at(const TileW<C> &tl, int buf, int lane, int i) {
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-  constexpr int DK = C::DK, FT = C::FT, QT = C::QT, NF = FT * NKB, D = C::DV;
+  constexpr int DK = C::DK;
+  const int G = lane >> 4, r = lane & 15, g = lane >> 5;
+  const int off = (KB0 + i % NKB) * 16 * DK + (i / NKB) * 32;
+  s16x4 part[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * h + 4 * g + (r >> 2);
+    const int chunk = (2 * (G & 1) + ((r & 3) >> 1)) ^ swz4(row);
+    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(tl.Ks(buf) + row * DK +
+                                                                 chunk * 8 + (r & 1) * 4 + off));
+  }
+  return __builtin_bit_cast(bf16x8,
+                            (s16x8)__builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// O^T += V^T P^T over key blocks KB0 .. KB0+NKB-1 (16 keys each) of the tile, V^T
+// fragments read with ds_read_b64_tr_b16 as in Tile::values (addresses through the
+// swizzle) C::DV ahead of their MFMAs in the ring fr (fragment i in slot i % (DV + 1);
+// with PRE the first DV are already there); P holds packed bf16 pairs.  The caller's
+// work(i) follows the MFMA of (fragment i / QT, query tile i % QT), each group fenced;
+// where no fragment of this step is left to fetch, tail(j) fetches fragment j of the
+// next step instead.
+template <class C, int KB0, int NKB, bool PRE, class Work, class Tail>
+__device__ __forceinline__ void values_part(const TileW<C> &tl, f32x16 (&O)[C::FT][C::QT],
+                                            const u32x4 (&P)[BN / 16][C::QT], int buf, int lane,
+                                            bf16x8 (&fr)[C::DV + 1], Work &&work, Tail &&tail) {
+  typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+  constexpr int DK = C::DK, FT = C::FT, QT = C::QT, NF = FT * NKB, D = C::DV, R = D + 1;
+  static_assert(NF % R == 0, "each value step starts the ring at slot 0");
   const int G = lane >> 4, r = lane & 15, g = lane >> 5;
   const bf16 *vt[2];
 #pragma unroll
@@ -548,21 +598,34 @@ __device__ __forceinline__ void values_part(const TileW<C> &tl, f32x16 (&O)[C::F
     return __builtin_bit_cast(bf16x8,
                               (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  bf16x8 fr[D + 1];
+  if constexpr (!PRE) {
 #pragma unroll
-  for (int i = 0; i < D; ++i) fr[i] = vfrag(i);
+    for (int i = 0; i < D; ++i) fr[i] = vfrag(i);
+  }
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    if (i + D < NF) fr[(i + D) % (D + 1)] = vfrag(i + D);
+    if (i + D < NF)
+      fr[(i + D) % R] = vfrag(i + D);
+    else
+      tail(i + D - NF);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      O[i / NKB][qt] = mfma32(fr[i % (D + 1)],
+      O[i / NKB][qt] = mfma32(fr[i % R],
                               __builtin_bit_cast(bf16x8, P[KB0 + i % NKB][qt]), O[i / NKB][qt]);
       work(i * QT + qt);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+}
+
+// The same with a ring of its own and nothing fetched for a next step.
+template <class C, int KB0, int NKB, class Work>
+__device__ __forceinline__ void values_part(const TileW<C> &tl, f32x16 (&O)[C::FT][C::QT],
+                                            const u32x4 (&P)[BN / 16][C::QT], int buf, int lane,
+                                            Work &&work) {
+  bf16x8 fr[C::DV + 1];
+  values_part<C, KB0, NKB, false>(tl, O, P, buf, lane, fr, work, [](int) {});
 }
 
 // Keys of half T past nk get -inf (only the window's last tile has any).
@@ -727,13 +790,33 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
           S1[qt][r] -= m[qt];
         }
     }
-    if (kt0 + 2 < kt1) {
-      tl.load(rs, kt0 + 2, (kt0 + 2) % NB);
-      wait_loads<C::LOADS>();
-    } else {
-      wait_loads<0>();
-    }
+    wait_loads<0>();
     __syncthreads();
+    if (kt0 + 2 < kt1) tl.load(rs, kt0 + 2, (kt0 + 2) % NB);
+
+    // The K and V^T fragment rings run across the steps: the last MFMAs of each phase
+    // issue the first reads of the next one, so no phase starts on an LDS latency.
+    // Ring slots: the first score half starts at slot 0, the second at slot B1, so that
+    // KB k-blocks later the next first half is back at 0; the value step at 0.  Reads
+    // of a stage that holds no tile of this request (after the last step) are not used.
+    // Only where the query fits 112 registers: otherwise the rings would spill.
+    constexpr bool XP = C::ASM_SCORES;
+    constexpr int R = C::DS + 1, B1 = (R - KB % R) % R;
+    // A phase that runs d fragments ahead has d tail slots; the next phase wants dn
+    // fragments: the last slot fetches any beyond d, slots beyond dn fetch nothing.
+    auto cover = [](int j, int d, int dn, auto &&fetch) {
+      if (j == d - 1) {
+#pragma unroll
+        for (int x = j; x < dn; ++x) fetch(x);
+      } else if (j < dn) {
+        fetch(j);
+      }
+    };
+    bf16x8 kfr[R], vfr[C::DV + 1];
+    if constexpr (XP) {
+#pragma unroll
+      for (int i = 0; i < C::DS; ++i) kfr[i] = tl.kfrag_at((kt0 + 1) % NB, 0, l32, g, i);
+    }
 
     // One tile step.  Keys past nk exist only in the window's last key tile: MASK 1
     // masks them, 0 knows kt is not that tile, 2 checks.  Where registers allow,
@@ -742,29 +825,40 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     auto tile_step = [&](const int kt, auto mask_tag) {
       constexpr int MASK = decltype(mask_tag)::value;
       const bool LAST = MASK == 1 || (MASK == 2 && kt == last_kt);
-      const int cur = kt % NB, prev = (kt + NB - 1) % NB;
+      const int cur = kt % NB, prev = (kt + NB - 1) % NB, next = (kt + 1) % NB;
       float ls[QT][2] = {}, late = 0.f;
-      const bool more = kt + 2 < kt1;
-      tl.template scores<0, false, false>(S0, Qr, init, cur, l32, g, [&](int i) {
-        exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend, late);
-      });
-      values_part<C, 0, BN / 16>(tl, O, P, prev, lane, [](int) {});
+      tl.template scores<0, false, false, 0, XP>(
+          S0, Qr, init, cur, l32, g, kfr,
+          [&](int i) { exp_slot<1, QT, KB * QT, !FOLD>(i, S1, P, m, ls, pend, late); },
+          [&](int j) {
+            if constexpr (XP)
+              cover(j, C::DS, C::DV,
+                    [&](int x) { vfr[x] = vfrag_at<C, 0, BN / 16>(tl, prev, lane, x); });
+          });
+      // Tile kt+1 (read from the end of the second half on) has landed for every wave,
+      // and every wave is done with the stage tile kt+2 goes to.
+      wait_loads<0>();
+      __syncthreads();
+      values_part<C, 0, BN / 16, XP>(
+          tl, O, P, prev, lane, vfr, [](int) {}, [&](int j) {
+            if constexpr (XP)
+              cover(j, C::DV, C::DS,
+                    [&](int x) { kfr[(B1 + x) % R] = tl.kfrag_at(cur, 1, l32, g, x); });
+          });
       __builtin_amdgcn_sched_barrier(0);
-      // Tile kt+2 is requested only now: the transpose reads above would otherwise
-      // make the compiler wait for these loads before the value step.
-      if (more) tl.load(rs, kt + 2, (kt + 2) % NB);
+      // Tile kt+2 is requested only now: the transpose reads of the value step would
+      // otherwise make the compiler wait for these loads.
+      if (kt + 2 < kt1) tl.load(rs, kt + 2, (kt + 2) % NB);
       if (LAST) mask_half<QT>(S0, kt * BN, nk, g);
-      tl.template scores<1, false, MASK != 0>(S1, Qr, init, cur, l32, g, [&](int i) {
-        exp_slot<0, QT, KB * QT, !FOLD>(i, S0, P, m, ls, pend, late);
-      });
+      tl.template scores<1, false, MASK != 0, B1, XP>(
+          S1, Qr, init, cur, l32, g, kfr,
+          [&](int i) { exp_slot<0, QT, KB * QT, !FOLD>(i, S0, P, m, ls, pend, late); },
+          [&](int j) {
+            if constexpr (XP) kfr[j] = tl.kfrag_at(next, 0, l32, g, j);
+          });
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt][0] + ls[qt][1];
       if (LAST) mask_half<QT>(S1, kt * BN + 32, nk, g);
-      if (more)
-        wait_loads<C::LOADS>();
-      else
-        wait_loads<0>();
-      __syncthreads();
     };
     if constexpr (C::ASM_SCORES) {
       const int kt_mid = kt1 == t.KT ? kt1 - 1 : kt1;  // steps before the last key tile

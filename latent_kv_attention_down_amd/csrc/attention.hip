@@ -394,6 +394,24 @@ __device__ __forceinline__ void store_rows(bf16 *dst, const f32x16 (&O)[FT][QT],
     }
 }
 
+// The same values into an LDS image of the wave's rows (row-major, DC wide), 16-byte
+// chunk k of row r at chunk position k ^ (r & 7), so that the lanes of one write
+// (32 rows) spread over the banks; the rows then leave in contiguous wave-wide stores.
+template <int FT, int QT, int DC>
+__device__ __forceinline__ void stage_rows(bf16 *img, const f32x16 (&O)[FT][QT], int qt, int r,
+                                           float inv, int g) {
+  bf16 *row = img + r * DC;
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16 v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = (bf16)(O[ft][qt][4 * i + j] * inv);
+      *(uint2 *)(row + (((ft * 4 + i) ^ (r & 7)) * 8) + g * 4) = *(const uint2 *)v4;
+    }
+}
+
 // Chunk swizzle of the unpadded key tile: 16-byte chunk c of tile row r sits at
 // chunk position c ^ swz4(r) of that row.  With it the 32-row K fragment reads and
 // the V^T transpose reads below touch every LDS bank equally often.
@@ -876,6 +894,12 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     unsigned char *rec = part + (size_t)(wg + rt) * C::REC;
     float *rec_m = (float *)(rec + (size_t)RW * DC * 2);
     float *rec_l = rec_m + RW;
+    // Normalised rows go through an LDS image of the wave's rows (the key stages are
+    // free: every wave is past its last read of them) and leave as whole 16-byte
+    // chunks, consecutive lanes on consecutive addresses.
+    constexpr int WR = QT * 32, CPR = DC / 8;
+    static_assert(CPR % 8 == 0 && (size_t)C::NW * WR * DC * 2 <= C::LDS, "row image");
+    bf16 *img = tl.base + wave * WR * DC;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
@@ -884,17 +908,30 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       // as does inf or NaN: such a row tile is recomputed by the safe kernel.
       // Sums above 2^64 made only of smaller weights are flagged too (harmless).
       if (!(lt <= kFastSumLimit)) flags[rt] = 1;
-      const int lrow = wave * QT * 32 + qt * 32 + l32;
-      const int row = row0 + lrow;
-      if (row < t.row_end) {
-        bf16 *dst = whole ? o + ((int64_t)b * s.R + row) * DC : (bf16 *)rec + (int64_t)lrow * DC;
-        store_rows<FT, QT>(dst, O, qt, 1.0f / lt, g);
-        if (!whole && g == 0) {
-          rec_m[lrow] = m[qt];
-          rec_l[lrow] = lt;
-        }
+      stage_rows<FT, QT, DC>(img, O, qt, qt * 32 + l32, 1.0f / lt, g);
+      const int lrow = wave * WR + qt * 32 + l32;
+      if (!whole && g == 0 && row0 + lrow < t.row_end) {
+        rec_m[lrow] = m[qt];
+        rec_l[lrow] = lt;
       }
     }
+    // LDS operations of one wave complete in order; this keeps the compiler from
+    // moving the reads above the writes of other lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      const int wrow0 = row0 + wave * WR;  // the wave's first row
+      bf16 *dst = whole ? o + ((int64_t)b * s.R + wrow0) * DC : (bf16 *)rec + (int64_t)wave * WR * DC;
+#pragma unroll 6
+      for (int it = 0; it < WR * CPR / 64; ++it) {
+        const int c = it * 64 + lane, r = c / CPR, k = c % CPR;
+        const uint4 v = *(const uint4 *)(img + r * DC + ((k ^ (r & 7)) * 8));
+        if (wrow0 + r < t.row_end) *(uint4 *)(dst + r * DC + k * 8) = v;
+      }
+    }
+    // the next row tile's first loads overwrite these images
+    __syncthreads();
   }
 }
 

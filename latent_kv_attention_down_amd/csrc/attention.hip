@@ -923,7 +923,8 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     {
       const int wrow0 = row0 + wave * WR;  // the wave's first row
       bf16 *dst = whole ? o + ((int64_t)b * s.R + wrow0) * DC : (bf16 *)rec + (int64_t)wave * WR * DC;
-#pragma unroll 6
+      constexpr int UNR = C::ASM_SCORES ? 6 : 4;  // 6 spills beside a 128-register query
+#pragma unroll UNR
       for (int it = 0; it < WR * CPR / 64; ++it) {
         const int c = it * 64 + lane, r = c / CPR, k = c % CPR;
         const uint4 v = *(const uint4 *)(img + r * DC + ((k ^ (r & 7)) * 8));

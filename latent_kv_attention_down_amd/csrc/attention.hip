@@ -25,8 +25,11 @@
 //    destinations: O fills the accumulation registers, and with S there as well
 //    the compiler moved every score in and out of them (two register moves per
 //    score element, in blocks the matrix unit could not hide).  The compiler
-//    cannot see these MFMAs, so each score half ends with an explicit wait for
-//    their results before any VALU instruction reads them;
+//    cannot see these MFMAs, so wherever a VALU instruction may read S right
+//    after them the score half ends with an explicit wait for their results;
+//  * the K and V^T fragment rings run across the three steps of a tile (each
+//    step's last MFMAs issue the next step's first LDS reads), and the output rows
+//    leave through an LDS image of each wave's rows as contiguous wave-wide stores;
 //  * fast path: each row's softmax reference is the max of the first key tile the
 //    workgroup sees for it and is never moved, so O is never rescaled inside the
 //    loop (a rescale would drag the AGPR-resident accumulators through VGPRs).

@@ -1,11 +1,14 @@
 """Benchmark of the VideoMLA latent-KV chunk step on one MI355X.
 
-A step is one mla_step call: cache write of the 3-frame chunk into the 21-frame
-ring, query preparation, latent chunk attention over the whole window, value
-up-projection and W_O, on the Wan-1.3B layer shape (bf16 storage, fp32
-accumulation), inputs resident in HBM.  Prints one JSON line.
+A step is one mla_step call per layer: cache write of the 3-frame chunk into the
+21-frame ring, query preparation, latent chunk attention over the whole window,
+value up-projection and W_O, on the Wan-1.3B layer shape (bf16 storage, fp32
+accumulation), inputs resident in HBM.  By default one layer; --layers 30 steps a
+30-layer stack (independent seeded weights, inputs and rings per layer, one
+stream, one shared workspace).  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L]
+                  [--no-cpu-baseline]
 """
 import argparse
 import ctypes
@@ -166,11 +169,13 @@ def cpu_baseline(s, w_exact, x_window, n_tokens):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     rows = np.linspace(0, s.chunk_tokens - 1, n_tokens).round().astype(int)
+    tpf = s.tokens_per_frame
+    tokens = {f: x_window[i * tpf:(i + 1) * tpf] for i, f in enumerate(s.window_frame_ids)}
     t0 = time.perf_counter()
-    O.step(s, w_exact, x_window, s.window_frame_ids, s.chunk_frame_ids, query_rows=rows)
+    r = O.step(s, w_exact, tokens, query_rows=rows)
     dt = time.perf_counter() - t0
     f1 = step_flops(s.with_(batch=1))
-    vis = O.visible_keys(s, s.window_frame_ids, s.chunk_frame_ids)[rows]
+    vis = O.visible_keys(s, r["window_ids"], O.chunk_frame_ids(s))[rows]
     flops = ((f1["total"] - f1["attention"]) * n_tokens / s.chunk_tokens
              + 2 * float(vis.sum()) * s.n_heads * (2 * s.d_c + s.d_rope))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
@@ -185,6 +190,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan1.3b-w21")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="layers per step, each with its own seeded weights, tokens and ring "
+                         "(30: the Wan-1.3B backbone's attention layers)")
     ap.add_argument("--batch", type=int, default=1,
                     help="independent requests per step, each with its own cache")
     ap.add_argument("--epilogue", choices=("two-stage", "absorbed"), default="absorbed",
@@ -209,17 +217,20 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design note, not a measured run.", file=sys.stderr)
         sys.exit(2)
+    if args.layers < 1:
+        print("--layers must be >= 1", file=sys.stderr)
+        sys.exit(2)
 
-    import numpy as np
     import torch
 
     import workload as W
     import latent_kv_attention_down_amd as mla
-    from latent_kv_attention_down_amd.layer import DeviceLayer
+    from latent_kv_attention_down_amd.layer import DeviceLayer, WorkspacePool
 
     s = W.shape_by_name(args.workload).with_(batch=args.batch)
-    print(f"[bench] workload {s.name}: {s.batch} x {s.chunk_tokens} query tokens x {s.n_heads} "
-          f"heads over {s.window_tokens} keys", file=sys.stderr, flush=True)
+    NL = args.layers
+    print(f"[bench] workload {s.name} x {NL} layer(s): {s.batch} x {s.chunk_tokens} query "
+          f"tokens x {s.n_heads} heads over {s.window_tokens} keys", file=sys.stderr, flush=True)
     if args.copy_calibration > 0:
         src = torch.ones(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -227,63 +238,93 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    stored, w_exact = W.draw_weights(s)
     ids = s.window_frame_ids
-    xs, xe = W.draw_frames(s, ids)
-    L = DeviceLayer(s, stored, batch=s.batch)
-    if args.epilogue == "absorbed":
-        L.absorb_value()  # weight preparation, once, outside the timed region
-    if args.query == "absorbed":
-        L.absorb_query()  # likewise
     tpf = s.tokens_per_frame
-    for i, f in enumerate(ids):
-        if f >= s.t0:
-            break
-        L.cache_write(L.chunk(1, f, 1), L.tokens(xs[:, i * tpf:(i + 1) * tpf]))
-    chunk = L.chunk(s.chunk_frames, s.t0, s.n_valid_frames, s.causal_frames)
-    x = L.tokens(xs[:, -s.chunk_frames * tpf:])
-    y = L.new_out(chunk, s.d_model)
-    ws = L.workspace(chunk)
+    pool = WorkspacePool()
+    layers = []  # (DeviceLayer, chunk tokens, y) per layer
+    w_exact0 = xe0 = None
+    for l in range(NL):
+        stored, w_exact = W.draw_weights(s, layer=l)
+        xs, xe = W.draw_frames(s, ids, layer=l)
+        if l == 0:
+            w_exact0, xe0 = w_exact, xe[0]
+        L = DeviceLayer(s, stored, batch=s.batch, pool=pool)
+        if args.epilogue == "absorbed":
+            L.absorb_value()  # weight preparation, once, outside the timed region
+        if args.query == "absorbed":
+            L.absorb_query()  # likewise
+        for i, f in enumerate(ids):
+            if f >= s.t0:
+                break
+            L.cache_write(L.chunk(1, f, 1), L.tokens(xs[:, i * tpf:(i + 1) * tpf]))
+        x = L.tokens(xs[:, -s.chunk_frames * tpf:])
+        chunk = L.chunk(s.chunk_frames, s.t0, s.n_valid_frames, s.causal_frames)
+        layers.append((L, x, L.new_out(chunk, s.d_model)))
+        del xs, xe
+        if NL > 1 and (l + 1) % 10 == 0:
+            print(f"[bench] {l + 1} of {NL} layers prefilled", file=sys.stderr, flush=True)
+    L0, x0, _ = layers[0]
+    chunk = L0.chunk(s.chunk_frames, s.t0, s.n_valid_frames, s.causal_frames)
+    ws = L0.workspace(chunk)
     stream = torch.cuda.current_stream().cuda_stream
     hip = Hip()
 
-    def one_step():
-        mla.step(L.cfg, L.weights, chunk, x, L.cache, y, ws, stream)
+    def one_step(evs=None):
+        for j, (L, x, y) in enumerate(layers):
+            if evs is not None:
+                mla.set_timing_events(evs[j][0], evs[j][1])
+            mla.step(L.cfg, L.weights, chunk, x, L.cache, y, ws, stream)
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(hip.event(), hip.event()) for _ in range(K)]
+    ev = [[(hip.event(), hip.event()) for _ in range(NL)] for _ in range(K)]
     t_start, t_stop = hip.event(), hip.event()
     torch.cuda.synchronize()
     hip.record(t_start, stream)
     for i in range(K):
-        mla.set_timing_events(ev[i][0], ev[i][1])
-        one_step()
+        one_step(ev[i])
     hip.record(t_stop, stream)
     mla.set_timing_events(None, None)
     torch.cuda.synchronize()
     ms_total = hip.ms(t_start, t_stop)
     ms_step = ms_total / K
-    attn_ms = [hip.ms(a, b) for a, b in ev]
-    attn_avg = sum(attn_ms) / K
-    assert torch.isfinite(y.float()).all(), "non-finite output"
+    attn_ms = [hip.ms(a, b) for row in ev for a, b in row]
+    attn_by_layer = [sum(hip.ms(*ev[i][j]) for i in range(K)) / K for j in range(NL)]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    for L, x, y in layers:
+        assert torch.isfinite(y.float()).all(), "non-finite output"
+
+    # the chunk attention on its own (a2-a4: query preparation, latent attention with
+    # its merge and fallback, per-head value up-projection), layer 0, back to back
+    out_heads = L0.new_out(chunk, s.n_heads * s.d_head)
+    for _ in range(3):
+        mla.chunk_attention(L0.cfg, L0.weights, chunk, x0, L0.cache, out_heads, ws, stream)
+    torch.cuda.synchronize()
+    ca_ev = [(hip.event(), hip.event()) for _ in range(K)]
+    for a, b in ca_ev:
+        hip.record(a, stream)
+        mla.chunk_attention(L0.cfg, L0.weights, chunk, x0, L0.cache, out_heads, ws, stream)
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    ca_ms = [hip.ms(a, b) for a, b in ca_ev]
+    ca_avg = sum(ca_ms) / K
 
     # cache write on its own: back-to-back launches between one pair of events
-    wr_ch = L.chunk(s.chunk_frames, s.t0, s.n_valid_frames)
+    wr_ch = L0.chunk(s.chunk_frames, s.t0, s.n_valid_frames)
     for _ in range(3):
-        mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
+        mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache, stream)
     torch.cuda.synchronize()
     nw = max(K, 20)
     hip.record(t_start, stream)
     for _ in range(nw):
-        mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
+        mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache, stream)
     hip.record(t_stop, stream)
     torch.cuda.synchronize()
     write_ms = hip.ms(t_start, t_stop) / nw
-    device_bytes = {"cache_per_request": L.cache[0].numel() * L.cache.element_size(),
+    device_bytes = {"cache_per_request_per_layer": L0.cache[0].numel() * L0.cache.element_size(),
                     "workspace": int(ws.numel()),
                     "peak_allocated": int(torch.cuda.max_memory_allocated())}
 
@@ -297,7 +338,7 @@ def main():
         for a, b in cold_ev:
             flush.fill_(1)
             hip.record(a, stream)
-            mla.cache_write(L.cfg, L.weights, wr_ch, x, L.cache, stream)
+            mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache, stream)
             hip.record(b, stream)
         torch.cuda.synchronize()
         cold_us = [1e3 * hip.ms(a, b) for a, b in cold_ev]
@@ -307,8 +348,9 @@ def main():
         del flush
 
     fl = step_flops(s)
-    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
-    attn_tflops = fl["attention"] / (attn_avg * 1e-3) / 1e12
+    tflops = NL * fl["total"] / (ms_step * 1e-3) / 1e12
+    kernel_tflops = fl["attention"] / (attn_avg * 1e-3) / 1e12
+    ca_tflops = fl["attention"] / (ca_avg * 1e-3) / 1e12
     wbytes = cache_write_bytes(s)
     write_gbs = wbytes / (write_ms * 1e-3) / 1e9
     csrc = os.path.join(ROOT, "latent_kv_attention_down_amd", "csrc")
@@ -330,40 +372,52 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights; no trained model)",
-        "config": {"workload": s.name, "batch": s.batch, "epilogue": args.epilogue,
-                   "query": args.query,
+        "config": {"workload": s.name if NL == 1 else f"{s.name}-{NL}layers", "layers": NL,
+                   "batch": s.batch, "epilogue": args.epilogue, "query": args.query,
                    "query_tokens": s.chunk_tokens,
                    "window_tokens": s.window_tokens, "chunk_frames": s.chunk_frames,
                    "window_frames": s.window_frames, "heads": s.n_heads, "d_c": s.d_c,
                    "d_rope": s.d_rope, "d_model": s.d_model, "grid": [s.grid_h, s.grid_w],
-                   "step_tflop": round(fl["total"] / 1e12, 4)},
-        "chunk_attention_tflops": round(attn_tflops, 2),
+                   "step_tflop": round(NL * fl["total"] / 1e12, 4)},
+        "chunk_attention_tflops": round(ca_tflops, 2),
+        "chunk_attention_ms": spread(ca_ms),
+        "chunk_attention_note": "mla_chunk_attention timed whole (query preparation, latent "
+                                "attention with its merge and fallback, per-head W^V_up), "
+                                "attention FLOPs only",
+        "fast_kernel_tflops": round(kernel_tflops, 2),
         "cache_write_gbs": round(write_gbs, 1),
         "cache_write_us": round(write_ms * 1e3, 2),
         "attention_ms": spread(attn_ms),
         "window_read_gbs": round(s.batch * s.window_tokens * (s.d_c + s.d_rope) * 2
                                  / (attn_avg * 1e-3) / 1e9, 1),
         "cache_write_cold_us": spread(cold_us) if cold_us else None,
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+                     "frac": round(kernel_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "k_latent_attn_w1 (latent attention, fast path)",
+                     "kernel": "k_latent_attn_w1 (the dominant kernel: latent attention, "
+                               "fast path, without its merge)",
                      "kernel_ms": round(attn_avg, 4)},
         "cache_write_roofline": {"bound": "hbm", "achieved": round(write_gbs, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(write_gbs / HBM_PEAK_GBS, 4),
                                  "traffic": cw_traffic,
-                                 "kernel": "k_cache_write_dma (cache write)",
+                                 "kernel": "mla_cache_write",
                                  "bytes_per_launch": wbytes},
         "device_bytes": device_bytes,
         "ceilings": (None if args.no_ceilings or args.copy_calibration > 0
                      else ceilings(hip, stream)),
     }
+    if NL > 1:
+        line["attention_ms_by_layer"] = [round(v, 4) for v in attn_by_layer]
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(s, w_exact, xe[0], args.cpu_tokens)
-    for a, b in ev:
+        line["cpu_baseline"] = cpu_baseline(s, w_exact0, xe0, args.cpu_tokens)
+    for row in ev:
+        for a, b in row:
+            hip.destroy(a)
+            hip.destroy(b)
+    for a, b in ca_ev:
         hip.destroy(a)
         hip.destroy(b)
     print(json.dumps(line), flush=True)

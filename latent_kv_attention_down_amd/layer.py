@@ -25,8 +25,24 @@ def to_host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+class WorkspacePool:
+    """One device workspace for several layers that are stepped in turn on one
+    stream (a backbone's attention layers): each call takes the same buffer,
+    grown to the largest size asked for."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = None
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
 class DeviceLayer:
-    def __init__(self, shape, stored_weights, batch=1, device="cuda"):
+    def __init__(self, shape, stored_weights, batch=1, device="cuda", pool=None):
         self.shape = shape
         self.dtype = shape.dtype
         self.tdtype = torch.bfloat16 if self.dtype == "bf16" else torch.float32
@@ -41,7 +57,7 @@ class DeviceLayer:
         self.cache = torch.zeros((batch, frames * tpf, shape.d_c + shape.d_rope),
                                  dtype=self.tdtype, device=device)
         assert self.cache.numel() * self.cache.element_size() == _lib.cache_bytes(self.cfg, batch)
-        self._ws = None
+        self.pool = pool if pool is not None else WorkspacePool(device)
 
     def absorb_value(self):
         """Compute B = [B_1 .. B_nh] (B_h = W_O,h W^V_up,h) on the device and make
@@ -71,9 +87,7 @@ class DeviceLayer:
         n = _lib.workspace_bytes(self.cfg, chunk)
         if n == 0:
             raise _lib.MLAError(_lib.validate(self.cfg, chunk), "mla_workspace_bytes")
-        if self._ws is None or self._ws.numel() < n:
-            self._ws = torch.empty(n + 256, dtype=torch.uint8, device=self.device)
-        return self._ws
+        return self.pool.get(n)
 
     def tokens(self, x_host):
         return to_device(x_host, self.dtype, self.device)

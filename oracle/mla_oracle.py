@@ -20,7 +20,9 @@ Readings taken where the paper is silent (same numbering as the design notes):
   * RoPE frequencies: axis group widths of a full-d_head split, D_y = D_x =
     2*floor(d_head/6), D_t = d_head - 2*D_y; pair k of axis a rotates by
     theta^(-2k/D_a) per unit position, k from 0 (the highest-frequency bands,
-    §3.2 and App. D.3); theta = 10000.
+    §3.2 and App. D.3); theta = 10000.  A layer may instead carry an explicit
+    per-pair table (an input, shared with the GPU like the weights), so that
+    parity does not rest on this reading.
   * Pair m is channels (2m, 2m+1) = (re, im), axis order t, y, x; the same
     rotation e^{+i*angle} for queries and keys.
   * Position of token n of latent frame f: (t, y, x) = (f, n // grid_w,
@@ -44,11 +46,12 @@ Readings taken where the paper is silent (same numbering as the design notes):
 import numpy as np
 
 __all__ = [
-    "rope_pair_split", "rope_omegas", "rope3d", "rmsnorm", "token_positions",
+    "rope_pair_split", "rope_omegas", "rope_frequencies", "rope3d", "rmsnorm", "token_positions",
     "ring_slot", "window_frames", "ring_rows_for_window", "context_times", "visible_keys",
     "cache_entries", "expected_ring", "query_parts", "reconstruct_kv",
     "attention_unabsorbed", "attention_absorbed", "query_absorbed", "value_absorbed_output",
-    "output_projection", "step", "cache_scalars_per_token", "dense_scalars_per_token",
+    "output_projection", "step", "chunk_frame_ids", "cache_scalars_per_token",
+    "dense_scalars_per_token",
 ]
 
 
@@ -83,6 +86,20 @@ def rope_omegas(d_head, pairs, theta=10000.0):
             omegas.append(float(theta) ** (-2.0 * k / widths[axis]))
             axes.append(axis)
     return np.array(omegas, dtype=np.float64), np.array(axes, dtype=np.int64)
+
+
+def rope_frequencies(s):
+    """Angular frequency and axis of every RoPE pair of a layer.  A layer may carry
+    an explicit table (rope_freq, one value per pair in t, y, x order, an input
+    like the weights); a missing or all-zero table means the bands derived from
+    theta by rope_omegas."""
+    om, ax = rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
+    table = getattr(s, "rope_freq", None)
+    if table is not None and any(float(v) != 0.0 for v in table):
+        if len(table) != len(om):
+            raise ValueError(f"rope_freq has {len(table)} entries for {len(om)} pairs")
+        om = np.asarray(table, dtype=np.float64)
+    return om, ax
 
 
 def rope3d(v, pos, omegas, axes):
@@ -185,7 +202,7 @@ def cache_entries(s, w, x, frames, times=None):
     x = np.asarray(x, dtype=np.float64)
     c = rmsnorm(x @ w["w_kv_down"].T, w["g_kv"], s.rms_eps)
     k_r = x @ w["w_kr"].T
-    om, ax = rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
+    om, ax = rope_frequencies(s)
     pos = token_positions(frames, s.grid_h, s.grid_w, times)
     return c, k_r, rope3d(k_r, pos, om, ax)
 
@@ -217,7 +234,7 @@ def query_parts(s, w, x, frames, times=None):
     c_q = rmsnorm(x @ w["w_q_down"].T, w["g_q"], s.rms_eps)
     q_nope = (c_q @ w["w_q_up"].T).reshape(n, s.n_heads, s.d_nope)
     q_r = (c_q @ w["w_qr"].T).reshape(n, s.n_heads, s.d_rope)
-    om, ax = rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
+    om, ax = rope_frequencies(s)
     pos = token_positions(frames, s.grid_h, s.grid_w, times)[:, None, :]
     return c_q, q_nope, rope3d(q_r, pos, om, ax)
 
@@ -294,22 +311,36 @@ def attention_absorbed(s, w, c_q, q_rope, c, k_rope):
     return y
 
 
-def step(s, w, x_window, window_ids, chunk_ids, query_rows=None):
-    """One chunk step for one batch element: cache entries for every attended
-    frame, queries for the chunk, attention, and W_O.  x_window holds the tokens
-    of window_ids (context order: sink frames, then the local window
-    chronologically); the chunk frames are the last ones, or all frames so far.
-    Keys and queries are rotated at absolute t, or at their frame's index in the
-    context when the shape rotates on window assembly (App. D.5).  query_rows
-    optionally restricts the queries to a subset of chunk tokens (indices into
-    the chunk).  With causal blocks (the training-time forward over a clip) each
-    query sees the context only up to the end of its block.  Returns
-    dict(out=(Nq, H*d_h), y=(Nq, d), c, k_rope)."""
-    tpf = s.tokens_per_frame
+def chunk_frame_ids(s):
+    """Absolute indices of the chunk's latent frames: t0 .. t0 + C - 1."""
+    return list(range(s.t0, s.t0 + s.chunk_frames))
+
+
+def _frame_tokens(tokens, f):
+    x = tokens(f) if callable(tokens) else tokens[f]
+    return np.asarray(x, dtype=np.float64)
+
+
+def step(s, w, tokens, query_rows=None):
+    """One chunk step for one batch element.  The attended frames are derived
+    here from the chunk (t0, C), the window length n_valid and the sink
+    (window_frames, App. D.4): the sink frames generated so far, then the local
+    window chronologically, the chunk's frames last.  tokens maps an absolute
+    frame index to that frame's (tpf, d) tokens (a dict, or a callable).  Cache
+    entries are formed for every attended frame, queries for the chunk, then
+    attention and W_O.  Keys and queries are rotated at absolute t, or at their
+    frame's index in the context when the shape rotates on window assembly
+    (App. D.5).  query_rows optionally restricts the queries to a subset of chunk
+    tokens (indices into the chunk).  With causal blocks (the training-time
+    forward over a clip) each query sees the context only up to the end of its
+    block.  Returns dict(out=(Nq, H*d_h), y=(Nq, d), c, k_rope, window_ids)."""
+    window_ids = window_frames(s.t0, s.chunk_frames, s.n_valid_frames,
+                               getattr(s, "sink_frames", 0))
+    chunk_ids = chunk_frame_ids(s)
+    x_window = np.concatenate([_frame_tokens(tokens, f) for f in window_ids])
     times = context_times(window_ids, getattr(s, "rope_at_read", False))
     c, _, k_rope = cache_entries(s, w, x_window, window_ids, times)
-    first = window_ids.index(chunk_ids[0])
-    x_chunk = np.asarray(x_window[first * tpf:(first + len(chunk_ids)) * tpf], dtype=np.float64)
+    x_chunk = np.concatenate([_frame_tokens(tokens, f) for f in chunk_ids])
     _, q_nope, q_rope = query_parts(s, w, x_chunk, chunk_ids, times)
     visible = visible_keys(s, window_ids, chunk_ids)
     if query_rows is not None:
@@ -318,4 +349,5 @@ def step(s, w, x_window, window_ids, chunk_ids, query_rows=None):
     masked = bool(getattr(s, "causal_frames", 0))
     out = attention_unabsorbed(s, w, q_nope, q_rope, c, k_rope,
                                visible=visible if masked else None)
-    return {"out": out, "y": output_projection(w, out), "c": c, "k_rope": k_rope}
+    return {"out": out, "y": output_projection(w, out), "c": c, "k_rope": k_rope,
+            "window_ids": window_ids}

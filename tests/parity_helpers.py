@@ -55,17 +55,20 @@ def assert_cache_rows(got, ref, dtype, what):
 class Run:
     """A layer on the GPU plus the exact inputs the oracle uses."""
 
-    def __init__(self, shape, seed=0, random_gains=False, scale=None, batch=1, layer=0):
+    def __init__(self, shape, seed=0, random_gains=False, scale=None, batch=1, layer=0,
+                 pool=None):
         from latent_kv_attention_down_amd.layer import DeviceLayer
         self.s = shape
         self.batch = batch
         self.stored, self.w = W.draw_weights(shape, layer=layer, seed=seed,
                                              random_gains=random_gains, scale=scale)
-        self.L = DeviceLayer(shape, self.stored, batch=batch)
+        self.L = DeviceLayer(shape, self.stored, batch=batch, pool=pool)
         self.seed = seed
         self.layer = layer
-        self.window_ids = shape.window_frame_ids
-        self.chunk_ids = shape.chunk_frame_ids
+        # the frames to draw and prefill are the ones the oracle says are attended
+        self.window_ids = O.window_frames(shape.t0, shape.chunk_frames, shape.n_valid_frames,
+                                          shape.sink_frames)
+        self.chunk_ids = O.chunk_frame_ids(shape)
         xs, xe = W.draw_frames(shape, self.window_ids, layer=layer, seed=seed, batch=batch)
         self.x_store, self.x = xs, xe
         tpf = shape.tokens_per_frame
@@ -89,9 +92,13 @@ class Run:
     def chunk_tokens(self):
         return self.L.tokens(self.x_store[:, self.chunk_slice])
 
+    def frame_tokens(self, b=0):
+        """Exact tokens of request b by absolute frame, as written to the GPU."""
+        return {f: self.x[b][i * self.tpf:(i + 1) * self.tpf]
+                for i, f in enumerate(self.window_ids)}
+
     def oracle(self, b=0, query_rows=None):
-        return O.step(self.s, self.w, self.x[b], self.window_ids, self.chunk_ids,
-                      query_rows=query_rows)
+        return O.step(self.s, self.w, self.frame_tokens(b), query_rows=query_rows)
 
     def oracle_ring(self, b=0):
         return O.expected_ring(self.s, self.w, self.x[b], self.window_ids)

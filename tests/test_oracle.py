@@ -26,11 +26,23 @@ def small_wan(**kw):
     return base.with_(**kw)
 
 
+def window_ids(s):
+    """The attended frames as the oracle derives them (sink frames, then the local
+    window), from the chunk, the window length and the sink."""
+    return O.window_frames(s.t0, s.chunk_frames, s.n_valid_frames, s.sink_frames)
+
+
 def layer_inputs(s, seed=0, random_gains=True):
     _, w = W.draw_weights(s, seed=seed, random_gains=random_gains)
-    ids = s.window_frame_ids
+    ids = window_ids(s)
     _, x = W.draw_frames(s, ids, seed=seed)
     return w, ids, x[0]
+
+
+def by_frame(s, ids, x):
+    """Frame index -> its tokens, for tokens x laid out frame after frame in ids."""
+    tpf = s.tokens_per_frame
+    return {f: x[i * tpf:(i + 1) * tpf] for i, f in enumerate(ids)}
 
 
 # ---------------------------------------------------------------- pin bodies
@@ -67,7 +79,7 @@ def pin_absorbed(o, s=None):
     oracle's unabsorbed step must equal Eq. 8-12 evaluated through A_h and B_h."""
     s = s or small_wan()
     w, ids, x = layer_inputs(s)
-    r = o.step(s, w, x, ids, s.chunk_frame_ids)
+    r = o.step(s, w, by_frame(s, ids, x))
     tpf = s.tokens_per_frame
     c_q, _, q_rope = o.query_parts(s, w, x[-s.chunk_frames * tpf:], s.chunk_frame_ids)
     y2 = o.attention_absorbed(s, w, c_q, q_rope, r["c"], r["k_rope"])
@@ -81,7 +93,7 @@ def pin_sdpa(o, s=None):
     (§3.3 Eq. 7 written as a dense attention layer, App. D.3)."""
     s = s or small_wan()
     w, ids, x = layer_inputs(s)
-    r = o.step(s, w, x, ids, s.chunk_frame_ids)
+    r = o.step(s, w, by_frame(s, ids, x))
     tpf = s.tokens_per_frame
     _, q_nope, q_rope = o.query_parts(s, w, x[-s.chunk_frames * tpf:], s.chunk_frame_ids)
     k_nope, v = o.reconstruct_kv(s, w, r["c"])
@@ -171,7 +183,7 @@ def pin_bruteforce(o):
     whose RoPE pairs cover all three axes and two frequency bands each."""
     s = tiny_brute_shape()
     w, ids, x = layer_inputs(s, seed=3)
-    r = o.step(s, w, x, ids, s.chunk_frame_ids)
+    r = o.step(s, w, by_frame(s, ids, x))
     for token in (0, 4, 7, 11):
         yb = np.array(brute_force_y(s, w, x, ids, s.chunk_frame_ids, token))
         err = np.abs(yb - r["y"][token]).max() / np.abs(yb).max()
@@ -263,27 +275,27 @@ def pin_read_rotation(o):
     key and query at its frame's index in the context."""
     s = small_wan(window_frames=4, n_valid_frames=4, chunk_frames=2, t0=8)
     w, ids, x = layer_inputs(s)
-    a = o.step(s, w, x, ids, s.chunk_frame_ids)
-    b = o.step(s.with_(rope_at_read=True), w, x, ids, s.chunk_frame_ids)
+    a = o.step(s, w, by_frame(s, ids, x))
+    b = o.step(s.with_(rope_at_read=True), w, by_frame(s, ids, x))
     assert np.abs(a["y"] - b["y"]).max() < 1e-12 * np.abs(a["y"]).max()
     sr = small_wan(window_frames=3, n_valid_frames=3, chunk_frames=2, t0=38, rope_at_read=True,
                    sink_frames=1)
     w, ids, x = layer_inputs(sr)
     assert ids == [0, 37, 38, 39]
     early = sr.with_(t0=8)
-    ids_e = early.window_frame_ids
+    ids_e = window_ids(early)
     assert ids_e == [0, 7, 8, 9]
-    r1 = o.step(sr, w, x, ids, sr.chunk_frame_ids)
-    r2 = o.step(early, w, x, ids_e, early.chunk_frame_ids)
+    r1 = o.step(sr, w, by_frame(sr, ids, x))
+    r2 = o.step(early, w, by_frame(early, ids_e, x))
     assert np.abs(r1["y"] - r2["y"]).max() < 1e-12 * np.abs(r1["y"]).max()
-    a1 = o.step(sr.with_(rope_at_read=False), w, x, ids, sr.chunk_frame_ids)
-    a2 = o.step(early.with_(rope_at_read=False), w, x, ids_e, early.chunk_frame_ids)
+    a1 = o.step(sr.with_(rope_at_read=False), w, by_frame(sr, ids, x))
+    a2 = o.step(early.with_(rope_at_read=False), w, by_frame(early, ids_e, x))
     assert not np.allclose(a1["y"], a2["y"])
     sb = tiny_brute_shape().with_(rope_at_read=True, sink_frames=1)
     w, ids, x = layer_inputs(sb, seed=5)
     assert ids == [0, 4, 5, 6]
     times = {f: i for i, f in enumerate(ids)}
-    r = o.step(sb, w, x, ids, sb.chunk_frame_ids)
+    r = o.step(sb, w, by_frame(sb, ids, x))
     for token in (0, 5, 9, 11):
         yb = np.array(brute_force_y(sb, w, x, ids, sb.chunk_frame_ids, token, times=times))
         err = np.abs(yb - r["y"][token]).max() / np.abs(yb).max()
@@ -303,36 +315,129 @@ def pin_chunk_causal(o):
     w, ids, x = layer_inputs(s)
     assert ids == list(range(6))
     tpf = s.tokens_per_frame
-    r = o.step(s, w, x, ids, s.chunk_frame_ids)
+    r = o.step(s, w, by_frame(s, ids, x))
     for k in range(3):
         dk = s.with_(chunk_frames=2, t0=2 * k, n_valid_frames=2 * k + 2, causal_frames=0)
-        ids_k = dk.window_frame_ids
+        ids_k = window_ids(dk)
         assert ids_k == list(range(2 * k + 2))
-        rk = o.step(dk, w, x[:len(ids_k) * tpf], ids_k, dk.chunk_frame_ids)
+        rk = o.step(dk, w, by_frame(s, ids, x))
         got = r["y"][2 * k * tpf:(2 * k + 2) * tpf]
         assert np.abs(got - rk["y"]).max() < 1e-12 * np.abs(rk["y"]).max(), k
     sb = tiny_brute_shape().with_(window_frames=4, chunk_frames=4, t0=0, n_valid_frames=4,
                                   causal_frames=2)
     wb, idb, xb = layer_inputs(sb, seed=4)
-    rb = o.step(sb, wb, xb, idb, sb.chunk_frame_ids)
+    rb = o.step(sb, wb, by_frame(sb, idb, xb))
     tb = sb.tokens_per_frame
     for token in (0, 7, 12, 23):
         vis = (token // tb) // 2 * 2 + 2
         yb = np.array(brute_force_y(sb, wb, xb[:vis * tb], idb[:vis], sb.chunk_frame_ids, token))
         err = np.abs(yb - rb["y"][token]).max() / np.abs(yb).max()
         assert err < 1e-12, (token, err)
-    full = o.step(s.with_(causal_frames=6), w, x, ids, s.chunk_frame_ids)
-    plain = o.step(s.with_(causal_frames=0), w, x, ids, s.chunk_frame_ids)
+    full = o.step(s.with_(causal_frames=6), w, by_frame(s, ids, x))
+    plain = o.step(s.with_(causal_frames=0), w, by_frame(s, ids, x))
     assert np.array_equal(full["y"], plain["y"])
     x2 = x.copy()
     x2[5 * tpf:] += 1.0
-    r2 = o.step(s, w, x2, ids, s.chunk_frame_ids)
+    r2 = o.step(s, w, by_frame(s, ids, x2))
     assert np.array_equal(r2["y"][:4 * tpf], r["y"][:4 * tpf])
     assert not np.allclose(r2["y"][4 * tpf:], r["y"][4 * tpf:])
 
 
+def pin_rmsnorm(o):
+    """RMSNorm (App. D.2 normalises c^KV and c^Q) against what the mathematics
+    fixes, not against a restatement of its formula:
+    (a) with unit gain and eps = 0 every output row has root-mean-square 1;
+    (b) it is invariant to positive scaling of the row at eps = 0, and eps
+        scales with the square of the row: RMSNorm(a u; a^2 eps) = RMSNorm(u; eps);
+    (c) the gain multiplies the normalised row elementwise;
+    (d) with unit gain the output's mean square is ms / (ms + eps), ms the
+        input's: eps sits inside the root, added to the mean square;
+    (e) a library routine: torch.nn.functional.rms_norm in fp64;
+    (f) a worked case: (3, 4) has mean square 12.5, so it maps to (3, 4) / sqrt(12.5);
+    (g) rows are normalised independently of each other."""
+    rng = np.random.default_rng(11)
+    n = 24
+    u = rng.normal(size=(40, n)) * rng.uniform(0.01, 10.0, size=(40, 1))
+    ones = np.ones(n)
+    r0 = o.rmsnorm(u, ones, 0.0)
+    assert np.allclose(np.sqrt(np.mean(r0 * r0, axis=-1)), 1.0, rtol=1e-14, atol=0)
+    for a in (1e-3, 0.5, 7.0, 1e4):
+        assert np.allclose(o.rmsnorm(a * u, ones, 0.0), r0, rtol=1e-13, atol=0)
+        assert np.allclose(o.rmsnorm(a * u, ones, 0.3 * a * a), o.rmsnorm(u, ones, 0.3),
+                           rtol=1e-13, atol=0)
+    g = rng.normal(1.0, 0.5, size=n)
+    assert np.allclose(o.rmsnorm(u, g, 1e-6), o.rmsnorm(u, ones, 1e-6) * g, rtol=1e-14, atol=0)
+    eps = 0.25
+    ms = np.mean(u * u, axis=-1)
+    r = o.rmsnorm(u, ones, eps)
+    assert np.allclose(np.mean(r * r, axis=-1), ms / (ms + eps), rtol=1e-13, atol=0)
+    for e in (1e-6, eps):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(u), (n,), weight=torch.from_numpy(g),
+                                           eps=e).numpy()
+        assert np.allclose(o.rmsnorm(u, g, e), ref, rtol=1e-13, atol=1e-15)
+    assert np.allclose(o.rmsnorm(np.array([3.0, 4.0]), np.ones(2), 0.0),
+                       np.array([3.0, 4.0]) / math.sqrt(12.5), rtol=1e-15, atol=0)
+    one = np.stack([o.rmsnorm(u[i], g, eps) for i in range(u.shape[0])])
+    assert np.allclose(one, o.rmsnorm(u, g, eps), rtol=1e-15, atol=0)
+
+
+def pin_rope_table(o):
+    """An explicit per-pair frequency table is used as given: rotating unit vectors
+    e_2m through the layer's key path gives (cos, sin) of the table's angle for
+    pair m at the token's coordinate on that pair's axis (§3.2 Eq. 5 with the
+    frequencies as an input), and an all-zero table means the derived bands."""
+    s = tiny_brute_shape()
+    om_derived, ax = o.rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
+    table = tuple(0.05 + 0.11 * m for m in range(s.d_rope // 2))
+    st = s.with_(rope_freq=table)
+    om, ax2 = o.rope_frequencies(st)
+    assert np.array_equal(ax, ax2) and np.array_equal(om, np.array(table))
+    om0, _ = o.rope_frequencies(s.with_(rope_freq=(0.0,) * (s.d_rope // 2)))
+    assert np.array_equal(om0, om_derived)
+    # the key path: W^K_R = identity on the first d_rope input channels, so k^R = x
+    w = {"w_kv_down": np.ones((s.d_c, s.d_model)), "g_kv": np.ones(s.d_c),
+         "w_kr": np.eye(s.d_rope, s.d_model)}
+    frames = [3, 11]
+    tpf = s.tokens_per_frame
+    for m in range(s.d_rope // 2):
+        x = np.zeros((len(frames) * tpf, s.d_model))
+        x[:, 2 * m] = 1.0
+        _, _, k_rope = o.cache_entries(st, w, x, frames)
+        for i, f in enumerate(frames):
+            for nn in range(tpf):
+                p = (f, nn // s.grid_w, nn % s.grid_w)[ax[m]]
+                row = k_rope[i * tpf + nn]
+                assert abs(row[2 * m] - math.cos(p * table[m])) < 1e-14
+                assert abs(row[2 * m + 1] - math.sin(p * table[m])) < 1e-14
+                others = np.delete(row, [2 * m, 2 * m + 1])
+                assert np.all(others == 0)
+
+
+def pin_window_derivation(o):
+    """The step derives its attended frames from (t0, C, n_valid, S) itself: frames
+    it does not attend are never read (a token source that refuses them), and the
+    returned window matches explicit cases of App. D.4 (sink first, then the
+    chronological window, the chunk last)."""
+    cases = [(small_wan(), [0, 1, 2, 3]),
+             (small_wan(window_frames=4, t0=9, n_valid_frames=3), [7, 8, 9]),
+             (small_wan(window_frames=3, n_valid_frames=3, chunk_frames=2, t0=38,
+                        rope_at_read=True, sink_frames=1), [0, 37, 38, 39])]
+    for s, expect in cases:
+        w, ids, x = layer_inputs(s)
+        assert ids == expect
+        tok = by_frame(s, ids, x)
+
+        def source(f, tok=tok):
+            if f not in tok:
+                raise AssertionError(f"frame {f} read but not attended")
+            return tok[f]
+        r = o.step(s, w, source)
+        assert r["window_ids"] == expect
+
+
 ALL_PINS = [pin_accounting, pin_absorbed, pin_sdpa, pin_bruteforce, pin_rope, pin_positions,
-            pin_sink_context, pin_read_rotation, pin_chunk_causal]
+            pin_sink_context, pin_read_rotation, pin_chunk_causal, pin_rmsnorm, pin_rope_table,
+            pin_window_derivation]
 
 
 # ---------------------------------------------------------------- the pins as tests
@@ -369,6 +474,42 @@ def test_token_positions():
     pin_positions(O)
 
 
+def test_rmsnorm_properties():
+    pin_rmsnorm(O)
+
+
+def test_explicit_rope_table():
+    pin_rope_table(O)
+
+
+def test_step_derives_its_window():
+    pin_window_derivation(O)
+
+
+def test_generator_window_matches_oracle():
+    """The seeded-input module lists a shape's attended frames too (it decides which
+    frames to draw and prefill); that list must be the oracle's window_frames for
+    every named workload and for random chunk/window/sink draws, so no expected
+    value rests on the generator's copy of the ring bookkeeping."""
+    for name, s in W.SHAPES.items():
+        assert s.window_frame_ids == window_ids(s), name
+    rng = np.random.default_rng(5)
+    base = W.shape_by_name("tiny-f32")
+    checked = 0
+    while checked < 500:
+        sink = int(rng.integers(0, 3))
+        wf = int(rng.integers(1, 9))
+        c = int(rng.integers(1, wf + 1))
+        t0 = int(rng.integers(0, 300))
+        nv = int(rng.integers(c, wf + 1))
+        s = base.with_(window_frames=wf, chunk_frames=c, t0=t0, n_valid_frames=nv,
+                       sink_frames=sink, rope_at_read=bool(sink))
+        if t0 + c - nv < sink:  # the local window would reach into the sink
+            continue
+        assert s.window_frame_ids == window_ids(s), s
+        checked += 1
+
+
 def test_rank_bound():
     """P-4: the composed operator [W_up^K W_down^KV; W_up^V W_down^KV] has rank at
     most d_c (§4 spectral analysis of the MLA projection)."""
@@ -384,7 +525,7 @@ def test_single_key_returns_its_value():
     """P-6: with one valid key the softmax weight is 1, so out_h = W_up,h^V c_j."""
     s = small_wan(grid_h=1, grid_w=1, n_valid_frames=1)
     w, ids, x = layer_inputs(s)
-    r = O.step(s, w, x, ids, s.chunk_frame_ids)
+    r = O.step(s, w, by_frame(s, ids, x))
     c = r["c"][0]
     for h in range(s.n_heads):
         v = w["w_v_up"][h * s.d_head:(h + 1) * s.d_head] @ c
@@ -396,7 +537,7 @@ def test_zero_query_averages_values():
     s = small_wan()
     w, ids, x = layer_inputs(s)
     w = dict(w, w_q_up=np.zeros_like(w["w_q_up"]), w_qr=np.zeros_like(w["w_qr"]))
-    r = O.step(s, w, x, ids, s.chunk_frame_ids)
+    r = O.step(s, w, by_frame(s, ids, x))
     _, v = O.reconstruct_kv(s, w, r["c"])
     mean = v.mean(axis=0).reshape(-1)
     assert np.allclose(r["out"], mean[None, :], rtol=1e-12, atol=1e-12)
@@ -409,7 +550,7 @@ def test_identical_keys_give_uniform_weights():
     w, ids, x = layer_inputs(s)
     x = np.broadcast_to(x[:1], x.shape).copy()
     w = dict(w, w_kr=np.zeros_like(w["w_kr"]))
-    r = O.step(s, w, x, ids, s.chunk_frame_ids)
+    r = O.step(s, w, by_frame(s, ids, x))
     _, v = O.reconstruct_kv(s, w, r["c"][:1])
     assert np.allclose(r["out"], v.reshape(1, -1), rtol=1e-12, atol=1e-12)
 
@@ -511,13 +652,13 @@ def test_chunk_causal_visible_keys():
     """Prefix lengths of the block mask: a 21-frame clip in 3-frame blocks, and a
     chunk that follows cached frames (the blocks start after them)."""
     s = W.shape_by_name("wan1.3b-clip21-causal3")
-    v = O.visible_keys(s, s.window_frame_ids, s.chunk_frame_ids)
+    v = O.visible_keys(s, window_ids(s), s.chunk_frame_ids)
     tpf = s.tokens_per_frame
     assert v.shape == (21 * tpf,)
     assert v[0] == v[3 * tpf - 1] == 3 * tpf and v[3 * tpf] == 6 * tpf and v[-1] == 21 * tpf
     assert int(v.sum()) == W.attended_pairs(s) == tpf * tpf * 3 * 3 * (1 + 2 + 3 + 4 + 5 + 6 + 7)
     t = small_wan(window_frames=6, chunk_frames=4, t0=2, n_valid_frames=6, causal_frames=2)
-    v = O.visible_keys(t, t.window_frame_ids, t.chunk_frame_ids)
+    v = O.visible_keys(t, window_ids(t), t.chunk_frame_ids)
     tp = t.tokens_per_frame
     assert list(v[::tp]) == [4 * tp, 4 * tp, 6 * tp, 6 * tp]
     assert int(v.sum()) == W.attended_pairs(t)
@@ -547,7 +688,8 @@ from oracle import mla_oracle as _M  # noqa: E402
 
 _ORIG = {k: getattr(_M, k) for k in ("rope3d", "rmsnorm", "reconstruct_kv",
                                      "attention_unabsorbed", "rope_omegas", "visible_keys",
-                                     "value_absorbed_output", "query_absorbed")}
+                                     "value_absorbed_output", "query_absorbed",
+                                     "window_frames")}
 
 
 def _mut_rope_sign(v, pos, omegas, axes):
@@ -641,10 +783,44 @@ def _mut_a_other_head_keys(s, w, h):
     return wq.T @ w["w_k_up"][g * s.d_nope:(g + 1) * s.d_nope]
 
 
+def _mut_rmsnorm_eps_outside(u, g, eps):
+    u = np.asarray(u, dtype=np.float64)
+    return u / (np.sqrt(np.mean(u * u, axis=-1, keepdims=True)) + eps) * g
+
+
+def _mut_rmsnorm_gain_inside(u, g, eps):
+    u = np.asarray(u, dtype=np.float64) * g
+    return u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+
+
+def _mut_rmsnorm_unbiased(u, g, eps):
+    u = np.asarray(u, dtype=np.float64)
+    n = u.shape[-1]
+    return u / np.sqrt(np.sum(u * u, axis=-1, keepdims=True) / max(n - 1, 1) + eps) * g
+
+
+def _mut_rmsnorm_no_eps(u, g, eps):
+    return _ORIG["rmsnorm"](u, g, 0.0)
+
+
+def _mut_rope_table_ignored(s):
+    return _M.rope_omegas(s.d_head, s.rope_pairs, s.rope_theta)
+
+
+def _mut_window_short(t0, chunk_frames, n_valid_frames, sink_frames=0):
+    return _ORIG["window_frames"](t0, chunk_frames, n_valid_frames, sink_frames)[1:]
+
+
 MUTANTS = {
     "rope rotation sign": dict(rope3d=_mut_rope_sign),
     "rope axis order": dict(rope3d=_mut_rope_axes),
     "rmsnorm sum instead of mean": dict(rmsnorm=_mut_rmsnorm_sum),
+    "rmsnorm eps outside the root": dict(rmsnorm=_mut_rmsnorm_eps_outside),
+    "rmsnorm gain before the norm": dict(rmsnorm=_mut_rmsnorm_gain_inside),
+    "rmsnorm over n - 1": dict(rmsnorm=_mut_rmsnorm_unbiased),
+    "rmsnorm without eps": dict(rmsnorm=_mut_rmsnorm_no_eps),
+    "explicit rope table ignored": dict(rope_frequencies=_mut_rope_table_ignored),
+    "window one frame short": dict(window_frames=_mut_window_short),
     "head/channel order in W_up^K": dict(reconstruct_kv=_mut_kv_head_order),
     "dropped RoPE score term": dict(attention_unabsorbed=_mut_drop_rope_term),
     "scale 1/sqrt(d_nope)": dict(attention_unabsorbed=_mut_scale_nope_only),
@@ -670,6 +846,6 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     for pin in ALL_PINS:
         try:
             pin(_M)
-        except AssertionError:
+        except Exception:  # an assertion, or the pin cannot even run on the mutant
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake: {name}"

@@ -5,6 +5,7 @@ its own and earlier blocks.  Through the C ABI against the fp64 oracle, same
 tolerances as the other parity tests."""
 import pytest
 
+import oracle as O
 import workload as W
 from parity_helpers import Run
 from test_parity_gpu import full_step, sampled_full, small_wan
@@ -42,7 +43,7 @@ def test_blocks_with_sink_and_read_rotation():
     keys before the chunk are the sink's."""
     s = small_wan(rope_at_read=True, sink_frames=1, window_frames=4, chunk_frames=4, t0=8,
                   n_valid_frames=4, causal_frames=2)
-    assert s.window_frame_ids == [0, 8, 9, 10, 11]
+    assert O.window_frames(s.t0, s.chunk_frames, s.n_valid_frames, s.sink_frames) == [0, 8, 9, 10, 11]
     full_step(Run(s, random_gains=True))
 
 

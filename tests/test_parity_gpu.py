@@ -177,10 +177,39 @@ def sampled_full(shape, batch=1):
     return run, y
 
 
-def test_wan13b_layer_sampled():
-    """Wan-1.3B layer, 3-frame chunk over the 21-frame window: the launch the
-    benchmark times, checked on sampled query tokens (all heads) and cache rows."""
-    sampled_full(W.shape_by_name("wan1.3b-w21"))
+@pytest.mark.timeout(600)
+def test_wan13b_layer_full_tensors():
+    """Wan-1.3B layer, 3-frame chunk over the 21-frame window, in the launch the
+    benchmark times (mla_step with both absorbed weight sets), compared in full:
+    every element of y (4680 x 1536), of out_heads from mla_chunk_attention
+    (4680 x 1536, the unabsorbed query route and per-head W^V_up) and of the ring
+    (21 slots x 1560 tokens x 224, one bf16 ulp) against the oracle -- no sampling."""
+    s = W.shape_by_name("wan1.3b-w21")
+    run = Run(s)
+    say(f"case {s.name} full tensors: prefill {len(run.window_ids) - s.chunk_frames} frames")
+    run.prefill()
+    ch = run.chunk()
+    x = run.chunk_tokens()
+    run.L.cache_write(ch, x)
+    out = run.L.chunk_attention(ch, x)
+    torch.cuda.synchronize()
+    out_h = to_host(out)[0]
+    run.L.absorb_value()
+    run.L.absorb_query()
+    y = run.L.step(ch, x)  # writes the chunk's frames again (same values), then attends
+    torch.cuda.synchronize()
+    y_h = to_host(y)[0]
+    ring = to_host(run.L.cache)[0]
+    say("  device done; oracle over all 4680 query tokens ...")
+    ref = run.oracle()
+    assert out_h.shape == ref["out"].shape == (4680, 1536)
+    fro, mx = assert_close(out_h, ref["out"], TOL["bf16"], "out_heads (all elements)")
+    say(f"  out_heads: frobenius {fro:.3e}, max {mx:.3e}")
+    fro, mx = assert_close(y_h, ref["y"], TOL["bf16"], "y (all elements)")
+    say(f"  y: frobenius {fro:.3e}, max {mx:.3e}")
+    ref_ring = run.oracle_ring()
+    assert ring.shape == ref_ring.shape == (21 * 1560, 224)
+    assert_cache_rows(ring, ref_ring, "bf16", "ring (all 32760 rows)")
 
 
 @pytest.mark.parametrize("name,batch", [("wan1.3b-w21", 3), ("wan1.3b-sink1-w6-t240", 4)])
@@ -200,5 +229,5 @@ def test_window_sweep_sampled(name):
                                   "wan1.3b-w21-dc192-dr64"])
 def test_latent_width_variants_full_size_sampled(name):
     """The (d_c, d_rope) variants at full Wan-1.3B size, in the launch the sweep times
-    (d_c = 256 runs the two-waves-per-SIMD kernel)."""
+    (d_c = 256 runs the attention kernel with 32 query rows per wave)."""
     sampled_full(W.shape_by_name(name))

@@ -1,0 +1,56 @@
+"""GPU parity of the 30-layer chunk step: the Wan-1.3B backbone has 30 blocks
+(VideoMLA §4.1), each with its own latent cache (App. C.1 counts 30 cached
+layers; App. D.4 keeps one cache per layer).  Thirty layers with independent
+seeded weights, tokens and rings are stepped in turn on one stream with one
+shared workspace, exactly as the benchmark's --layers 30 mode times them, and
+checked through the C ABI against the fp64 oracle: the first and the last layer
+on every element of y and of the ring, the others on sampled query tokens (all
+heads) and sampled ring rows."""
+import numpy as np
+import pytest
+import torch
+
+import workload as W
+from latent_kv_attention_down_amd.layer import WorkspacePool, to_host
+from parity_helpers import TOL, Run, assert_cache_rows, assert_close, say
+from test_parity_gpu import sample_rows
+
+pytestmark = pytest.mark.gpu
+
+N_LAYERS = 30
+
+
+@pytest.mark.timeout(900)
+def test_thirty_layer_step():
+    s = W.shape_by_name("wan1.3b-w21")
+    pool = WorkspacePool()
+    runs = []
+    for l in range(N_LAYERS):
+        run = Run(s, layer=l, pool=pool)
+        run.L.absorb_value()
+        run.L.absorb_query()
+        run.prefill()
+        runs.append(run)
+        if (l + 1) % 10 == 0:
+            say(f"{l + 1} of {N_LAYERS} layers prefilled")
+    ch = runs[0].chunk()
+    ys = [run.L.step(ch, run.chunk_tokens()) for run in runs]
+    torch.cuda.synchronize()
+    say("30-layer step done on the device; checking each layer against the oracle")
+    ring_rng = np.random.default_rng(3)
+    for l, (run, y) in enumerate(zip(runs, ys)):
+        full = l in (0, N_LAYERS - 1)
+        rows = None if full else sample_rows(s, n=24, seed=100 + l)
+        ref = run.oracle(query_rows=rows)
+        y_h = to_host(y)[0]
+        fro, mx = assert_close(y_h if full else y_h[rows], ref["y"], TOL["bf16"], f"layer {l} y")
+        ring = to_host(run.L.cache)[0]
+        ref_ring = run.oracle_ring()
+        if full:
+            assert_cache_rows(ring, ref_ring, "bf16", f"layer {l} ring (all rows)")
+        else:
+            r = ring_rng.choice(ring.shape[0], 400, replace=False)
+            assert_cache_rows(ring[r], ref_ring[r], "bf16", f"layer {l} ring sample")
+        say(f"layer {l:2d} ({'full' if full else 'sampled'}): y frobenius {fro:.3e}, "
+            f"max {mx:.3e}")
+        run.x = run.x_store = None  # release the layer's host tokens

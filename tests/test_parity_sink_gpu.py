@@ -27,13 +27,13 @@ def test_sink_and_local_window():
     frame 10 from slot 1); the chunk is frames 12-13."""
     s = small_wan(rope_at_read=True, sink_frames=1, window_frames=3, chunk_frames=2, t0=12,
                   n_valid_frames=3)
-    assert s.window_frame_ids == [0, 11, 12, 13]
+    assert O.window_frames(s.t0, s.chunk_frames, s.n_valid_frames, s.sink_frames) == [0, 11, 12, 13]
     full_step(Run(s, random_gains=True))
 
 
 def test_sink_fp32_tiny():
     s = W.shape_by_name("tiny-f32").with_(rope_at_read=True, sink_frames=1, t0=6)
-    assert s.window_frame_ids == [0, 3, 4, 5, 6]
+    assert O.window_frames(s.t0, s.chunk_frames, s.n_valid_frames, s.sink_frames) == [0, 3, 4, 5, 6]
     full_step(Run(s, random_gains=True))
 
 
@@ -41,7 +41,7 @@ def test_sink_frame_attends_only_itself():
     """The first chunk of a rollout is the sink frame alone: no local frames."""
     s = small_wan(rope_at_read=True, sink_frames=1, window_frames=3, chunk_frames=1, t0=0,
                   n_valid_frames=0)
-    assert s.window_frame_ids == [0]
+    assert O.window_frames(s.t0, s.chunk_frames, s.n_valid_frames, s.sink_frames) == [0]
     full_step(Run(s))
 
 
@@ -65,9 +65,7 @@ def test_rollout_through_eviction():
     ring = to_host(L.cache)[0]
     ref_ring = O.expected_ring(s, w, xe[0], frames)
     assert_cache_rows(ring, ref_ring, "bf16", "ring after the rollout")
-    ids = s.window_frame_ids
-    x_ctx = np.concatenate([xe[0][f * tpf:(f + 1) * tpf] for f in ids])
-    ref = O.step(s, w, x_ctx, ids, s.chunk_frame_ids)
+    ref = O.step(s, w, {f: xe[0][f * tpf:(f + 1) * tpf] for f in frames})
     assert_close(to_host(out)[0], ref["out"], TOL["bf16"], "out_heads")
 
 

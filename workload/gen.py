@@ -72,13 +72,60 @@ def draw_weights(s, layer=0, seed=0, random_gains=False, scale=None):
 
 def draw_frames(s, frames, layer=0, seed=0, batch=None):
     """Inputs for the given absolute latent frames: shape (B, len(frames)*tpf, d).
-    Batch element b uses seed + 7919*b so requests differ."""
+    Batch element b uses seed + 7919*b so requests differ.  Every (request, frame)
+    has its own seed, so the frames are drawn and rounded on a few threads (NumPy
+    releases the GIL for both); the values do not depend on the thread count."""
     B = s.batch if batch is None else batch
     tpf = s.tokens_per_frame
-    out = np.empty((B, len(frames) * tpf, s.d_model), dtype=np.float64)
-    for b in range(B):
-        for i, f in enumerate(frames):
-            rng = np.random.Generator(np.random.PCG64(
-                np.random.SeedSequence([seed + 7919 * b, layer, 10000 + f])))
-            out[b, i * tpf:(i + 1) * tpf] = rng.normal(0.0, 1.0, size=(tpf, s.d_model))
-    return _store(out, s.dtype)
+    n = len(frames)
+    stored = np.empty((B, n * tpf, s.d_model), dtype=np.uint16 if s.dtype == "bf16"
+                      else np.float32)
+    exact = np.empty((B, n * tpf, s.d_model), dtype=np.float64)
+
+    def one(job):
+        b, i = divmod(job, n)
+        rng = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence([seed + 7919 * b, layer, 10000 + frames[i]])))
+        st, ex = _store(rng.normal(0.0, 1.0, size=(tpf, s.d_model)), s.dtype)
+        stored[b, i * tpf:(i + 1) * tpf] = st
+        exact[b, i * tpf:(i + 1) * tpf] = ex
+
+    jobs = B * n
+    if jobs * tpf * s.d_model < (1 << 20):
+        for j in range(jobs):
+            one(j)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(8, jobs)) as ex:
+            list(ex.map(one, range(jobs)))
+    return stored, exact
+
+
+def draw_rope_freq(s, seed=0, low=0.02, high=1.5):
+    """A random explicit RoPE frequency table (one fp32 value per pair, uniform in
+    [low, high) radians per position), drawn from SeedSequence([seed, 20000]) and
+    rounded to fp32 -- an input given to both sides like the weights."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 20000])))
+    v = rng.uniform(low, high, size=s.d_rope // 2).astype(np.float32)
+    return tuple(float(t) for t in v)
+
+
+class FrameTokens:
+    """Tokens of any absolute latent frame on demand, drawn with the per-frame seed
+    of draw_frames and cached: frames(f) -> (stored (tpf, d), exact fp64 (tpf, d))
+    for request b.  Calling the object returns the exact values, so it can be
+    handed to anything that asks for a frame's tokens."""
+
+    def __init__(self, s, layer=0, seed=0, b=0):
+        self.s, self.layer, self.seed, self.b = s, layer, seed, b
+        self._cache = {}
+
+    def frames(self, f):
+        if f not in self._cache:
+            st, ex = draw_frames(self.s, [f], layer=self.layer, seed=self.seed + 7919 * self.b,
+                                 batch=1)
+            self._cache[f] = (st[0], ex[0])
+        return self._cache[f]
+
+    def __call__(self, f):
+        return self.frames(f)[1]

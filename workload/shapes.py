@@ -32,6 +32,8 @@ class MLAShape:
     rope_at_read: bool = False # cache keeps k^R unrotated; rotation on window assembly
     sink_frames: int = 0       # leading frames kept for good (read-time rotation only)
     causal_frames: int = 0     # chunk-causal blocks of this many chunk frames (0: no mask)
+    rope_freq: tuple = None    # explicit radians per position for each RoPE pair (t, y, x
+                               # order), fp32 values; None: the bands derived from rope_theta
 
     @property
     def tokens_per_frame(self) -> int:

@@ -273,7 +273,7 @@ def main():
         for j, (L, x, y) in enumerate(layers):
             if evs is not None:
                 mla.set_timing_events(evs[j][0], evs[j][1])
-            mla.step(L.cfg, L.weights, chunk, x, L.cache, y, ws, stream)
+            mla.step(L.cfg, L.weights, chunk, x, L.cache_desc, y, ws, stream)
 
     for _ in range(args.warmup):
         one_step()
@@ -301,12 +301,12 @@ def main():
     # its merge and fallback, per-head value up-projection), layer 0, back to back
     out_heads = L0.new_out(chunk, s.n_heads * s.d_head)
     for _ in range(3):
-        mla.chunk_attention(L0.cfg, L0.weights, chunk, x0, L0.cache, out_heads, ws, stream)
+        mla.chunk_attention(L0.cfg, L0.weights, chunk, x0, L0.cache_desc, out_heads, ws, stream)
     torch.cuda.synchronize()
     ca_ev = [(hip.event(), hip.event()) for _ in range(K)]
     for a, b in ca_ev:
         hip.record(a, stream)
-        mla.chunk_attention(L0.cfg, L0.weights, chunk, x0, L0.cache, out_heads, ws, stream)
+        mla.chunk_attention(L0.cfg, L0.weights, chunk, x0, L0.cache_desc, out_heads, ws, stream)
         hip.record(b, stream)
     torch.cuda.synchronize()
     ca_ms = [hip.ms(a, b) for a, b in ca_ev]
@@ -315,12 +315,12 @@ def main():
     # cache write on its own: back-to-back launches between one pair of events
     wr_ch = L0.chunk(s.chunk_frames, s.t0, s.n_valid_frames)
     for _ in range(3):
-        mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache, stream)
+        mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache_desc, stream)
     torch.cuda.synchronize()
     nw = max(K, 20)
     hip.record(t_start, stream)
     for _ in range(nw):
-        mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache, stream)
+        mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache_desc, stream)
     hip.record(t_stop, stream)
     torch.cuda.synchronize()
     write_ms = hip.ms(t_start, t_stop) / nw
@@ -338,7 +338,7 @@ def main():
         for a, b in cold_ev:
             flush.fill_(1)
             hip.record(a, stream)
-            mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache, stream)
+            mla.cache_write(L0.cfg, L0.weights, wr_ch, x0, L0.cache_desc, stream)
             hip.record(b, stream)
         torch.cuda.synchronize()
         cold_us = [1e3 * hip.ms(a, b) for a, b in cold_ev]

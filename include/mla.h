@@ -33,6 +33,12 @@
  *     crosses this boundary.
  *   - Two calls that write the same cache, or share a workspace, must not run
  *     concurrently.
+ *   - Failure injection: with the environment variable MLA_FAULT_INJECT=launch,
+ *     every entry point that would launch a kernel returns MLA_ERR_HIP after
+ *     its argument checks and before anything reaches the HIP runtime, with
+ *     mla_last_error() naming the injection, so a caller's handling of launch
+ *     failures can be exercised without a GPU.  Unset (the default), it has no
+ *     effect.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -77,6 +83,10 @@ typedef struct {
   float rope_theta;      /* frequency base; pair k of axis a turns by              */
                          /* theta^(-2k/D_a) per position, D_y = D_x = 2*(d_head/6),*/
                          /* D_t = d_head - 2*D_y (highest bands first, §3.2)       */
+  float rope_freq[64];   /* explicit radians per position of pair p (the t pairs,  */
+                         /* then y, then x; entries past d_rope/2 ignored), each   */
+                         /* finite.  All d_rope/2 entries zero: the table is       */
+                         /* derived from rope_theta as above.                      */
   int32_t grid_h;        /* latent tokens per frame = grid_h * grid_w (30 x 52)    */
   int32_t grid_w;
   int32_t window_frames; /* W: local ring capacity in latent frames (21, or 6)     */
@@ -114,6 +124,33 @@ typedef struct {
                          /* needed); NULL: W^Q_up, (W^K_up,h)^T and W^Q_R apart     */
 } mla_weights;
 
+/*
+ * Where one layer's ring cache lives (App. D.4 keeps the inference cache as the
+ * two tensors c^KV, B x T_cache x d_c, and k^R, B x T_cache x d_rope).  Element
+ * i of ring row r of request b is at
+ *     c_kv + b * c_kv_batch_stride + r * c_kv_row_stride + i   (i < d_c)
+ *     k_r  + b * k_r_batch_stride  + r * k_r_row_stride  + i   (i < d_rope)
+ * in units of the element type cfg->dtype.  Rules (INVALID_ARG or ALIGNMENT
+ * otherwise): both pointers non-NULL and 16-byte aligned, distinct; row strides
+ * at least the part's width; row and batch strides multiples of 16 bytes; with
+ * batch > 1 a batch stride of at least (S + W) * tpf rows.  The two parts and the
+ * requests must not overlap.
+ * The interleaved layout -- one buffer of mla_cache_bytes(), row = [c^KV | k] of
+ * d_c + d_rope elements, k_r = c_kv + d_c, both row strides d_c + d_rope, both
+ * batch strides (S + W) * tpf * (d_c + d_rope), as mla_cache_interleaved() fills
+ * it -- is read in place by the attention kernels.  Any other layout is accepted
+ * by every entry point: its attended rows are first gathered into the workspace
+ * in that layout, which costs one extra read and write of the attended window.
+ */
+typedef struct {
+  void *c_kv;
+  void *k_r;
+  int64_t c_kv_row_stride;
+  int64_t k_r_row_stride;
+  int64_t c_kv_batch_stride;
+  int64_t k_r_batch_stride;
+} mla_cache;
+
 /* The chunk being generated and the window it sees.                             */
 typedef struct {
   int32_t batch;          /* B >= 1 independent requests (separate caches)        */
@@ -135,15 +172,14 @@ typedef struct {
 } mla_chunk;
 
 /*
- * Cache layout (every entry point that takes `cache`): S + W latent-frame slots
- * per request, contiguous, shape (B, (S + W) * grid_h * grid_w, d_c + d_rope),
- * element type cfg->dtype.  Frame f < S occupies slot f for good; frame f >= S
- * occupies slot S + (f - S) mod W (FIFO over the local slots).  Token n of the
- * frame (row-major over the grid) is row slot * grid_h * grid_w + n, holding
- * [ c^KV (d_c) | k (d_rope) ] with k = RoPE3D(k^R) at the token's absolute
- * position (t, y, x) = (f, n / grid_w, n % grid_w) under MLA_ROPE_AT_WRITE, or
- * the unrotated k^R under MLA_ROPE_AT_READ.  Only the d_c + d_rope scalars per
- * token are stored (App. E, Eq. 13).
+ * Ring contents (every entry point that takes `cache`): S + W latent-frame slots
+ * per request, (S + W) * grid_h * grid_w rows.  Frame f < S occupies slot f for
+ * good; frame f >= S occupies slot S + (f - S) mod W (FIFO over the local slots).
+ * Token n of the frame (row-major over the grid) is row slot * grid_h * grid_w +
+ * n, holding c^KV (d_c) and k (d_rope) with k = RoPE3D(k^R) at the token's
+ * absolute position (t, y, x) = (f, n / grid_w, n % grid_w) under
+ * MLA_ROPE_AT_WRITE, or the unrotated k^R under MLA_ROPE_AT_READ.  Only the
+ * d_c + d_rope scalars per token are stored (App. E, Eq. 13).
  */
 
 /* Host-only checks of cfg and chunk (no HIP call).  MLA_OK, INVALID_ARG or
@@ -161,18 +197,24 @@ size_t mla_workspace_bytes(const mla_config *cfg, const mla_chunk *chunk);
  * Host-only. */
 size_t mla_cache_bytes(const mla_config *cfg, int32_t batch);
 
+/* Fill *cache with the interleaved layout over `base`, a buffer of
+ * mla_cache_bytes(cfg, batch) bytes (see mla_cache).  MLA_OK, or INVALID_ARG /
+ * ALIGNMENT for an invalid cfg, a NULL or misaligned base, or batch < 1.
+ * Host-only; writes nothing but *cache. */
+int mla_cache_interleaved(const mla_config *cfg, int32_t batch, void *base, mla_cache *cache);
+
 /*
  * Cache write (§3.1 Eq. 1, App. D.2 RMSNorm, §3.2 Eq. 5, App. D.4 FIFO).
  *   x     (B, C * grid_h * grid_w, d) tokens of frames t0 .. t0+C-1, in order.
- *   cache ring described above; the rows of the slots of frames t0 .. t0+C-1
- *         are overwritten, evicting the frames that held them; nothing else is
- *         touched.  Only batch, chunk_frames and t0 of `chunk` are used; the
- *         chunk's frames >= S must fit the W local slots.
+ *   cache ring described above (any layout mla_cache allows); the rows of the
+ *         slots of frames t0 .. t0+C-1 are overwritten, evicting the frames that
+ *         held them; nothing else is touched.  Only batch, chunk_frames and t0 of
+ *         `chunk` are used; the chunk's frames >= S must fit the W local slots.
  * One fused kernel: [W^KV_down; W^K_R] x, RMSNorm of the latent, rotation of
  * k^R (MLA_ROPE_AT_WRITE only), rounding to cfg->dtype and the ring store.
  */
 int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
-                    const void *x, void *cache, void *stream);
+                    const void *x, const mla_cache *cache, void *stream);
 
 /*
  * Chunk attention (§3.3 Eq. 7 in the absorbed form of App. E Eq. 8-12).
@@ -184,11 +226,12 @@ int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk
  *   workspace device scratch of at least mla_workspace_bytes(cfg, chunk).
  * Every query attends to every valid cached token (no mask inside the window),
  * unless chunk->causal_frames cuts the chunk into causal blocks (see mla_chunk).
- * Under MLA_ROPE_AT_READ the attended frames are first gathered into the
- * workspace in context order with k^R rotated at window-local positions.
+ * Under MLA_ROPE_AT_READ, or with a cache that is not in the interleaved layout,
+ * the attended frames are first gathered into the workspace in context order
+ * (under MLA_ROPE_AT_READ with k^R rotated at window-local positions).
  */
 int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
-                        const void *x, const void *cache, void *out_heads,
+                        const void *x, const mla_cache *cache, void *out_heads,
                         void *workspace, size_t ws_bytes, void *stream);
 
 /*
@@ -200,7 +243,7 @@ int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_c
  *   y  (B, C * tpf, d).
  */
 int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
-             const void *x, void *cache, void *y, void *workspace, size_t ws_bytes,
+             const void *x, const mla_cache *cache, void *y, void *workspace, size_t ws_bytes,
              void *stream);
 
 /*
@@ -243,7 +286,7 @@ int mla_query_absorbed_weights(const mla_config *cfg, const mla_weights *w, void
  * attended as stored.
  */
 int mla_latent_attention(const mla_config *cfg, const mla_chunk *chunk, const void *q_lat,
-                         const void *cache, void *o_lat, void *workspace, size_t ws_bytes,
+                         const mla_cache *cache, void *o_lat, void *workspace, size_t ws_bytes,
                          void *stream);
 
 /* Measurement hook: when both are non-NULL, later calls on this thread record

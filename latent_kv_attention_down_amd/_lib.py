@@ -23,9 +23,15 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 class Config(ctypes.Structure):
     _fields_ = [("d_model", _i32), ("n_heads", _i32), ("d_head", _i32), ("d_nope", _i32),
                 ("d_rope", _i32), ("d_c", _i32), ("d_q", _i32), ("rope_pairs", _i32 * 3),
-                ("rope_theta", ctypes.c_float), ("grid_h", _i32), ("grid_w", _i32),
+                ("rope_theta", ctypes.c_float), ("rope_freq", ctypes.c_float * 64),
+                ("grid_h", _i32), ("grid_w", _i32),
                 ("window_frames", _i32), ("dtype", _i32), ("rms_eps", ctypes.c_float),
                 ("rope_mode", _i32), ("sink_frames", _i32)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("c_kv", _vp), ("k_r", _vp), ("c_kv_row_stride", _i64), ("k_r_row_stride", _i64),
+                ("c_kv_batch_stride", _i64), ("k_r_batch_stride", _i64)]
 
 
 class Weights(ctypes.Structure):
@@ -43,11 +49,14 @@ SIGNATURES = {
     "mla_validate": (ctypes.c_int, [_P(Config), _P(Chunk)]),
     "mla_workspace_bytes": (_sz, [_P(Config), _P(Chunk)]),
     "mla_cache_bytes": (_sz, [_P(Config), _i32]),
-    "mla_cache_write": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _vp, _vp]),
-    "mla_chunk_attention": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _vp, _vp,
+    "mla_cache_interleaved": (ctypes.c_int, [_P(Config), _i32, _vp, _P(Cache)]),
+    "mla_cache_write": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _P(Cache), _vp]),
+    "mla_chunk_attention": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _P(Cache), _vp,
                                            _vp, _sz, _vp]),
-    "mla_step": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _vp, _vp, _vp, _sz, _vp]),
-    "mla_latent_attention": (ctypes.c_int, [_P(Config), _P(Chunk), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_step": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _P(Cache), _vp, _vp, _sz,
+                                _vp]),
+    "mla_latent_attention": (ctypes.c_int, [_P(Config), _P(Chunk), _vp, _P(Cache), _vp, _vp, _sz,
+                                            _vp]),
     "mla_value_absorbed_weights": (ctypes.c_int, [_P(Config), _P(Weights), _vp, _vp]),
     "mla_query_absorbed_weights": (ctypes.c_int, [_P(Config), _P(Weights), _vp, _vp]),
     "mla_set_timing_events": (None, [_vp, _vp]),
@@ -59,9 +68,13 @@ SIGNATURES = {
 _lib = None
 
 
-def load(path=LIB_PATH):
-    """Load libmla.so once; raise if it is missing (there is no fallback path)."""
+def load(path=None):
+    """Load libmla.so once; raise if it is missing (there is no fallback path).
+    MLA_LIBRARY names another build of the same library (for instance the host-
+    sanitized one the ABI tests run against)."""
     global _lib
+    if path is None:
+        path = os.environ.get("MLA_LIBRARY") or LIB_PATH
     if _lib is None:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with "
@@ -100,6 +113,8 @@ def make_config(shape, dtype=None):
     for i, v in enumerate(shape.rope_pairs):
         c.rope_pairs[i] = int(v)
     c.rope_theta = float(shape.rope_theta)
+    for i, v in enumerate(getattr(shape, "rope_freq", None) or ()):
+        c.rope_freq[i] = float(v)
     c.rms_eps = float(shape.rms_eps)
     c.dtype = MLA_BF16 if dt == "bf16" else MLA_F32
     c.rope_mode = MLA_ROPE_AT_READ if getattr(shape, "rope_at_read", False) else MLA_ROPE_AT_WRITE
@@ -124,6 +139,36 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def interleaved_cache(cfg, batch, base):
+    """The mla_cache descriptor of the interleaved layout over one buffer (a device
+    tensor of mla_cache_bytes(cfg, batch) bytes, or a device address)."""
+    c = Cache()
+    addr = base if isinstance(base, int) or base is None else base.data_ptr()
+    _check(load().mla_cache_interleaved(ctypes.byref(cfg), int(batch), addr, ctypes.byref(c)),
+           "mla_cache_interleaved")
+    return c
+
+
+def split_cache(c_kv, k_r):
+    """The mla_cache descriptor of two separate device tensors, c_kv (B, rows, >= d_c)
+    and k_r (B, rows, >= d_rope) with unit column stride (any row and batch stride)."""
+    c = Cache()
+    c.c_kv, c.k_r = c_kv.data_ptr(), k_r.data_ptr()
+    c.c_kv_row_stride, c.k_r_row_stride = c_kv.stride(1), k_r.stride(1)
+    c.c_kv_batch_stride, c.k_r_batch_stride = c_kv.stride(0), k_r.stride(0)
+    return c
+
+
+def _cache(cfg, cache):
+    """A Cache struct as given, or the interleaved descriptor of a (B, rows, d_c +
+    d_rope) device tensor."""
+    if isinstance(cache, Cache):
+        return ctypes.byref(cache)
+    if cache is None:
+        return None
+    return ctypes.byref(interleaved_cache(cfg, cache.shape[0], cache))
+
+
 def _stream(stream):
     if stream is not None:
         return stream
@@ -145,19 +190,20 @@ def cache_bytes(cfg, batch):
 
 def cache_write(cfg, weights, chunk, x, cache, stream=None):
     _check(load().mla_cache_write(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(chunk),
-                                  _ptr(x), _ptr(cache), _stream(stream)), "mla_cache_write")
+                                  _ptr(x), _cache(cfg, cache), _stream(stream)), "mla_cache_write")
 
 
 def chunk_attention(cfg, weights, chunk, x, cache, out_heads, workspace, stream=None):
     _check(load().mla_chunk_attention(ctypes.byref(cfg), ctypes.byref(weights),
-                                      ctypes.byref(chunk), _ptr(x), _ptr(cache), _ptr(out_heads),
+                                      ctypes.byref(chunk), _ptr(x), _cache(cfg, cache),
+                                      _ptr(out_heads),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "mla_chunk_attention")
 
 
 def step(cfg, weights, chunk, x, cache, y, workspace, stream=None):
     _check(load().mla_step(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(chunk), _ptr(x),
-                           _ptr(cache), _ptr(y), _ptr(workspace),
+                           _cache(cfg, cache), _ptr(y), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)),
            "mla_step")
 
@@ -175,7 +221,7 @@ def query_absorbed_weights(cfg, weights, w_qlat, stream=None):
 
 def latent_attention(cfg, chunk, q_lat, cache, o_lat, workspace, stream=None):
     _check(load().mla_latent_attention(ctypes.byref(cfg), ctypes.byref(chunk), _ptr(q_lat),
-                                       _ptr(cache), _ptr(o_lat), _ptr(workspace),
+                                       _cache(cfg, cache), _ptr(o_lat), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream)), "mla_latent_attention")
 

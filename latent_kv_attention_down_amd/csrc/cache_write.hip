@@ -66,11 +66,18 @@ __device__ void finish_rows(float *tile, int ld, int rows, int m0, const CacheWr
   (void)N;
 }
 
-__device__ __forceinline__ int64_t ring_row(const CacheWriteArgs &a, int m) {
+// Address of column c (of the d_c + d_rope) of the ring row that chunk token m
+// goes to: request m / T_q, slot of its frame, token within the frame.  A
+// 16-byte piece of 8 columns never straddles the two parts (d_c % 8 == 0 on the
+// bf16 path).
+template <typename T>
+__device__ __forceinline__ T *ring_elem(const CacheWriteArgs &a, int m, int c) {
   const int b = m / a.T_q, i = m % a.T_q;
   const int64_t f = a.t0 + i / a.tpf;
   const int64_t slot = f < a.S ? f : a.S + (f - a.S) % a.W;
-  return (int64_t)b * a.cache_batch_rows + slot * a.tpf + (i % a.tpf);
+  const int64_t row = slot * a.tpf + (i % a.tpf);
+  return c < a.d_c ? (T *)a.ring.c_kv + b * a.ring.c_batch + row * a.ring.c_row + c
+                   : (T *)a.ring.k_r + b * a.ring.r_batch + row * a.ring.r_row + (c - a.d_c);
 }
 
 // bf16: the 32-token x tile stays in LDS for the whole reduction; wave w owns
@@ -258,10 +265,9 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteAr
   }
   __syncthreads();
   // 16-byte stores of the finished rows into the ring
-  bf16 *cache = (bf16 *)a.cache;
   for (int id = tid; id < kBM * (N / 8); id += NT) {
     const int r = id / (N / 8), c8 = (id % (N / 8)) * 8, m = m0 + r;
-    if (m < a.M) *(bf16x8 *)(cache + ring_row(a, m) * N + c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
+    if (m < a.M) *(bf16x8 *)ring_elem<bf16>(a, m, c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
   }
 }
 
@@ -452,10 +458,9 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArg
     }
   }
   __syncthreads();
-  bf16 *cache = (bf16 *)a.cache;
   for (int id = tid; id < kBM * (N / 8); id += NT) {
     const int r = id / (N / 8), c8 = (id % (N / 8)) * 8, m = m0 + r;
-    if (m < a.M) *(bf16x8 *)(cache + ring_row(a, m) * N + c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
+    if (m < a.M) *(bf16x8 *)ring_elem<bf16>(a, m, c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
   }
 }
 
@@ -503,9 +508,7 @@ __global__ __launch_bounds__(256) void k_cache_write_f32(CacheWriteArgs a) {
   __syncthreads();
   finish_rows<float>(tile, N, 1, m, a);
   __syncthreads();
-  float *cache = (float *)a.cache;
-  const int64_t row = ring_row(a, m);
-  for (int j = tid; j < N; j += 256) cache[row * N + j] = tile[j];
+  for (int j = tid; j < N; j += 256) *ring_elem<float>(a, m, j) = tile[j];
 }
 
 }  // namespace

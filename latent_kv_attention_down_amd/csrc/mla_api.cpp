@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -48,7 +49,9 @@ struct Dims {
   int64_t first_local;  // first local frame attended
   int64_t nk;           // attended keys: (n_sink + n_valid) * tpf
   bool at_read;         // keys rotated on window assembly
-  int64_t start0;       // rotate-at-write: the window as (up to) two ring ranges,
+  bool gathered;        // the window is gathered into the workspace (read-time
+                        // rotation, or a ring not in the interleaved layout)
+  int64_t start0;       // keys read in place: the window as (up to) two ring ranges,
   int64_t len0;         // [start0, start0 + len0) then [0, nk - len0)
   int64_t t0_q;         // temporal coordinate of the chunk's first frame for queries
   int64_t nblk;         // chunk-causal blocks (1: no mask)
@@ -58,7 +61,9 @@ struct Dims {
   size_t esz;
 };
 
-Dims dims(const mla_config &c, const mla_chunk &k) {
+// in_place: the ring is in the interleaved layout, so the attention kernels can
+// read it where it is (see mla_cache).
+Dims dims(const mla_config &c, const mla_chunk &k, bool in_place = true) {
   Dims d;
   d.tpf = (int64_t)c.grid_h * c.grid_w;
   d.T_q = (int64_t)k.chunk_frames * d.tpf;
@@ -72,18 +77,19 @@ Dims dims(const mla_config &c, const mla_chunk &k) {
   d.first_local = last - k.n_valid_frames + 1;
   d.nk = (d.n_sink + k.n_valid_frames) * d.tpf;
   d.at_read = c.rope_mode == MLA_ROPE_AT_READ;
-  if (d.at_read) {
-    // the assembled window is one contiguous range in context order; frame i of
-    // the context has temporal coordinate i, and the chunk's frames are consecutive
+  d.gathered = d.at_read || !in_place;
+  // queries: frame i of the read-time context has temporal coordinate i (the
+  // chunk's frames are consecutive); otherwise the absolute frame index (S == 0)
+  d.t0_q = !d.at_read ? k.t0 : (k.t0 < S ? k.t0 : d.n_sink + (k.t0 - d.first_local));
+  if (d.gathered) {
+    // the gathered window is one contiguous range in context order
     d.start0 = 0;
     d.len0 = d.nk;
-    d.t0_q = k.t0 < S ? k.t0 : d.n_sink + (k.t0 - d.first_local);
   } else {  // S == 0
     const int64_t slot0 = d.first_local % c.window_frames;
     const int64_t run = std::min<int64_t>(k.n_valid_frames, c.window_frames - slot0);
     d.start0 = slot0 * d.tpf;
     d.len0 = run * d.tpf;
-    d.t0_q = k.t0;
   }
   // the chunk's frames are the last C frames of the context (sinks included when
   // the chunk starts inside them)
@@ -102,6 +108,13 @@ Dims dims(const mla_config &c, const mla_chunk &k) {
   return d;
 }
 
+// An explicit frequency table is given when any of the d_rope / 2 entries is set.
+bool explicit_freq(const mla_config &c) {
+  for (int p = 0; p < c.d_rope / 2 && p < 64; ++p)
+    if (c.rope_freq[p] != 0.f) return true;
+  return false;
+}
+
 int validate_config(const mla_config *c) {
   if (!c) return fail(MLA_ERR_INVALID_ARG, "cfg is NULL");
   if (c->d_model <= 0 || c->n_heads <= 0 || c->d_head <= 0 || c->d_nope <= 0 || c->d_rope <= 0 ||
@@ -115,7 +128,9 @@ int validate_config(const mla_config *c) {
     if (c->rope_pairs[a] < 0) return fail(MLA_ERR_INVALID_ARG, "negative rope_pairs");
   if (c->rope_pairs[0] + c->rope_pairs[1] + c->rope_pairs[2] != c->d_rope / 2)
     return fail(MLA_ERR_INVALID_ARG, "rope_pairs must sum to d_rope / 2");
-  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta))
+  for (int p = 0; p < c->d_rope / 2; ++p)
+    if (!std::isfinite(c->rope_freq[p])) return fail(MLA_ERR_INVALID_ARG, "rope_freq must be finite");
+  if (!explicit_freq(*c) && (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)))
     return fail(MLA_ERR_INVALID_ARG, "rope_theta must be positive and finite");
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
     return fail(MLA_ERR_INVALID_ARG, "rms_eps must be >= 0 and finite");
@@ -213,16 +228,19 @@ int validate_weights(const mla_config &c, const mla_weights *w, bool write, bool
 // RoPE table: pair k of axis a turns by theta^(-2k / D_a) per unit position with
 // D_y = D_x = 2 * floor(d_head / 6) and D_t = d_head - 2 * D_y; the pairs of each
 // axis take its highest-frequency bands (k = 0, 1, ...).
+// An explicit rope_freq table replaces the derived bands entry for entry.
 mla::RopeTable rope_table(const mla_config &c) {
   mla::RopeTable t;
   std::memset(&t, 0, sizeof(t));
   const int d_sp = 2 * (c.d_head / 6);
   const int width[3] = {c.d_head - 2 * d_sp, d_sp, d_sp};
+  const bool given = explicit_freq(c);
   int p = 0;
   for (int a = 0; a < 3; ++a)
     for (int k = 0; k < c.rope_pairs[a]; ++k, ++p) {
       t.axis[p] = a;
-      t.omega[p] = (float)std::pow((double)c.rope_theta, -2.0 * k / (double)width[a]);
+      t.omega[p] = given ? c.rope_freq[p]
+                         : (float)std::pow((double)c.rope_theta, -2.0 * k / (double)width[a]);
     }
   t.n_pairs = p;
   return t;
@@ -247,7 +265,7 @@ mla::AttnArgs attn_shape(const mla_config &c, const mla_chunk &k, const Dims &d)
   a.R = (int)d.R;
   a.DC = c.d_c;
   a.DR = c.d_rope;
-  a.cache_rows = d.at_read ? d.nk : d.ring;
+  a.cache_rows = d.gathered ? d.nk : d.ring;
   a.nk = (int)d.nk;
   a.start0 = (int)d.start0;
   a.len0 = (int)d.len0;
@@ -294,8 +312,10 @@ Workspace carve(const mla_config &c, const mla_chunk &k) {
   w.part = take(part);
   w.flags = take(flags);
   w.out_heads = take((size_t)d.M * c.n_heads * c.d_head * d.esz);
-  // read-time rotation: the attended frames gathered in context order, rotated
-  w.win = take(d.at_read ? (size_t)k.batch * d.nk * d.DK * d.esz : 0);
+  // the attended frames gathered in context order (read-time rotation, or a ring
+  // that is not in the interleaved layout); the workspace size does not depend on
+  // the ring's layout, so the room is always there
+  w.win = take((size_t)k.batch * d.nk * d.DK * d.esz);
   w.total = off;
   return w;
 }
@@ -310,15 +330,68 @@ int hip_fail(hipError_t e, const char *stage) {
     if (e_ != hipSuccess) return hip_fail(e_, stage); \
   } while (0)
 
+// The ring parts of a validated cache descriptor.
+mla::RingParts ring_parts(const mla_cache &r) {
+  mla::RingParts p;
+  p.c_kv = r.c_kv;
+  p.k_r = r.k_r;
+  p.c_row = r.c_kv_row_stride;
+  p.r_row = r.k_r_row_stride;
+  p.c_batch = r.c_kv_batch_stride;
+  p.r_batch = r.k_r_batch_stride;
+  return p;
+}
+
+// Checks of a cache descriptor (the rules stated with mla_cache in mla.h).
+int validate_cache(const mla_config &c, int32_t batch, const mla_cache *r) {
+  if (!r) return fail(MLA_ERR_INVALID_ARG, "cache is NULL");
+  if (!r->c_kv || !r->k_r) return fail(MLA_ERR_INVALID_ARG, "cache parts c_kv and k_r must be set");
+  if (r->c_kv == r->k_r) return fail(MLA_ERR_INVALID_ARG, "cache parts c_kv and k_r coincide");
+  if (!aligned16(r->c_kv) || !aligned16(r->k_r))
+    return fail(MLA_ERR_ALIGNMENT, "cache parts must be 16-byte aligned");
+  const int64_t esz = c.dtype == MLA_BF16 ? 2 : 4, per16 = 16 / esz;
+  if (r->c_kv_row_stride < c.d_c || r->k_r_row_stride < c.d_rope)
+    return fail(MLA_ERR_INVALID_ARG, "cache row strides must cover d_c and d_rope elements");
+  if (r->c_kv_row_stride % per16 || r->k_r_row_stride % per16 || r->c_kv_batch_stride % per16 ||
+      r->k_r_batch_stride % per16)
+    return fail(MLA_ERR_ALIGNMENT, "cache strides must be multiples of 16 bytes");
+  const int64_t rows = ((int64_t)c.sink_frames + c.window_frames) * c.grid_h * c.grid_w;
+  if (batch > 1 && (r->c_kv_batch_stride < rows * r->c_kv_row_stride ||
+                    r->k_r_batch_stride < rows * r->k_r_row_stride))
+    return fail(MLA_ERR_INVALID_ARG, "cache batch strides must hold a whole ring per request");
+  if (r->c_kv_batch_stride < 0 || r->k_r_batch_stride < 0)
+    return fail(MLA_ERR_INVALID_ARG, "cache batch strides must be >= 0");
+  return MLA_OK;
+}
+
+// The interleaved layout: rows of d_c + d_rope elements, k_r right after c_kv,
+// requests one ring after another.  The attention kernels read it in place.
+bool cache_in_place(const mla_config &c, int32_t batch, const mla_cache &r) {
+  const int64_t dk = (int64_t)c.d_c + c.d_rope, esz = c.dtype == MLA_BF16 ? 2 : 4;
+  const int64_t rows = ((int64_t)c.sink_frames + c.window_frames) * c.grid_h * c.grid_w;
+  if ((const unsigned char *)r.k_r != (const unsigned char *)r.c_kv + c.d_c * esz) return false;
+  if (r.c_kv_row_stride != dk || r.k_r_row_stride != dk) return false;
+  if (batch > 1 && (r.c_kv_batch_stride != rows * dk || r.k_r_batch_stride != rows * dk)) return false;
+  return true;
+}
+
+// MLA_FAULT_INJECT=launch: refuse every launch before it reaches the HIP runtime.
+int launch_gate() {
+  const char *v = std::getenv("MLA_FAULT_INJECT");
+  if (v && std::strcmp(v, "launch") == 0)
+    return fail(MLA_ERR_HIP, "MLA_FAULT_INJECT=launch: launch refused before reaching the HIP runtime");
+  return MLA_OK;
+}
+
 int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
-                    void *cache, hipStream_t st) {
+                    const mla_cache &cache, hipStream_t st) {
   const Dims d = dims(c, k);
   mla::CacheWriteArgs a;
   a.x = x;
   a.w_kv = w.w_kv_down;
   a.w_kr = w.w_kr;
   a.g_kv = w.g_kv;
-  a.cache = cache;
+  a.ring = ring_parts(cache);
   a.M = (int)d.M;
   a.T_q = (int)d.T_q;
   a.d = c.d_model;
@@ -330,7 +403,6 @@ int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &
   a.S = c.sink_frames;
   a.rotate = d.at_read ? 0 : 1;
   a.t0 = k.t0;
-  a.cache_batch_rows = d.ring;
   a.eps = c.rms_eps;
   a.rope = rope_table(c);
   if (c.dtype == MLA_BF16)
@@ -340,12 +412,42 @@ int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &
   return MLA_OK;
 }
 
-// Latent attention over `keys`: the ring itself (rotate-at-write), or the window
-// assembled in context order in the workspace (read-time rotation).
-int run_latent_attention(const mla_config &c, const mla_chunk &k, const void *q_lat,
+// The attended keys: the ring itself when it is in the interleaved layout and keys
+// were rotated at write; otherwise the attended frames gathered in context order
+// into the workspace (rotated at window-local positions under read-time rotation,
+// §3.2 Eq. 5, App. D.4-D.5; copied as stored for another layout).
+int attended_keys(const mla_config &c, const mla_chunk &k, const Dims &d, const mla_cache &cache,
+                  unsigned char *ws, const void **keys, hipStream_t st) {
+  if (!d.gathered) {
+    *keys = cache.c_kv;
+    return MLA_OK;
+  }
+  const Workspace L = carve(c, k);
+  mla::AssembleArgs wa;
+  wa.ring = ring_parts(cache);
+  wa.win = ws + L.win;
+  wa.B = k.batch;
+  wa.tpf = (int)d.tpf;
+  wa.grid_w = c.grid_w;
+  wa.d_c = c.d_c;
+  wa.d_rope = c.d_rope;
+  wa.nk = d.nk;
+  wa.S = c.sink_frames;
+  wa.W = c.window_frames;
+  wa.n_sink = (int)d.n_sink;
+  wa.first_local = d.first_local;
+  wa.rotate = d.at_read ? 1 : 0;
+  wa.rope = rope_table(c);
+  MLA_HIP(mla::assemble_window(wa, c.dtype == MLA_BF16, st), "window assembly");
+  *keys = ws + L.win;
+  return MLA_OK;
+}
+
+// Latent attention over `keys`: the ring itself, or the window gathered in context
+// order in the workspace.
+int run_latent_attention(const mla_config &c, const mla_chunk &k, const Dims &d, const void *q_lat,
                          const void *keys, void *o_lat, unsigned char *ws, bool flags_zeroed,
                          hipStream_t st) {
-  const Dims d = dims(c, k);
   const Workspace L = carve(c, k);
   mla::AttnArgs a = attn_shape(c, k, d);
   a.q = q_lat;
@@ -400,9 +502,9 @@ int run_gemm(const mla_config &c, const mla::GemmArgs &g, bool out_f32, hipStrea
 // Query preparation, latent attention and, when out_heads is given, the per-head
 // value up-projection.
 int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chunk &k,
-                        const void *x, const void *cache, void *out_heads, unsigned char *ws,
+                        const void *x, const mla_cache &cache, void *out_heads, unsigned char *ws,
                         hipStream_t st) {
-  const Dims d = dims(c, k);
+  const Dims d = dims(c, k, cache_in_place(c, k.batch, cache));
   const Workspace L = carve(c, k);
   const bool bf = c.dtype == MLA_BF16;
   const int nh = c.n_heads;
@@ -458,30 +560,10 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
   rq.in_place = w.w_qlat != nullptr;
   if (rq.in_place) rq.q_r = nullptr;
   MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
-  // read-time rotation: gather the sink and local frames in context order and
-  // rotate k^R at window-local positions (§3.2 Eq. 5, App. D.4-D.5)
-  const void *keys = cache;
-  if (d.at_read) {
-    mla::AssembleArgs wa;
-    wa.cache = cache;
-    wa.win = ws + L.win;
-    wa.B = k.batch;
-    wa.tpf = (int)d.tpf;
-    wa.grid_w = c.grid_w;
-    wa.d_c = c.d_c;
-    wa.d_rope = c.d_rope;
-    wa.ring = d.ring;
-    wa.nk = d.nk;
-    wa.S = c.sink_frames;
-    wa.W = c.window_frames;
-    wa.n_sink = (int)d.n_sink;
-    wa.first_local = d.first_local;
-    wa.rope = rope_table(c);
-    MLA_HIP(mla::assemble_window(wa, bf, st), "window assembly");
-    keys = ws + L.win;
-  }
+  const void *keys = nullptr;
+  MLA_TRY(attended_keys(c, k, d, cache, ws, &keys, st));
   // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16)
-  MLA_TRY(run_latent_attention(c, k, q_lat, keys, o_lat, ws, true, st));
+  MLA_TRY(run_latent_attention(c, k, d, q_lat, keys, o_lat, ws, true, st));
   if (!out_heads) return MLA_OK;  // O_lat stays in the workspace
   // o_h = W^V_up,h O_lat,h  (Eq. 2)
   MLA_TRY(run_gemm(c, gemm(o_lat, (int64_t)nh * c.d_c, c.d_c, w.w_v_up, c.d_c,
@@ -520,49 +602,70 @@ size_t mla_cache_bytes(const mla_config *cfg, int32_t batch) {
          cfg->grid_w * (size_t)(cfg->d_c + cfg->d_rope) * esz;
 }
 
+int mla_cache_interleaved(const mla_config *cfg, int32_t batch, void *base, mla_cache *cache) {
+  g_last_error.clear();
+  MLA_TRY(validate_config(cfg));
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1");
+  if (!base || !cache) return fail(MLA_ERR_INVALID_ARG, "base or cache is NULL");
+  if (!aligned16(base)) return fail(MLA_ERR_ALIGNMENT, "base must be 16-byte aligned");
+  const int64_t dk = (int64_t)cfg->d_c + cfg->d_rope, esz = cfg->dtype == MLA_BF16 ? 2 : 4;
+  const int64_t rows = ((int64_t)cfg->sink_frames + cfg->window_frames) * cfg->grid_h * cfg->grid_w;
+  cache->c_kv = base;
+  cache->k_r = (unsigned char *)base + cfg->d_c * esz;
+  cache->c_kv_row_stride = cache->k_r_row_stride = dk;
+  cache->c_kv_batch_stride = cache->k_r_batch_stride = rows * dk;
+  return MLA_OK;
+}
+
 int mla_cache_write(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
-                    const void *x, void *cache, void *stream) {
+                    const void *x, const mla_cache *cache, void *stream) {
   g_last_error.clear();
   MLA_TRY(validate_config(cfg));
   MLA_TRY(validate_chunk_write(cfg, chunk));
   MLA_TRY(validate_weights(*cfg, w, true, false, false, false));
-  if (!x || !cache) return fail(MLA_ERR_INVALID_ARG, "x or cache is NULL");
-  if (!aligned16(x) || !aligned16(cache)) return fail(MLA_ERR_ALIGNMENT, "x and cache must be 16-byte aligned");
-  return run_cache_write(*cfg, *w, *chunk, x, cache, (hipStream_t)stream);
+  if (!x) return fail(MLA_ERR_INVALID_ARG, "x is NULL");
+  if (!aligned16(x)) return fail(MLA_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  MLA_TRY(validate_cache(*cfg, chunk->batch, cache));
+  MLA_TRY(launch_gate());
+  return run_cache_write(*cfg, *w, *chunk, x, *cache, (hipStream_t)stream);
 }
 
 int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
-                        const void *x, const void *cache, void *out_heads, void *workspace,
+                        const void *x, const mla_cache *cache, void *out_heads, void *workspace,
                         size_t ws_bytes, void *stream) {
   g_last_error.clear();
   MLA_TRY(validate(cfg, chunk));
   MLA_TRY(validate_weights(*cfg, w, false, true, true, false));
-  if (!x || !cache || !out_heads) return fail(MLA_ERR_INVALID_ARG, "x, cache or out_heads is NULL");
-  if (!aligned16(x) || !aligned16(cache) || !aligned16(out_heads))
-    return fail(MLA_ERR_ALIGNMENT, "x, cache and out_heads must be 16-byte aligned");
+  if (!x || !out_heads) return fail(MLA_ERR_INVALID_ARG, "x or out_heads is NULL");
+  if (!aligned16(x) || !aligned16(out_heads))
+    return fail(MLA_ERR_ALIGNMENT, "x and out_heads must be 16-byte aligned");
+  MLA_TRY(validate_cache(*cfg, chunk->batch, cache));
   MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
-  return run_chunk_attention(*cfg, *w, *chunk, x, cache, out_heads, (unsigned char *)workspace,
+  MLA_TRY(launch_gate());
+  return run_chunk_attention(*cfg, *w, *chunk, x, *cache, out_heads, (unsigned char *)workspace,
                              (hipStream_t)stream);
 }
 
 int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk, const void *x,
-             void *cache, void *y, void *workspace, size_t ws_bytes, void *stream) {
+             const mla_cache *cache, void *y, void *workspace, size_t ws_bytes, void *stream) {
   g_last_error.clear();
   MLA_TRY(validate(cfg, chunk));
   MLA_TRY(validate_weights(*cfg, w, true, true, false, true));
-  if (!x || !cache || !y) return fail(MLA_ERR_INVALID_ARG, "x, cache or y is NULL");
-  if (!aligned16(x) || !aligned16(cache) || !aligned16(y))
-    return fail(MLA_ERR_ALIGNMENT, "x, cache and y must be 16-byte aligned");
+  if (!x || !y) return fail(MLA_ERR_INVALID_ARG, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y))
+    return fail(MLA_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
+  MLA_TRY(validate_cache(*cfg, chunk->batch, cache));
   MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
+  MLA_TRY(launch_gate());
   const mla_config &c = *cfg;
   const mla_chunk &k = *chunk;
   hipStream_t st = (hipStream_t)stream;
   unsigned char *ws = (unsigned char *)workspace;
   const Workspace L = carve(c, k);
   const Dims d = dims(c, k);
-  MLA_TRY(run_cache_write(c, *w, k, x, cache, st));
+  MLA_TRY(run_cache_write(c, *w, k, x, *cache, st));
   if (w->w_b) {
-    MLA_TRY(run_chunk_attention(c, *w, k, x, cache, nullptr, ws, st));
+    MLA_TRY(run_chunk_attention(c, *w, k, x, *cache, nullptr, ws, st));
     // y = sum_h B_h O_lat,h  (App. E Eq. 10-11): row (token) of O_lat is n_h * d_c wide
     const int64_t kb = (int64_t)c.n_heads * c.d_c;
     MLA_TRY(run_gemm(c, gemm(ws + L.o_lat, kb, 0, w->w_b, kb, 0, y, c.d_model, 0, d.M, c.d_model,
@@ -570,7 +673,7 @@ int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk
                      false, st, "value-absorbed output projection"));
     return MLA_OK;
   }
-  MLA_TRY(run_chunk_attention(c, *w, k, x, cache, ws + L.out_heads, ws, st));
+  MLA_TRY(run_chunk_attention(c, *w, k, x, *cache, ws + L.out_heads, ws, st));
   // y = W_O out  (§3.3)
   MLA_TRY(run_gemm(c, gemm(ws + L.out_heads, (int64_t)c.n_heads * c.d_head, 0, w->w_o,
                            (int64_t)c.n_heads * c.d_head, 0, y, c.d_model, 0, d.M, c.d_model,
@@ -588,6 +691,7 @@ int mla_query_absorbed_weights(const mla_config *cfg, const mla_weights *w, void
   if (!w_qlat) return fail(MLA_ERR_INVALID_ARG, "w_qlat is NULL");
   if (!aligned16(w->w_k_up) || !aligned16(w->w_q_up) || !aligned16(w->w_qr) || !aligned16(w_qlat))
     return fail(MLA_ERR_ALIGNMENT, "w_k_up, w_q_up, w_qr and w_qlat must be 16-byte aligned");
+  MLA_TRY(launch_gate());
   MLA_HIP(mla::absorb_query(w->w_k_up, w->w_q_up, w->w_qr, w_qlat, cfg->n_heads, cfg->d_nope,
                             cfg->d_c, cfg->d_rope, cfg->d_q, cfg->dtype == MLA_BF16,
                             (hipStream_t)stream),
@@ -603,6 +707,7 @@ int mla_value_absorbed_weights(const mla_config *cfg, const mla_weights *w, void
   if (!w_b) return fail(MLA_ERR_INVALID_ARG, "w_b is NULL");
   if (!aligned16(w->w_v_up) || !aligned16(w->w_o) || !aligned16(w_b))
     return fail(MLA_ERR_ALIGNMENT, "w_v_up, w_o and w_b must be 16-byte aligned");
+  MLA_TRY(launch_gate());
   MLA_HIP(mla::absorb_value(w->w_o, w->w_v_up, w_b, cfg->d_model, cfg->n_heads, cfg->d_head,
                             cfg->d_c, cfg->dtype == MLA_BF16, (hipStream_t)stream),
           "value absorption");
@@ -610,19 +715,25 @@ int mla_value_absorbed_weights(const mla_config *cfg, const mla_weights *w, void
 }
 
 int mla_latent_attention(const mla_config *cfg, const mla_chunk *chunk, const void *q_lat,
-                         const void *cache, void *o_lat, void *workspace, size_t ws_bytes,
+                         const mla_cache *cache, void *o_lat, void *workspace, size_t ws_bytes,
                          void *stream) {
   g_last_error.clear();
   MLA_TRY(validate(cfg, chunk));
   if (cfg->rope_mode != MLA_ROPE_AT_WRITE || cfg->sink_frames != 0)
     return fail(MLA_ERR_UNSUPPORTED, "mla_latent_attention attends the cache as stored: "
                                      "needs MLA_ROPE_AT_WRITE and no sink");
-  if (!q_lat || !cache || !o_lat) return fail(MLA_ERR_INVALID_ARG, "q_lat, cache or o_lat is NULL");
-  if (!aligned16(q_lat) || !aligned16(cache) || !aligned16(o_lat))
-    return fail(MLA_ERR_ALIGNMENT, "q_lat, cache and o_lat must be 16-byte aligned");
+  if (!q_lat || !o_lat) return fail(MLA_ERR_INVALID_ARG, "q_lat or o_lat is NULL");
+  if (!aligned16(q_lat) || !aligned16(o_lat))
+    return fail(MLA_ERR_ALIGNMENT, "q_lat and o_lat must be 16-byte aligned");
+  MLA_TRY(validate_cache(*cfg, chunk->batch, cache));
   MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
-  return run_latent_attention(*cfg, *chunk, q_lat, cache, o_lat, (unsigned char *)workspace,
-                              false, (hipStream_t)stream);
+  MLA_TRY(launch_gate());
+  const Dims d = dims(*cfg, *chunk, cache_in_place(*cfg, chunk->batch, *cache));
+  unsigned char *ws = (unsigned char *)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  const void *keys = nullptr;
+  MLA_TRY(attended_keys(*cfg, *chunk, d, *cache, ws, &keys, st));
+  return run_latent_attention(*cfg, *chunk, d, q_lat, keys, o_lat, ws, false, st);
 }
 
 void mla_set_timing_events(void *ev_start, void *ev_stop) {

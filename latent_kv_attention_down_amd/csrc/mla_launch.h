@@ -22,17 +22,25 @@ struct GemmArgs {
 hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st);
 hipError_t gemm_f32_nt(const GemmArgs &g, hipStream_t st);
 
+// The ring of one layer in two parts: element i of row r of request b is at
+// c_kv + b * c_batch + r * c_row + i (i < d_c) and k_r + b * r_batch + r * r_row + i
+// (i < d_rope), in elements.  The interleaved layout has k_r = c_kv + d_c and both
+// row strides d_c + d_rope.
+struct RingParts {
+  void *c_kv, *k_r;
+  int64_t c_row, r_row, c_batch, r_batch;
+};
+
 // Fused cache write: [W_kv_down; W_kr] x -> RMSNorm(latent) * g, RoPE(k^R) -> ring rows.
 struct CacheWriteArgs {
   const void *x, *w_kv, *w_kr, *g_kv;
-  void *cache;
+  RingParts ring;
   int M;          // B * tokens in the chunk
   int T_q;        // tokens in the chunk per request
   int d, d_c, d_rope, tpf, grid_w, W;
   int S;                     // sink frames: frame f < S in slot f, else S + (f - S) mod W
   int rotate;                // 1: rotate k^R at the absolute position; 0: store it as is
   int64_t t0;
-  int64_t cache_batch_rows;  // (S + W) * tpf
   float eps;
   RopeTable rope;
 };
@@ -57,16 +65,18 @@ struct RopeQArgs {
 };
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st);
 
-// Window assembly for read-time rotation: context frame i (the n_sink sink frames,
-// then frames first_local, first_local+1, ...) is copied from its ring slot to rows
-// i*tpf .. of `win`, with the d_rope positional columns rotated at (i, y, x).
+// Window assembly: context frame i (the n_sink sink frames, then frames
+// first_local, first_local+1, ...) is copied from its ring slot to rows i*tpf .. of
+// `win` in the interleaved layout; with `rotate` the d_rope positional columns are
+// rotated at (i, y, x) on the way (read-time rotation), else copied as stored.
 struct AssembleArgs {
-  const void *cache;  // (B, ring, d_c + d_rope)
+  RingParts ring;     // read only
   void *win;          // (B, nk, d_c + d_rope)
   int B, tpf, grid_w, d_c, d_rope;
-  int64_t ring, nk;
+  int64_t nk;
   int S, W, n_sink;
   int64_t first_local;
+  int rotate;
   RopeTable rope;
 };
 hipError_t assemble_window(const AssembleArgs &a, bool bf16, hipStream_t st);

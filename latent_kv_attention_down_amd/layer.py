@@ -42,7 +42,14 @@ class WorkspacePool:
 
 
 class DeviceLayer:
-    def __init__(self, shape, stored_weights, batch=1, device="cuda", pool=None):
+    """One layer's weights and ring cache on the device.  cache_layout picks how the
+    ring is held: "interleaved" (one tensor, rows [c^KV | k], read in place by the
+    attention kernels), "split" (the two tensors c^KV and k^R) or "split-padded"
+    (the two tensors inside larger allocations, so rows and requests have strides
+    of their own); the library is handed the matching mla_cache descriptor."""
+
+    def __init__(self, shape, stored_weights, batch=1, device="cuda", pool=None,
+                 cache_layout="interleaved"):
         self.shape = shape
         self.dtype = shape.dtype
         self.tdtype = torch.bfloat16 if self.dtype == "bf16" else torch.float32
@@ -54,9 +61,27 @@ class DeviceLayer:
         self.batch = batch
         tpf = shape.grid_h * shape.grid_w
         frames = getattr(shape, "sink_frames", 0) + shape.window_frames
-        self.cache = torch.zeros((batch, frames * tpf, shape.d_c + shape.d_rope),
-                                 dtype=self.tdtype, device=device)
-        assert self.cache.numel() * self.cache.element_size() == _lib.cache_bytes(self.cfg, batch)
+        rows = frames * tpf
+        self.cache_layout = cache_layout
+        if cache_layout == "interleaved":
+            self.cache = torch.zeros((batch, rows, shape.d_c + shape.d_rope),
+                                     dtype=self.tdtype, device=device)
+            assert self.cache.numel() * self.cache.element_size() == _lib.cache_bytes(self.cfg,
+                                                                                     batch)
+            self.cache_desc = _lib.interleaved_cache(self.cfg, batch, self.cache)
+        elif cache_layout in ("split", "split-padded"):
+            pad = 8 if cache_layout == "split-padded" else 0
+            cbuf = torch.zeros((batch, rows + pad, shape.d_c + pad), dtype=self.tdtype,
+                               device=device)
+            kbuf = torch.zeros((batch, rows + 2 * pad, shape.d_rope + 2 * pad), dtype=self.tdtype,
+                               device=device)
+            self._bufs = (cbuf, kbuf)
+            self.c_kv = cbuf[:, :rows, :shape.d_c]
+            self.k_r = kbuf[:, :rows, :shape.d_rope]
+            self.cache = None
+            self.cache_desc = _lib.split_cache(self.c_kv, self.k_r)
+        else:
+            raise ValueError(f"unknown cache layout {cache_layout!r}")
         self.pool = pool if pool is not None else WorkspacePool(device)
 
     def absorb_value(self):
@@ -80,6 +105,13 @@ class DeviceLayer:
         self.weights = _lib.make_weights(self.tensors)
         return w_qlat
 
+    def ring(self):
+        """The ring as one (B, rows, d_c + d_rope) device tensor (a copy for the
+        split layouts)."""
+        if self.cache is not None:
+            return self.cache
+        return torch.cat([self.c_kv, self.k_r], dim=-1)
+
     def chunk(self, chunk_frames, t0, n_valid_frames, causal_frames=0):
         return _lib.make_chunk(self.batch, chunk_frames, t0, n_valid_frames, causal_frames)
 
@@ -98,23 +130,23 @@ class DeviceLayer:
                            device=self.device)
 
     def cache_write(self, chunk, x):
-        _lib.cache_write(self.cfg, self.weights, chunk, x, self.cache)
+        _lib.cache_write(self.cfg, self.weights, chunk, x, self.cache_desc)
 
     def chunk_attention(self, chunk, x):
         s = self.shape
         out = self.new_out(chunk, s.n_heads * s.d_head)
-        _lib.chunk_attention(self.cfg, self.weights, chunk, x, self.cache, out,
+        _lib.chunk_attention(self.cfg, self.weights, chunk, x, self.cache_desc, out,
                              self.workspace(chunk))
         return out
 
     def step(self, chunk, x):
         y = self.new_out(chunk, self.shape.d_model)
-        _lib.step(self.cfg, self.weights, chunk, x, self.cache, y, self.workspace(chunk))
+        _lib.step(self.cfg, self.weights, chunk, x, self.cache_desc, y, self.workspace(chunk))
         return y
 
     def latent_attention(self, chunk, q_lat):
         s = self.shape
         o = torch.empty((q_lat.shape[0], q_lat.shape[1], s.d_c), dtype=self.tdtype,
                         device=self.device)
-        _lib.latent_attention(self.cfg, chunk, q_lat, self.cache, o, self.workspace(chunk))
+        _lib.latent_attention(self.cfg, chunk, q_lat, self.cache_desc, o, self.workspace(chunk))
         return o

@@ -56,13 +56,13 @@ class Run:
     """A layer on the GPU plus the exact inputs the oracle uses."""
 
     def __init__(self, shape, seed=0, random_gains=False, scale=None, batch=1, layer=0,
-                 pool=None):
+                 pool=None, cache_layout="interleaved"):
         from latent_kv_attention_down_amd.layer import DeviceLayer
         self.s = shape
         self.batch = batch
         self.stored, self.w = W.draw_weights(shape, layer=layer, seed=seed,
                                              random_gains=random_gains, scale=scale)
-        self.L = DeviceLayer(shape, self.stored, batch=batch, pool=pool)
+        self.L = DeviceLayer(shape, self.stored, batch=batch, pool=pool, cache_layout=cache_layout)
         self.seed = seed
         self.layer = layer
         # the frames to draw and prefill are the ones the oracle says are attended

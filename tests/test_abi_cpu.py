@@ -158,15 +158,20 @@ def test_sink_window_geometry(kw, ok):
 
 
 def test_cache_and_workspace_bytes_with_sink():
-    """The ring holds S sink slots plus W local slots; read-time rotation adds the
-    assembled window (attended keys x (d_c + d_rope)) to the workspace."""
+    """The ring holds S sink slots plus W local slots; the workspace always has room
+    for the gathered window (attended keys x (d_c + d_rope)), used by read-time
+    rotation and by rings not in the interleaved layout, so its size does not depend
+    on either."""
     s = W.shape_by_name("wan1.3b-sink1-w6-t240")
     cfg = mla.make_config(s)
     assert mla.cache_bytes(cfg, 1) == (1 + 6) * 1560 * 224 * 2
     w21 = W.shape_by_name("wan1.3b-w21")
     a = mla.workspace_bytes(mla.make_config(w21), chunk_of(w21))
     b = mla.workspace_bytes(mla.make_config(w21.with_(rope_at_read=True)), chunk_of(w21))
-    assert b - a >= 21 * 1560 * 224 * 2
+    assert a == b
+    one = mla.workspace_bytes(mla.make_config(w21.with_(window_frames=22)),
+                              chunk_of(w21, t0=19, n_valid_frames=22))
+    assert one - a >= 1560 * 224 * 2  # one more attended frame: one more frame of window room
 
 
 @pytest.mark.parametrize("causal,ok", [(0, True), (1, True), (3, True), (7, True), (21, True),
@@ -201,13 +206,20 @@ def test_bf16_ring_over_2gib_is_refused():
                         chunk_of(s)) == mla.MLA_OK
 
 
+def fake_cache(cfg, batch=1, base=1 << 20):
+    """An interleaved descriptor over a made-up device address (never dereferenced:
+    the calls below fail or are refused before any launch)."""
+    return mla.interleaved_cache(cfg, batch, base)
+
+
 def test_latent_attention_refuses_read_rotation(lib):
     s = W.shape_by_name("wan1.3b-w21-read")
     cfg = mla.make_config(s)
     ch = chunk_of(s)
     n = mla.workspace_bytes(cfg, ch)
-    assert lib.mla_latent_attention(ctypes.byref(cfg), ctypes.byref(ch), 4096, 4096, 4096, 4096, n,
-                                    None) == mla.MLA_ERR_UNSUPPORTED
+    cache = fake_cache(cfg)
+    assert lib.mla_latent_attention(ctypes.byref(cfg), ctypes.byref(ch), 4096, ctypes.byref(cache),
+                                    4096, 4096, n, None) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_fp32_path_accepts_odd_dims():
@@ -227,11 +239,15 @@ def test_null_arguments_fail_before_any_launch(lib):
     # misaligned pointers are refused before any HIP call
     fake = {n: 4096 for n, _ in mla.Weights._fields_}
     wt = mla.Weights(**fake)
-    assert lib.mla_cache_write(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4097, 4096,
-                               None) == mla.MLA_ERR_ALIGNMENT
+    cache = fake_cache(cfg)
+    assert lib.mla_cache_write(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4097,
+                               ctypes.byref(cache), None) == mla.MLA_ERR_ALIGNMENT
+    # a NULL cache descriptor is refused
+    assert lib.mla_cache_write(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, None,
+                               None) == mla.MLA_ERR_INVALID_ARG
     # a workspace that is too small is refused before any HIP call
-    assert lib.mla_latent_attention(ctypes.byref(cfg), ctypes.byref(ch), 4096, 4096, 4096, 4096, 16,
-                                    None) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_latent_attention(ctypes.byref(cfg), ctypes.byref(ch), 4096, ctypes.byref(cache),
+                                    4096, 4096, 16, None) == mla.MLA_ERR_WORKSPACE
 
 
 def test_value_absorbed_weights_checks_before_launch(lib):
@@ -250,12 +266,13 @@ def test_value_absorbed_weights_checks_before_launch(lib):
     ch = chunk_of(s)
     n = mla.workspace_bytes(cfg, ch)
     # no w_b and no w_o: refused; a misaligned w_b: refused (both before any launch)
+    cache = fake_cache(cfg)
     wt = mla.Weights(**dict(fake, w_o=None, w_b=None))
-    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
-                        4096, n, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096,
+                        ctypes.byref(cache), 4096, 4096, n, None) == mla.MLA_ERR_INVALID_ARG
     wt = mla.Weights(**dict(fake, w_o=None, w_v_up=None, w_b=4100))
-    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
-                        4096, n, None) == mla.MLA_ERR_ALIGNMENT
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096,
+                        ctypes.byref(cache), 4096, 4096, n, None) == mla.MLA_ERR_ALIGNMENT
 
 
 def test_query_absorbed_weights_checks_before_launch(lib):
@@ -272,12 +289,13 @@ def test_query_absorbed_weights_checks_before_launch(lib):
                                               None) == mla.MLA_ERR_INVALID_ARG, missing
     ch = chunk_of(s)
     n = mla.workspace_bytes(cfg, ch)
+    cache = fake_cache(cfg)
     wt = mla.Weights(**dict(fake, w_qr=None, w_qlat=None))
-    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
-                        4096, n, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096,
+                        ctypes.byref(cache), 4096, 4096, n, None) == mla.MLA_ERR_INVALID_ARG
     wt = mla.Weights(**dict(fake, w_q_up=None, w_k_up=None, w_qr=None, w_qlat=4100))
-    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096, 4096, 4096,
-                        4096, n, None) == mla.MLA_ERR_ALIGNMENT
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(wt), ctypes.byref(ch), 4096,
+                        ctypes.byref(cache), 4096, 4096, n, None) == mla.MLA_ERR_ALIGNMENT
 
 
 def test_status_strings(lib):
@@ -285,3 +303,150 @@ def test_status_strings(lib):
                        (-3, "MLA_ERR_ALIGNMENT"), (-4, "MLA_ERR_WORKSPACE"), (-5, "MLA_ERR_HIP")):
         assert mla.status_string(code) == name
     assert mla.status_string(42) == "MLA_UNKNOWN_STATUS"
+
+
+# ---------------------------------------------------------------- cache descriptor
+def test_interleaved_descriptor():
+    """mla_cache_interleaved: k_r right after the d_c latent elements of the same row,
+    rows of d_c + d_rope, requests one ring apart (the layout mla_cache_bytes sizes)."""
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    c = mla.interleaved_cache(cfg, 3, 1 << 20)
+    assert c.c_kv == 1 << 20 and c.k_r == (1 << 20) + 192 * 2
+    assert c.c_kv_row_stride == c.k_r_row_stride == 224
+    assert c.c_kv_batch_stride == c.k_r_batch_stride == 21 * 1560 * 224
+    assert 3 * c.c_kv_batch_stride * 2 == mla.cache_bytes(cfg, 3)
+    f = mla.interleaved_cache(mla.make_config(s, dtype="f32"), 1, 1 << 20)
+    assert f.k_r == (1 << 20) + 192 * 4
+    lib = mla.load()
+    out = mla.Cache()
+    assert lib.mla_cache_interleaved(ctypes.byref(cfg), 1, 4100, ctypes.byref(out)) == \
+        mla.MLA_ERR_ALIGNMENT
+    assert lib.mla_cache_interleaved(ctypes.byref(cfg), 0, 4096, ctypes.byref(out)) == \
+        mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_interleaved(ctypes.byref(cfg), 1, None, ctypes.byref(out)) == \
+        mla.MLA_ERR_INVALID_ARG
+
+
+def _split(c_kv=1 << 20, k_r=1 << 24, cr=192, kr=32, cb=21 * 1560 * 192, kb=21 * 1560 * 32):
+    c = mla.Cache()
+    c.c_kv, c.k_r, c.c_kv_row_stride, c.k_r_row_stride = c_kv, k_r, cr, kr
+    c.c_kv_batch_stride, c.k_r_batch_stride = cb, kb
+    return c
+
+
+@pytest.mark.parametrize("kw,batch,code", [
+    (dict(), 2, mla.MLA_ERR_HIP),                           # valid: refused only by injection
+    (dict(cr=200, kr=40, cb=21 * 1560 * 200, kb=21 * 1560 * 40), 2, mla.MLA_ERR_HIP),
+    (dict(c_kv=None), 1, mla.MLA_ERR_INVALID_ARG),
+    (dict(k_r=None), 1, mla.MLA_ERR_INVALID_ARG),
+    (dict(k_r=1 << 20), 1, mla.MLA_ERR_INVALID_ARG),          # both parts at one address
+    (dict(c_kv=(1 << 20) + 8), 1, mla.MLA_ERR_ALIGNMENT),
+    (dict(k_r=(1 << 24) + 4), 1, mla.MLA_ERR_ALIGNMENT),
+    (dict(cr=191), 1, mla.MLA_ERR_INVALID_ARG),             # row narrower than d_c
+    (dict(kr=16), 1, mla.MLA_ERR_INVALID_ARG),              # row narrower than d_rope
+    (dict(cr=196), 1, mla.MLA_ERR_ALIGNMENT),               # 392-byte rows: not 16-byte steps
+    (dict(kb=21 * 1560 * 32 + 4), 2, mla.MLA_ERR_ALIGNMENT),
+    (dict(cb=21 * 1560 * 192 - 192), 2, mla.MLA_ERR_INVALID_ARG),  # requests would overlap
+    (dict(cb=21 * 1560 * 192 - 192), 1, mla.MLA_ERR_HIP),   # one request: no batch stride used
+])
+def test_cache_descriptor_rules(kw, batch, code, monkeypatch):
+    """Every rule of mla_cache is checked on the host before anything is launched;
+    a valid descriptor gets as far as the launch (refused here by the injection)."""
+    monkeypatch.setenv("MLA_FAULT_INJECT", "launch")
+    lib = mla.load()
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    ch = chunk_of(s, batch=batch)
+    cache = _split(**kw)
+    w = mla.Weights(**{n: 4096 for n, _ in mla.Weights._fields_})
+    st = lib.mla_cache_write(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ch), 4096,
+                             ctypes.byref(cache), None)
+    assert st == code, (kw, mla.status_string(st), mla.last_error())
+    n = mla.workspace_bytes(cfg, ch)
+    st = lib.mla_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ch), 4096,
+                      ctypes.byref(cache), 4096, 4096, n, None)
+    assert st == code, (kw, mla.status_string(st), mla.last_error())
+
+
+@pytest.mark.parametrize("freq,code", [
+    ((0.0,) * 16, mla.MLA_OK),                      # all zero: derived from theta
+    (tuple(0.1 * (i + 1) for i in range(16)), mla.MLA_OK),
+    ((0.0,) * 15 + (2.5,), mla.MLA_OK),              # one set entry makes the table explicit
+    ((float("nan"),) + (0.1,) * 15, mla.MLA_ERR_INVALID_ARG),
+    ((0.1,) * 15 + (float("inf"),), mla.MLA_ERR_INVALID_ARG),
+])
+def test_rope_freq_table_rules(freq, code):
+    s = W.shape_by_name("wan1.3b-w21").with_(rope_freq=freq)
+    assert mla.validate(mla.make_config(s), chunk_of(s)) == code, mla.last_error()
+
+
+def test_explicit_table_makes_theta_unused():
+    """rope_theta is only needed when the table is derived from it."""
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s.with_(rope_freq=(0.3,) * 16))
+    cfg.rope_theta = 0.0
+    assert mla.validate(cfg, chunk_of(s)) == mla.MLA_OK
+    cfg = mla.make_config(s)
+    cfg.rope_theta = 0.0
+    assert mla.validate(cfg, chunk_of(s)) == mla.MLA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- failure injection
+def test_fault_injection_reaches_every_launching_entry_point(monkeypatch):
+    """MLA_FAULT_INJECT=launch: every entry point that would launch returns
+    MLA_ERR_HIP after its argument checks, with the injection named in
+    mla_last_error(); invalid arguments still give their own codes first; unset,
+    the hook is inert (host-only calls are unaffected either way)."""
+    lib = mla.load()
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    ch = chunk_of(s)
+    n = mla.workspace_bytes(cfg, ch)
+    cache = fake_cache(cfg)
+    w = mla.Weights(**{k: 4096 for k, _ in mla.Weights._fields_})
+    monkeypatch.setenv("MLA_FAULT_INJECT", "launch")
+    calls = {
+        "mla_cache_write": lambda: lib.mla_cache_write(ctypes.byref(cfg), ctypes.byref(w),
+                                                       ctypes.byref(ch), 4096,
+                                                       ctypes.byref(cache), None),
+        "mla_chunk_attention": lambda: lib.mla_chunk_attention(
+            ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ch), 4096, ctypes.byref(cache), 4096,
+            4096, n, None),
+        "mla_step": lambda: lib.mla_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ch),
+                                         4096, ctypes.byref(cache), 4096, 4096, n, None),
+        "mla_latent_attention": lambda: lib.mla_latent_attention(
+            ctypes.byref(cfg), ctypes.byref(ch), 4096, ctypes.byref(cache), 4096, 4096, n, None),
+        "mla_value_absorbed_weights": lambda: lib.mla_value_absorbed_weights(
+            ctypes.byref(cfg), ctypes.byref(w), 4096, None),
+        "mla_query_absorbed_weights": lambda: lib.mla_query_absorbed_weights(
+            ctypes.byref(cfg), ctypes.byref(w), 4096, None),
+    }
+    for name, call in calls.items():
+        assert call() == mla.MLA_ERR_HIP, name
+        assert "MLA_FAULT_INJECT" in mla.last_error(), name
+    # argument errors come first
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ch), 4096,
+                        ctypes.byref(cache), 4096, 4096, 16, None) == mla.MLA_ERR_WORKSPACE
+    # host-only calls never launch, so they are unaffected
+    assert mla.validate(cfg, ch) == mla.MLA_OK and mla.workspace_bytes(cfg, ch) == n
+    assert mla.last_error() == ""
+    monkeypatch.setenv("MLA_FAULT_INJECT", "something-else")
+    assert lib.mla_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ch), 4096,
+                        ctypes.byref(cache), 4096, 4096, 16, None) == mla.MLA_ERR_WORKSPACE
+
+
+def test_binding_raises_on_injected_launch_failure(monkeypatch):
+    """The Python binding turns MLA_ERR_HIP into MLAError carrying the status and the
+    library's message."""
+    monkeypatch.setenv("MLA_FAULT_INJECT", "launch")
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    w = mla.Weights(**{k: 4096 for k, _ in mla.Weights._fields_})
+
+    class FakeTensor:
+        def data_ptr(self):
+            return 4096
+    with pytest.raises(mla.MLAError) as e:
+        mla.cache_write(cfg, w, chunk_of(s), FakeTensor(), fake_cache(cfg), stream=0)
+    assert e.value.status == mla.MLA_ERR_HIP and "MLA_FAULT_INJECT" in str(e.value)

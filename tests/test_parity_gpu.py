@@ -31,7 +31,7 @@ def full_step(run, check_cache=True, sample=None):
     y = run.L.step(ch, run.chunk_tokens())
     torch.cuda.synchronize()
     tol = TOL[run.s.dtype]
-    ring = to_host(run.L.cache)
+    ring = to_host(run.L.ring())
     y_h = to_host(y)
     for b in range(run.batch):
         ref = run.oracle(b, query_rows=sample)
@@ -84,7 +84,7 @@ def test_partial_window_leaves_other_slots_untouched():
     only the valid frames are attended."""
     run = Run(small_wan(t0=5, n_valid_frames=3))
     full_step(run)
-    ring = to_host(run.L.cache)[0]
+    ring = to_host(run.L.ring())[0]
     written = {O.ring_slot(f, 5) for f in run.window_ids}
     for slot in range(5):
         rows = ring[slot * run.tpf:(slot + 1) * run.tpf]
@@ -129,6 +129,48 @@ def test_single_token_frames_fp32():
     full_step(Run(s))
 
 
+@pytest.mark.parametrize("layout", ["split", "split-padded"])
+def test_two_tensor_cache(layout):
+    """The cache as App. D.4 writes it, two tensors c^KV (B x T x d_c) and k^R
+    (B x T x d_rope), here with their own row and request strides: the cache write
+    stores into both parts and the attention reads them through the gathered
+    window.  Ring contents and y against the oracle."""
+    full_step(Run(small_wan(t0=9), random_gains=True, cache_layout=layout))
+
+
+def test_two_tensor_cache_batch_sink_fp32():
+    """Strided two-tensor caches with two requests (batch strides), with a sink frame
+    and read-time rotation, and in fp32."""
+    full_step(Run(small_wan(t0=6), batch=2, cache_layout="split-padded"))
+    full_step(Run(small_wan(rope_at_read=True, sink_frames=1, window_frames=3, chunk_frames=2,
+                            t0=12, n_valid_frames=3), cache_layout="split-padded"))
+    full_step(Run(W.shape_by_name("tiny-f32"), random_gains=True, cache_layout="split-padded"))
+
+
+def test_two_tensor_cache_matches_interleaved_bitwise():
+    """Gathering a two-tensor ring into the workspace changes nothing but where the
+    keys come from: y is bit-identical to the interleaved ring's."""
+    ys = []
+    for layout in ("interleaved", "split-padded"):
+        run = Run(small_wan(t0=8), cache_layout=layout)
+        run.prefill()
+        y = run.L.step(run.chunk(), run.chunk_tokens())
+        torch.cuda.synchronize()
+        ys.append(y.clone())
+    assert torch.equal(ys[0], ys[1])
+
+
+@pytest.mark.parametrize("read", [False, True])
+def test_explicit_rope_frequency_table(read):
+    """An explicit per-pair frequency table (drawn at random, an input to both sides
+    like the weights), so the comparison does not rest on the derived bands."""
+    s = small_wan(t0=9, rope_at_read=read)
+    s = s.with_(rope_freq=W.draw_rope_freq(s, seed=4))
+    full_step(Run(s, random_gains=True))
+    t = W.shape_by_name("tiny-f32")
+    full_step(Run(t.with_(rope_freq=W.draw_rope_freq(t, seed=5), rope_at_read=read)))
+
+
 def test_run_to_run_bitwise_deterministic():
     run = Run(small_wan())
     run.prefill()
@@ -169,7 +211,7 @@ def sampled_full(shape, batch=1):
     y = full_step(run, check_cache=False, sample=sample_rows(shape))
     # cache: sampled ring rows of every request against the oracle's entries
     rng = np.random.default_rng(2)
-    ring = to_host(run.L.cache)
+    ring = to_host(run.L.ring())
     for b in range(batch):
         ref = run.oracle_ring(b)
         rows = rng.choice(ring.shape[1], 600, replace=False)
@@ -199,7 +241,7 @@ def test_wan13b_layer_full_tensors():
     y = run.L.step(ch, x)  # writes the chunk's frames again (same values), then attends
     torch.cuda.synchronize()
     y_h = to_host(y)[0]
-    ring = to_host(run.L.cache)[0]
+    ring = to_host(run.L.ring())[0]
     say("  device done; oracle over all 4680 query tokens ...")
     ref = run.oracle()
     assert out_h.shape == ref["out"].shape == (4680, 1536)
@@ -210,6 +252,16 @@ def test_wan13b_layer_full_tensors():
     ref_ring = run.oracle_ring()
     assert ring.shape == ref_ring.shape == (21 * 1560, 224)
     assert_cache_rows(ring, ref_ring, "bf16", "ring (all 32760 rows)")
+
+
+def test_wan13b_two_tensor_cache_sampled():
+    """Full Wan-1.3B size with the ring held as two tensors (App. D.4's c^KV and k^R):
+    sampled query tokens (all heads) and ring rows against the oracle."""
+    run = Run(W.shape_by_name("wan1.3b-w21"), cache_layout="split")
+    full_step(run, check_cache=False, sample=sample_rows(run.s))
+    ring = to_host(run.L.ring())[0]
+    rows = np.random.default_rng(2).choice(ring.shape[0], 600, replace=False)
+    assert_cache_rows(ring[rows], run.oracle_ring()[rows], "bf16", "two-tensor ring sample")
 
 
 @pytest.mark.parametrize("name,batch", [("wan1.3b-w21", 3), ("wan1.3b-sink1-w6-t240", 4)])

@@ -44,7 +44,7 @@ def test_thirty_layer_step():
         ref = run.oracle(query_rows=rows)
         y_h = to_host(y)[0]
         fro, mx = assert_close(y_h if full else y_h[rows], ref["y"], TOL["bf16"], f"layer {l} y")
-        ring = to_host(run.L.cache)[0]
+        ring = to_host(run.L.ring())[0]
         ref_ring = run.oracle_ring()
         if full:
             assert_cache_rows(ring, ref_ring, "bf16", f"layer {l} ring (all rows)")

@@ -1,8 +1,9 @@
 """GPU parity over seeded random layer and window configurations: grid sizes from one
 token per frame up, every latent width the bf16 path is built for, both RoPE
 placements, sink frames, partial windows, wrapped rings, causal blocks, batches of
-requests and both output epilogues, each checked through the C ABI against the fp64
-oracle at the usual tolerances.  Invalid draws (as the library's own validation
+requests, both output epilogues, explicit RoPE frequency tables and all three ring
+layouts, each checked through the C ABI against the fp64 oracle at the usual
+tolerances.  Invalid draws (as the library's own validation
 judges them) are redrawn, so every case is one the ABI accepts."""
 import os
 
@@ -43,7 +44,11 @@ def draw_case(seed):
         ch = mla.make_chunk(1, s.chunk_frames, s.t0, s.n_valid_frames, s.causal_frames)
         if mla.validate(mla.make_config(s), ch) != mla.MLA_OK:
             continue
-        return s, int(rng.integers(1, 3)), bool(rng.integers(2)), bool(rng.integers(2))
+        if rng.random() < 0.3:
+            s = s.with_(rope_freq=W.draw_rope_freq(s, seed=seed))
+        layout = ("interleaved", "split", "split-padded")[int(rng.integers(3))]
+        return (s, int(rng.integers(1, 3)), bool(rng.integers(2)), bool(rng.integers(2)),
+                layout)
 
 
 # MLA_RANDOM_CASES widens the sweep for a one-off longer run; 24 by default.
@@ -52,8 +57,8 @@ CASES = int(os.environ.get("MLA_RANDOM_CASES", "24"))
 
 @pytest.mark.parametrize("seed", range(CASES))
 def test_random_configuration(seed):
-    s, batch, absorbed, query = draw_case(seed)
-    run = Run(s, batch=batch, random_gains=True, seed=seed)
+    s, batch, absorbed, query, layout = draw_case(seed)
+    run = Run(s, batch=batch, random_gains=True, seed=seed, cache_layout=layout)
     if absorbed:
         run.L.absorb_value()
     if query:

@@ -62,7 +62,7 @@ def test_rollout_through_eviction():
     ch = L.chunk(2, 12, 3)
     out = L.chunk_attention(ch, L.tokens(xs[:, 12 * tpf:14 * tpf]))
     torch.cuda.synchronize()
-    ring = to_host(L.cache)[0]
+    ring = to_host(L.ring())[0]
     ref_ring = O.expected_ring(s, w, xe[0], frames)
     assert_cache_rows(ring, ref_ring, "bf16", "ring after the rollout")
     ref = O.step(s, w, {f: xe[0][f * tpf:(f + 1) * tpf] for f in frames})

@@ -247,6 +247,23 @@ int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk
              void *stream);
 
 /*
+ * mla_step without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It computes exactly what mla_step computes (the same kernels, bit for
+ * bit), using a scratch array of MLA_STATIC_SCRATCH_BYTES that the library keeps in
+ * the memory of every GPU it runs on until the process ends; it allocates nothing.
+ * A problem whose mla_workspace_bytes() exceeds that size is refused with
+ * MLA_ERR_WORKSPACE before anything is launched (one Wan-1.3B request at the
+ * 21- or 42-frame window fits).  Every call on one GPU uses that GPU's array, which
+ * keeps the last call's contents (the step clears what it needs cleared itself):
+ * calls that overlap on one GPU -- two streams, two threads -- race on it and must
+ * be serialised by the caller.  Other arguments and errors as mla_step.
+ */
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+int mla_step_static(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+                    const void *x, const mla_cache *cache, void *y, void *stream);
+
+/*
  * Value absorption into the output projection (App. E Eq. 10-11), a weight
  * preparation done once per weight set:
  *   w_b (d, n_h * d_c) cfg->dtype, written: column h*d_c + c of row n is

@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     MLA_ERR_HIP, MLA_BF16, MLA_F32, MLA_ROPE_AT_WRITE, MLA_ROPE_AT_READ, Config, Weights, Chunk,
     Cache, interleaved_cache, split_cache,
     MLAError, load, make_config, make_chunk, make_weights, validate, workspace_bytes, cache_bytes, cache_write,
-    chunk_attention, step, value_absorbed_weights, query_absorbed_weights, latent_attention,
+    chunk_attention, step, step_static, MLA_STATIC_SCRATCH_BYTES, value_absorbed_weights, query_absorbed_weights, latent_attention,
     set_timing_events, attention_grid, status_string,
     last_error, SIGNATURES, LIB_PATH,
 )

@@ -57,6 +57,8 @@ SIGNATURES = {
                                 _vp]),
     "mla_latent_attention": (ctypes.c_int, [_P(Config), _P(Chunk), _vp, _P(Cache), _vp, _vp, _sz,
                                             _vp]),
+    "mla_step_static": (ctypes.c_int, [_P(Config), _P(Weights), _P(Chunk), _vp, _P(Cache), _vp,
+                                       _vp]),
     "mla_value_absorbed_weights": (ctypes.c_int, [_P(Config), _P(Weights), _vp, _vp]),
     "mla_query_absorbed_weights": (ctypes.c_int, [_P(Config), _P(Weights), _vp, _vp]),
     "mla_set_timing_events": (None, [_vp, _vp]),
@@ -206,6 +208,15 @@ def step(cfg, weights, chunk, x, cache, y, workspace, stream=None):
                            _cache(cfg, cache), _ptr(y), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)),
            "mla_step")
+
+
+def step_static(cfg, weights, chunk, x, cache, y, stream=None):
+    _check(load().mla_step_static(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(chunk),
+                                  _ptr(x), _cache(cfg, cache), _ptr(y), _stream(stream)),
+           "mla_step_static")
+
+
+MLA_STATIC_SCRATCH_BYTES = 256 << 20
 
 
 def value_absorbed_weights(cfg, weights, w_b, stream=None):

@@ -1,13 +1,14 @@
 // Host side of the C ABI declared in include/mla.h: argument validation, ring and
 // window index arithmetic, workspace carving and the launch sequence of the MLA
 // chunk step on the caller's stream.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "mla.h"
@@ -21,6 +22,7 @@ thread_local hipEvent_t g_ev_stop = nullptr;
 
 constexpr int kMaxAttnGrid = 512;  // persistent attention workgroups, upper bound
 constexpr size_t kAlign = 256;
+constexpr size_t kStaticScratchBytes = MLA_STATIC_SCRATCH_BYTES;  // mla_step_static
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -581,6 +583,77 @@ int check_ws(const mla_config &c, const mla_chunk &k, void *ws, size_t ws_bytes)
   return MLA_OK;
 }
 
+// Checks of mla_step's arguments other than the workspace.
+int validate_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+                  const void *x, const mla_cache *cache, const void *y) {
+  MLA_TRY(validate(cfg, chunk));
+  MLA_TRY(validate_weights(*cfg, w, true, true, false, true));
+  if (!x || !y) return fail(MLA_ERR_INVALID_ARG, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y))
+    return fail(MLA_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
+  MLA_TRY(validate_cache(*cfg, chunk->batch, cache));
+  return MLA_OK;
+}
+
+// The chunk step on validated arguments: cache write, chunk attention, output
+// projection (§3.3), in `ws` laid out by carve().
+int run_step(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
+             const mla_cache &cache, void *y, unsigned char *ws, hipStream_t st) {
+  const Workspace L = carve(c, k);
+  const Dims d = dims(c, k);
+  MLA_TRY(run_cache_write(c, w, k, x, cache, st));
+  if (w.w_b) {
+    MLA_TRY(run_chunk_attention(c, w, k, x, cache, nullptr, ws, st));
+    // y = sum_h B_h O_lat,h  (App. E Eq. 10-11): row (token) of O_lat is n_h * d_c wide
+    const int64_t kb = (int64_t)c.n_heads * c.d_c;
+    MLA_TRY(run_gemm(c, gemm(ws + L.o_lat, kb, 0, w.w_b, kb, 0, y, c.d_model, 0, d.M, c.d_model,
+                             (int)kb, 1, 1.f),
+                     false, st, "value-absorbed output projection"));
+    return MLA_OK;
+  }
+  MLA_TRY(run_chunk_attention(c, w, k, x, cache, ws + L.out_heads, ws, st));
+  // y = W_O out  (§3.3)
+  MLA_TRY(run_gemm(c, gemm(ws + L.out_heads, (int64_t)c.n_heads * c.d_head, 0, w.w_o,
+                           (int64_t)c.n_heads * c.d_head, 0, y, c.d_model, 0, d.M, c.d_model,
+                           c.n_heads * c.d_head, 1, 1.f),
+                   false, st, "output projection"));
+  return MLA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- static scratch
+// mla_step_static's scratch: one array in every device's memory, held until the
+// process ends.  Host code must not use the array's name as a device address (it
+// names the host-side stand-in): static_scratch() asks the runtime for the current
+// device's copy once and keeps that address per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char *g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(unsigned char **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "static scratch: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "static scratch: device index beyond 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "static scratch: hipGetSymbolAddress");
+    if (!p || ((uintptr_t)p & (kAlign - 1)) != 0)
+      return fail(MLA_ERR_HIP, "static scratch: the runtime gave no 256-byte aligned address");
+    g_scratch_ptr[dev] = (unsigned char *)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -649,37 +722,27 @@ int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_c
 int mla_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk, const void *x,
              const mla_cache *cache, void *y, void *workspace, size_t ws_bytes, void *stream) {
   g_last_error.clear();
-  MLA_TRY(validate(cfg, chunk));
-  MLA_TRY(validate_weights(*cfg, w, true, true, false, true));
-  if (!x || !y) return fail(MLA_ERR_INVALID_ARG, "x or y is NULL");
-  if (!aligned16(x) || !aligned16(y))
-    return fail(MLA_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
-  MLA_TRY(validate_cache(*cfg, chunk->batch, cache));
+  MLA_TRY(validate_step(cfg, w, chunk, x, cache, y));
   MLA_TRY(check_ws(*cfg, *chunk, workspace, ws_bytes));
   MLA_TRY(launch_gate());
-  const mla_config &c = *cfg;
-  const mla_chunk &k = *chunk;
-  hipStream_t st = (hipStream_t)stream;
-  unsigned char *ws = (unsigned char *)workspace;
-  const Workspace L = carve(c, k);
-  const Dims d = dims(c, k);
-  MLA_TRY(run_cache_write(c, *w, k, x, *cache, st));
-  if (w->w_b) {
-    MLA_TRY(run_chunk_attention(c, *w, k, x, *cache, nullptr, ws, st));
-    // y = sum_h B_h O_lat,h  (App. E Eq. 10-11): row (token) of O_lat is n_h * d_c wide
-    const int64_t kb = (int64_t)c.n_heads * c.d_c;
-    MLA_TRY(run_gemm(c, gemm(ws + L.o_lat, kb, 0, w->w_b, kb, 0, y, c.d_model, 0, d.M, c.d_model,
-                             (int)kb, 1, 1.f),
-                     false, st, "value-absorbed output projection"));
-    return MLA_OK;
-  }
-  MLA_TRY(run_chunk_attention(c, *w, k, x, *cache, ws + L.out_heads, ws, st));
-  // y = W_O out  (§3.3)
-  MLA_TRY(run_gemm(c, gemm(ws + L.out_heads, (int64_t)c.n_heads * c.d_head, 0, w->w_o,
-                           (int64_t)c.n_heads * c.d_head, 0, y, c.d_model, 0, d.M, c.d_model,
-                           c.n_heads * c.d_head, 1, 1.f),
-                   false, st, "output projection"));
-  return MLA_OK;
+  return run_step(*cfg, *w, *chunk, x, *cache, y, (unsigned char *)workspace,
+                  (hipStream_t)stream);
+}
+
+int mla_step_static(const mla_config *cfg, const mla_weights *w, const mla_chunk *chunk,
+                    const void *x, const mla_cache *cache, void *y, void *stream) {
+  g_last_error.clear();
+  MLA_TRY(validate_step(cfg, w, chunk, x, cache, y));
+  const size_t need = carve(*cfg, *chunk).total;
+  if (need > kStaticScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "mla_step_static: this problem needs " + std::to_string(need) +
+                                       " bytes of scratch; the static scratch holds " +
+                                       std::to_string(kStaticScratchBytes) +
+                                       " (use mla_step with a workspace)");
+  MLA_TRY(launch_gate());
+  unsigned char *ws = nullptr;
+  MLA_TRY(static_scratch(&ws));
+  return run_step(*cfg, *w, *chunk, x, *cache, y, ws, (hipStream_t)stream);
 }
 
 int mla_query_absorbed_weights(const mla_config *cfg, const mla_weights *w, void *w_qlat,

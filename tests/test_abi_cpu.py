@@ -450,3 +450,30 @@ def test_binding_raises_on_injected_launch_failure(monkeypatch):
     with pytest.raises(mla.MLAError) as e:
         mla.cache_write(cfg, w, chunk_of(s), FakeTensor(), fake_cache(cfg), stream=0)
     assert e.value.status == mla.MLA_ERR_HIP and "MLA_FAULT_INJECT" in str(e.value)
+
+
+def test_static_step_refuses_problems_beyond_its_scratch(monkeypatch):
+    """mla_step_static's scratch holds MLA_STATIC_SCRATCH_BYTES: a problem whose
+    workspace would be larger (three Wan-1.3B requests in one call) is refused on the
+    host with MLA_ERR_WORKSPACE and a message naming both sizes; one request fits
+    and gets as far as the launch (refused here by the injection)."""
+    monkeypatch.setenv("MLA_FAULT_INJECT", "launch")
+    lib = mla.load()
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    w = mla.Weights(**{k: 4096 for k, _ in mla.Weights._fields_})
+    one, three = chunk_of(s), chunk_of(s, batch=3)
+    assert mla.workspace_bytes(cfg, one) <= mla.MLA_STATIC_SCRATCH_BYTES
+    assert mla.workspace_bytes(cfg, three) > mla.MLA_STATIC_SCRATCH_BYTES
+    c1, c3 = fake_cache(cfg, 1), fake_cache(cfg, 3)
+    st = lib.mla_step_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(three), 4096,
+                             ctypes.byref(c3), 4096, None)
+    assert st == mla.MLA_ERR_WORKSPACE
+    assert str(mla.MLA_STATIC_SCRATCH_BYTES) in mla.last_error()
+    st = lib.mla_step_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(one), 4096,
+                             ctypes.byref(c1), 4096, None)
+    assert st == mla.MLA_ERR_HIP and "MLA_FAULT_INJECT" in mla.last_error()
+    # argument checks as mla_step's
+    assert lib.mla_step_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(one), 4097,
+                               ctypes.byref(c1), 4096, None) == mla.MLA_ERR_ALIGNMENT
+    assert lib.mla_step_static(None, None, None, None, None, None, None) == mla.MLA_ERR_INVALID_ARG

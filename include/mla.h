@@ -33,6 +33,12 @@
  *     crosses this boundary.
  *   - Two calls that write the same cache, or share a workspace, must not run
  *     concurrently.
+ *   - Safe-path hook: the bf16 attention kernel recomputes a row tile on its
+ *     slower, rescaling path when its row sums, taken against the first key tile's
+ *     maximum, exceed 2^64 (scores more than 64 above it, base 2).  With the
+ *     environment variable MLA_ATTN_OVERFLOW_LIMIT=v (a number > 0, below 2^64)
+ *     the bound is v instead, so that path can be exercised on ordinary data;
+ *     results are exact either way.
  *   - Failure injection: with the environment variable MLA_FAULT_INJECT=launch,
  *     every entry point that would launch a kernel returns MLA_ERR_HIP after
  *     its argument checks and before anything reaches the HIP runtime, with
@@ -316,6 +322,15 @@ void mla_set_timing_events(void *ev_start, void *ev_stop);
  * (one persistent workgroup per compute unit, capped by the work); host-only
  * apart from one device-attribute query. */
 int mla_attention_grid(const mla_config *cfg, const mla_chunk *chunk);
+
+/* Where the bf16 attention leaves its overflow flags in the workspace: *offset
+ * (bytes from the workspace start) and *count int32 flags, one per row tile of
+ * the fast kernel.  After a call, a nonzero flag means that row tile's scores
+ * rose more than 64 (base 2) above its first key tile's maximum, so the safe
+ * path recomputed it (exact either way).  Host-only; MLA_OK, or INVALID_ARG for
+ * an invalid cfg/chunk or NULL outputs; *count = 0 on the fp32 path. */
+int mla_overflow_flags(const mla_config *cfg, const mla_chunk *chunk, size_t *offset,
+                       int64_t *count);
 
 const char *mla_status_string(int status);
 /* Thread-local text of the last failure on this thread ("" if none). */

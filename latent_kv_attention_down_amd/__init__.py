@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     Cache, interleaved_cache, split_cache,
     MLAError, load, make_config, make_chunk, make_weights, validate, workspace_bytes, cache_bytes, cache_write,
     chunk_attention, step, step_static, MLA_STATIC_SCRATCH_BYTES, value_absorbed_weights, query_absorbed_weights, latent_attention,
-    set_timing_events, attention_grid, status_string,
+    set_timing_events, attention_grid, overflow_flags, status_string,
     last_error, SIGNATURES, LIB_PATH,
 )

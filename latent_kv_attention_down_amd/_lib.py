@@ -63,6 +63,7 @@ SIGNATURES = {
     "mla_query_absorbed_weights": (ctypes.c_int, [_P(Config), _P(Weights), _vp, _vp]),
     "mla_set_timing_events": (None, [_vp, _vp]),
     "mla_attention_grid": (ctypes.c_int, [_P(Config), _P(Chunk)]),
+    "mla_overflow_flags": (ctypes.c_int, [_P(Config), _P(Chunk), _P(_sz), _P(_i64)]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -243,6 +244,14 @@ def set_timing_events(ev_start, ev_stop):
 
 def attention_grid(cfg, chunk):
     return load().mla_attention_grid(ctypes.byref(cfg), ctypes.byref(chunk))
+
+
+def overflow_flags(cfg, chunk):
+    """(byte offset, count) of the int32 overflow flags in the workspace."""
+    off, n = _sz(), _i64()
+    _check(load().mla_overflow_flags(ctypes.byref(cfg), ctypes.byref(chunk), ctypes.byref(off),
+                                     ctypes.byref(n)), "mla_overflow_flags")
+    return off.value, n.value
 
 
 def status_string(status):

@@ -34,8 +34,9 @@
 //    workgroup sees for it and is never moved, so O is never rescaled inside the
 //    loop (a rescale would drag the AGPR-resident accumulators through VGPRs).
 //    Any row whose later scores exceed the reference by more than 64 (base 2) has
-//    its row tile flagged, and the safe kernel (reference raised lazily, O
-//    rescaled) recomputes exactly those row tiles.  Below that bound every weight
+//    its row tile flagged (a lower bound can be set to exercise this on ordinary
+//    data), and the safe kernel (reference raised lazily, O rescaled) recomputes
+//    exactly those row tiles.  Below that bound every weight
 //    is at most 2^64, far inside fp32 and bf16 range;
 //  * the fast grid is persistent: workgroup g takes the flat range
 //    [gT/G, (g+1)T/G) of T = (row tiles) x (key tiles) tile steps, so every CU gets
@@ -74,6 +75,7 @@ struct Sched {
   int G;
   int RW;
   int nblk, blk_rows, blk_rt, blk_keys, nk0;
+  float sum_limit;  // row sums above it flag the row tile (at most kFastSumLimit)
 };
 
 __host__ __device__ __forceinline__ int wg_of(const Sched &s, int64_t flat) {
@@ -910,7 +912,7 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       // above 2^64 (a score more than 64 above the reference) makes lt exceed 2^64,
       // as does inf or NaN: such a row tile is recomputed by the safe kernel.
       // Sums above 2^64 made only of smaller weights are flagged too (harmless).
-      if (!(lt <= kFastSumLimit)) flags[rt] = 1;
+      if (!(lt <= s.sum_limit)) flags[rt] = 1;
       stage_rows<FT, QT, DC>(img, O, qt, qt * 32 + l32, 1.0f / lt, g);
       const int lrow = wave * WR + qt * 32 + l32;
       if (!whole && g == 0 && row0 + lrow < t.row_end) {
@@ -1154,6 +1156,7 @@ Sched make_sched(const AttnArgs &a, int rows_per_wg, int grid) {
   s.T = (int64_t)s.B * s.Tb;
   s.G = (int)((int64_t)grid < s.T ? (int64_t)grid : s.T);
   if (s.G < 1) s.G = 1;
+  s.sum_limit = a.sum_limit > 0.f && a.sum_limit < kFastSumLimit ? a.sum_limit : kFastSumLimit;
   return s;
 }
 

@@ -377,6 +377,17 @@ bool cache_in_place(const mla_config &c, int32_t batch, const mla_cache &r) {
   return true;
 }
 
+// MLA_ATTN_OVERFLOW_LIMIT=v (a number > 0): the fast attention kernel flags row
+// tiles whose row sums exceed v instead of 2^64, so the safe path can be exercised
+// on ordinary data; unset or invalid: 2^64.
+float overflow_limit() {
+  const char *v = std::getenv("MLA_ATTN_OVERFLOW_LIMIT");
+  if (!v || !*v) return 0.f;
+  char *end = nullptr;
+  const float f = std::strtof(v, &end);
+  return (end && *end == 0 && f > 0.f && std::isfinite(f)) ? f : 0.f;
+}
+
 // MLA_FAULT_INJECT=launch: refuse every launch before it reaches the HIP runtime.
 int launch_gate() {
   const char *v = std::getenv("MLA_FAULT_INJECT");
@@ -459,6 +470,7 @@ int run_latent_attention(const mla_config &c, const mla_chunk &k, const Dims &d,
   a.flags = (int *)(ws + L.flags);
   a.flags_zeroed = flags_zeroed;
   a.grid = attn_grid_cus();
+  a.sum_limit = overflow_limit();
   if (c.dtype == MLA_BF16)
     MLA_HIP(mla::latent_attention_bf16(a, g_ev_start, g_ev_stop, st), "latent attention");
   else
@@ -817,6 +829,17 @@ int mla_attention_grid(const mla_config *cfg, const mla_chunk *chunk) {
   const int64_t t = mla::latent_attention_counts(attn_shape(*cfg, *chunk, d)).steps;
   const int64_t g = (int64_t)attn_grid_cus() * al.wgs_per_cu;
   return (int)(g < t ? g : t);
+}
+
+int mla_overflow_flags(const mla_config *cfg, const mla_chunk *chunk, size_t *offset,
+                       int64_t *count) {
+  g_last_error.clear();
+  MLA_TRY(validate(cfg, chunk));
+  if (!offset || !count) return fail(MLA_ERR_INVALID_ARG, "offset or count is NULL");
+  const Workspace L = carve(*cfg, *chunk);
+  *offset = L.flags;
+  *count = L.n_flags;
+  return MLA_OK;
 }
 
 const char *mla_status_string(int status) {

@@ -111,6 +111,9 @@ struct AttnArgs {
   // attends the first min(nk0 + (k + 1) * blk_keys, nk) keys.  No mask: nblk = 1,
   // blk_rows = R, blk_keys = nk, nk0 = 0.
   int nblk, blk_rows, blk_keys, nk0;
+  // Row sums (weights relative to the first key tile's max) above this send the
+  // row tile to the safe path: 2^64 (overflow guard), or lower to force it.
+  float sum_limit;
 };
 // Row tiles (with causal blocks, a block's last tile may be partial) and
 // (row tile, key tile) steps of the bf16 kernel for these arguments.

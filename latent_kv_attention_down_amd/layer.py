@@ -121,6 +121,13 @@ class DeviceLayer:
             raise _lib.MLAError(_lib.validate(self.cfg, chunk), "mla_workspace_bytes")
         return self.pool.get(n)
 
+    def overflow_flags(self, chunk):
+        """The attention's overflow flags left in the workspace by the last call
+        (one per row tile; nonzero: recomputed by the safe path), as a host array."""
+        off, n = _lib.overflow_flags(self.cfg, chunk)
+        ws = self.workspace(chunk)
+        return ws[off:off + 4 * n].view(torch.int32).cpu().numpy()
+
     def tokens(self, x_host):
         return to_device(x_host, self.dtype, self.device)
 

@@ -477,3 +477,16 @@ def test_static_step_refuses_problems_beyond_its_scratch(monkeypatch):
     assert lib.mla_step_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(one), 4097,
                                ctypes.byref(c1), 4096, None) == mla.MLA_ERR_ALIGNMENT
     assert lib.mla_step_static(None, None, None, None, None, None, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_overflow_flag_location():
+    """The overflow flags lie inside the workspace, one per row tile of the fast
+    kernel (256 query rows: 56160 rows at the Wan-1.3B chunk -> 220 tiles); none on
+    the fp32 path."""
+    s = W.shape_by_name("wan1.3b-w21")
+    cfg = mla.make_config(s)
+    off, n = mla.overflow_flags(cfg, chunk_of(s))
+    assert n == (4680 * 12 + 255) // 256 and off % 256 == 0
+    assert off + 4 * n <= mla.workspace_bytes(cfg, chunk_of(s))
+    t = W.shape_by_name("tiny-f32")
+    assert mla.overflow_flags(mla.make_config(t), chunk_of(t))[1] == 0

@@ -9,7 +9,7 @@ import torch
 import oracle as O
 import workload as W
 from latent_kv_attention_down_amd.layer import to_host
-from parity_helpers import TOL, Run, assert_cache_rows, assert_close, say
+from parity_helpers import TOL, Run, assert_cache_rows, assert_close, rel_errors, say
 
 pytestmark = pytest.mark.gpu
 
@@ -105,14 +105,78 @@ def test_latent_and_rope_widths(dc, dr):
 
 
 def test_sharp_softmax():
-    """W_q_down x8: logits of standard deviation ~8 nats."""
-    full_step(Run(small_wan(), scale={"w_q_down": 8.0}), check_cache=False)
+    """RMSNorm gain of c^Q x8 (the scale must come after the normalisation, which
+    would cancel one on W^Q_down): logits of standard deviation ~8 nats, still
+    inside the fast kernel's range, so no row tile is flagged."""
+    for s in (small_wan(), long_window()):
+        run = Run(s, scale={"g_q": 8.0})
+        full_step(run, check_cache=False)
+        flags = run.L.overflow_flags(run.chunk())
+        assert len(flags) > 0 and not flags.any(), flags
 
 
-def test_very_sharp_softmax_takes_the_safe_path():
-    """W_q_down x40: later scores exceed the first tile's max by far more than 2^64,
-    so the fast kernel flags the row tiles and the safe kernel recomputes them."""
-    full_step(Run(small_wan(), scale={"w_q_down": 40.0}), check_cache=False)
+def long_window(**kw):
+    """One Wan frame of queries over three frames of keys: 74 row tiles x 74 key
+    tiles, so each workgroup's piece spans about 21 key tiles (in a small problem
+    every piece is one key tile, whose own max is its reference and nothing can
+    overflow)."""
+    return W.shape_by_name("wan1.3b-w21").with_(window_frames=3, chunk_frames=1, t0=2,
+                                                 n_valid_frames=3, **kw)
+
+
+@pytest.mark.parametrize("case", ["small", "long", "batch-causal", "sink-read", "dc256"])
+def test_safe_path_recomputes_flagged_row_tiles(case, monkeypatch):
+    """The bound of the fast kernel forced down to 2 (MLA_ATTN_OVERFLOW_LIMIT): every
+    row sum exceeds it, every row tile is flagged and recomputed by the safe kernel
+    (lazy rescaling), on ordinary data and at the usual
+    tolerance, with causal blocks, two requests, a sink with read-time rotation and
+    the 32-rows-per-wave d_c = 256 build."""
+    monkeypatch.setenv("MLA_ATTN_OVERFLOW_LIMIT", "2")
+    shape, batch = {
+        "small": (small_wan(), 1),
+        "long": (long_window(), 1),
+        "batch-causal": (small_wan(t0=6, window_frames=6, chunk_frames=4, n_valid_frames=6,
+                                   causal_frames=2), 2),
+        "sink-read": (small_wan(rope_at_read=True, sink_frames=1, window_frames=3,
+                                chunk_frames=2, t0=12, n_valid_frames=3), 1),
+        "dc256": (small_wan(d_c=256), 1),
+    }[case]
+    run = Run(shape, batch=batch, random_gains=True)
+    full_step(run, check_cache=False)
+    flags = run.L.overflow_flags(run.chunk())
+    assert flags.all(), f"{int((flags == 0).sum())} of {len(flags)} row tiles not flagged"
+
+
+def test_needle_key_overflows_the_fast_kernel():
+    """A needle: one token of the middle frame with x scaled by 64 (exact in bf16),
+    so its positional key k^R = W^K_R x, which RMSNorm does not touch, is 64 times
+    larger and its scores reach far above the rest.  Pieces that start before its
+    key tile see scores more than 64 (base 2) above their reference, so the fast
+    kernel flags their row tiles by itself and the safe path recomputes them.
+    Parity here is the Frobenius relative error alone: with scores this sharp
+    (tens of units, base 2), the bf16 rounding of the absorbed query and the keys
+    by itself moves single rows by about 1.4e-2 of max|y| in fp64 (computed on the
+    CPU for this case), so the max-abs criterion measures the inputs' precision,
+    not the path; the safe path itself is held to both criteria on ordinary data
+    by the forced-bound test above."""
+    run = Run(long_window())
+    tpf = run.s.tokens_per_frame
+    run.x[:, tpf + 700] *= 64.0
+    run.x_store = W.round_to_bf16_bits(run.x)
+    run.prefill()
+    ch = run.chunk()
+    y = run.L.step(ch, run.chunk_tokens())
+    torch.cuda.synchronize()
+    flags = run.L.overflow_flags(ch)
+    assert flags.any(), "no row tile was flagged: the fast kernel did not detect the overflow"
+    fro, _ = rel_errors(to_host(y)[0], run.oracle()["y"])
+    assert fro <= TOL["bf16"], fro
+
+
+def test_cache_write_register_staged_path():
+    """d_model = 96 (not a multiple of 64) takes the register-staged bf16 cache-write
+    kernel instead of the direct-load one; ring and y against the oracle."""
+    full_step(Run(small_wan(d_model=96), random_gains=True))
 
 
 def test_batch_of_two_requests():

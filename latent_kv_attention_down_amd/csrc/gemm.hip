@@ -4,8 +4,11 @@
 //    waves of WTM x WTN built from 32x32x16 MFMAs (256x256 tiles of 128x64 waves for
 //    large problems, 256x128 / 128x128 / 128x64 tiles of 64x64 or 64x32 waves else).  KC-wide k chunks of A and B go
 //    through an NS-stage LDS ring filled by global_load_lds_dwordx4 (vector loads
-//    into registers top out near 34 GB/s per CU, the direct path near 100 GB/s for
-//    L2-resident operands).  16-byte chunk c of stage row r sits at chunk
+//    into registers top out near 34 GB/s per CU, the direct path near 64-70 GB/s
+//    per CU for L2-resident operands with the whole chip busy).  Optionally the
+//    epilogue also produces per-row sums of squares of the result and scales its
+//    columns (the RMSNorm of c^Q taken apart), or scales rows by the RMS those sums
+//    give (see GemmArgs).  16-byte chunk c of stage row r sits at chunk
 //    c ^ ((r >> 1) & (KC/8 - 1)), applied on the global side of each load, so the
 //    32-row fragment reads are free of bank conflicts.  Rows past M or N read a
 //    clamped valid row; their results are not stored.
@@ -120,7 +123,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_nt(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32>
+// Epilogue modes of k_gemm_dma (GemmArgs): plain, producer of row sums of squares
+// with a column scale, consumer scaling rows by them.
+enum { EP_PLAIN = 0, EP_SSQ_OUT = 1, EP_ROW_RMS = 2 };
+
+template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32, int EP = EP_PLAIN>
 struct GemmDma {
   static constexpr int NW = (BM / WTM) * (BN / WTN), NT = NW * 64;
   static constexpr int ROWB = KC * 2;                  // bytes per stage row
@@ -128,10 +135,16 @@ struct GemmDma {
   static constexpr int A_LOADS = BM / RPL, B_LOADS = BN / RPL;
   static constexpr int LPW = (A_LOADS + B_LOADS) / NW;  // loads per wave per stage
   static constexpr int SB = (BM + BN) * ROWB;          // stage bytes
-  // the epilogue reuses the stages as a BM x (BN + one 16-byte piece) output tile
-  static constexpr int OUT_B = OUT_F32 ? 4 : 2;
+  // the epilogue reuses the stages as a BM x (BN + one 16-byte piece) output tile,
+  // fp32 when the producer epilogue sums squares; past both, the producer keeps the
+  // tile's BN column scales and the consumer its BM row scales for the whole kernel
+  static constexpr int OUT_B = (OUT_F32 || EP == EP_SSQ_OUT) ? 4 : 2;
   static constexpr size_t EPI = (size_t)BM * (BN + 16 / OUT_B) * OUT_B;
-  static constexpr size_t LDS = (size_t)SB * NS > EPI ? (size_t)SB * NS : EPI;
+  static constexpr size_t XOFF = (size_t)SB * NS > EPI ? (size_t)SB * NS : EPI;
+  static constexpr size_t LDS =
+      XOFF + (EP == EP_SSQ_OUT ? (size_t)BN * 4 : EP == EP_ROW_RMS ? (size_t)BM * 4 : 0);
+  static_assert(!(OUT_F32 && EP != EP_PLAIN), "row-sum epilogues write bf16");
+  static_assert(LDS <= 163840, "LDS");
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(LPW * NW == A_LOADS + B_LOADS, "loads do not split over the waves");
   static_assert(NS >= 2 && NS <= 4, "stage count");
@@ -140,11 +153,11 @@ struct GemmDma {
 template <int KC>
 __device__ __forceinline__ int gswz(int row) { return (row >> 1) & (KC / 8 - 1); }
 
-template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32>
+template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32, int EP>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64)
 __attribute__((amdgpu_waves_per_eu(WTM * WTN >= 128 * 64 ? 2 : 4, 8)))
 void k_gemm_dma(GemmArgs g) {
-  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32>;
+  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32, EP>;
   constexpr int TM = D::TM, TN = D::TN, LPW = D::LPW, RPL = D::RPL, CPR = KC / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   typedef __attribute__((address_space(3))) void lds_void;
@@ -191,6 +204,22 @@ void k_gemm_dma(GemmArgs g) {
 #pragma unroll
   for (int kc = 0; kc < NS - 1; ++kc)
     if (kc < nk) issue(kc);
+  // Epilogue operands, fetched while the first stages are in flight (their wait
+  // coincides with that of stage 0, which the loop needs anyway) and kept in LDS past
+  // the stages: the tile's column scales (producer), or 1 / RMS of each of its rows
+  // from the producer's pieces, summed in a fixed order (consumer).
+  float *xs = (float *)(smem + D::XOFF);
+  if (EP == EP_SSQ_OUT)
+    for (int c = tid; c < BN; c += D::NT)
+      xs[c] = (g.col_scale && n0 + c < g.N) ? to_f32(((const bf16 *)g.col_scale)[n0 + c]) : 1.0f;
+  if (EP == EP_ROW_RMS)
+    for (int r = tid; r < BM; r += D::NT) {
+      const int64_t row = min(m0 + r, g.M - 1);
+      float ss = 0.f;
+#pragma unroll 4
+      for (int p = 0; p < g.ssq_parts; ++p) ss += g.ssq_in[(int64_t)p * g.M + row];
+      xs[r] = 1.0f / sqrtf(ss * g.ssq_scale + g.ssq_eps);
+    }
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -257,20 +286,72 @@ void k_gemm_dma(GemmArgs g) {
   // Results through LDS for 16-byte stores.  acc[i][j][4q + r] is row
   // 8q + 4*(lane/32) + r, column l32 of the 32x32 tile.
   typedef typename std::conditional<OUT_F32, float, bf16>::type OutT;
-  constexpr int VEC = 16 / sizeof(OutT), LDC = BN + VEC;  // padded row of the tile
-  OutT *tile = (OutT *)smem;
+  typedef typename std::conditional<OUT_F32 || EP == EP_SSQ_OUT, float, bf16>::type TileT;
+  constexpr int VEC = 16 / sizeof(TileT), LDC = BN + VEC;  // padded row of the tile
+  TileT *tile = (TileT *)smem;
   __syncthreads();  // stages no longer read
+  const float *rs = xs;  // row scales (consumer), written before the k loop
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    // the lane's 16 rows of this 32-row tile come in four runs of four consecutive
+    // rows: their scales are four 16-byte reads
+    f32x4 rsv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      rsv[q] = EP == EP_ROW_RMS ? *(const f32x4 *)(rs + wm * WTM + i * 32 + q * 8 + g8 * 4)
+                                : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wm * WTM + i * 32 + (r >> 2) * 8 + g8 * 4 + (r & 3);
-        tile[row * LDC + wn * WTN + j * 32 + l32] = (OutT)(acc[i][j][r] * g.alpha);
+        float v = acc[i][j][r] * g.alpha;
+        if (EP == EP_ROW_RMS) v *= rsv[r >> 2][r & 3];
+        tile[row * LDC + wn * WTN + j * 32 + l32] = (TileT)v;
       }
+  }
   __syncthreads();
   OutT *C = (OutT *)g.C + b * g.sC;
+  if (EP == EP_SSQ_OUT) {
+    // sums of squares of each row over 64-column pieces, one thread per (row, piece),
+    // in a fixed order (the starting column rotates with the row to spread the banks)
+    for (int id = tid; id < BM * (BN / 64); id += D::NT) {
+      const int r = id % BM, col0 = (id / BM) * 64;
+      if (m0 + r < g.M && n0 + col0 < g.N) {
+        // 16 independent 16-byte reads, summed as a fixed tree; columns past N hold
+        // the results of a clamped row of B and are left out
+        float part[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const f32x4 v = *(const f32x4 *)(tile + r * LDC + col0 + 4 * q);
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t += (n0 + col0 + 4 * q + e < g.N) ? v[e] * v[e] : 0.f;
+          part[q] = t;
+        }
+#pragma unroll
+        for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+          for (int q = 0; q < w; ++q) part[q] += part[q + w];
+        g.ssq_out[(int64_t)((n0 + col0) / 64) * g.M + m0 + r] = part[0];
+      }
+    }
+    // bf16 output, each column scaled
+    for (int id = tid; id < BM * (BN / 8); id += D::NT) {
+      const int r = id / (BN / 8), c = (id % (BN / 8)) * 8;
+      if (m0 + r < g.M && n0 + c < g.N) {
+        const f32x4 a = *(const f32x4 *)(tile + r * LDC + c), b4 = *(const f32x4 *)(tile + r * LDC + c + 4);
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = (bf16)(a[e] * xs[c + e]);
+          o[4 + e] = (bf16)(b4[e] * xs[c + 4 + e]);
+        }
+        *(bf16x8 *)((bf16 *)C + (int64_t)(m0 + r) * g.ldc + n0 + c) = o;
+      }
+    }
+    return;
+  }
   for (int id = tid; id < BM * (BN / VEC); id += D::NT) {
     const int r = id / (BN / VEC), c = (id % (BN / VEC)) * VEC;
     if (m0 + r < g.M && n0 + c < g.N)
@@ -278,11 +359,11 @@ void k_gemm_dma(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32>
+template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32, int EP = EP_PLAIN>
 hipError_t launch_dma(const GemmArgs &g, hipStream_t st) {
-  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32>;
+  using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32, EP>;
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.batch);
-  const auto kern = k_gemm_dma<BM, BN, WTM, WTN, KC, NS, OUT_F32>;
+  const auto kern = k_gemm_dma<BM, BN, WTM, WTN, KC, NS, OUT_F32, EP>;
   if (D::LDS > 65536) {
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)D::LDS);
@@ -294,6 +375,8 @@ hipError_t launch_dma(const GemmArgs &g, hipStream_t st) {
 
 template <int BM, int BN, int WTM, int WTN, int KC, int NS>
 hipError_t launch_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
+  if (g.ssq_out) return launch_dma<BM, BN, WTM, WTN, KC, NS, false, EP_SSQ_OUT>(g, st);
+  if (g.ssq_in) return launch_dma<BM, BN, WTM, WTN, KC, NS, false, EP_ROW_RMS>(g, st);
   return out_f32 ? launch_dma<BM, BN, WTM, WTN, KC, NS, true>(g, st)
                  : launch_dma<BM, BN, WTM, WTN, KC, NS, false>(g, st);
 }
@@ -309,11 +392,17 @@ hipError_t gemm_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
   // 3-frame chunk the 2688-wide query GEMM (209 tiles in one round, against 399 of
   // 256x128 in two); the chunk's output projection (114 tiles) stays at 256x128.
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-  if (!out_f32 && g.N >= 512 && tiles256 >= 200)
+  if (!out_f32 && !g.ssq_out && g.N >= 512 && tiles256 >= 200) {
+    if (g.ssq_in) return launch_dma<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS>(g, st);
     return launch_dma<256, 256, 128, 64, 64, 2, false>(g, st);
+  }
   if (g.N >= 1024) return launch_dma<256, 128, 64, 64, KC, 3>(g, out_f32, st);
+  // 128x128 tiles with two 64-wide stages (64 KB of LDS, 68 KB with an fp32 output
+  // tile) leave room for a second workgroup on the CU: the per-head W^V_up GEMM
+  // (K = 192, three k chunks, 444 tiles) then runs in one round, 9.4 us against
+  // 13.4 us with four stages, and W^Q_down is no slower (20.8 against 21.6 us).
   if (g.N % 128 == 0 && mt128 * (g.N / 128) * g.batch >= 200)
-    return launch_dma<128, 128, 64, 64, KC, 4>(g, out_f32, st);
+    return launch_dma<128, 128, 64, 64, KC, KC == 64 ? 2 : 4>(g, out_f32, st);
   return launch_dma<128, 64, 64, 32, KC, 4>(g, out_f32, st);
 }
 
@@ -350,6 +439,8 @@ hipError_t launch_bf16(const GemmArgs &g, bool out_f32, hipStream_t st) {
 
 hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  const bool extra = g.ssq_out || g.ssq_in || g.col_scale;
+  if (extra && (out_f32 || g.batch != 1 || (g.ssq_out && g.ssq_in))) return hipErrorInvalidValue;
   // direct loads need 16-byte aligned rows; the 16-byte tile stores need the same
   // of C and whole 16-byte pieces of every row (N a multiple of 8 bf16 / 4 fp32)
   const int vec = out_f32 ? 4 : 8;
@@ -359,6 +450,7 @@ hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st) {
                        g.N % vec == 0;
   if (aligned && g.K > 0 && g.K % 64 == 0) return gemm_dma<64>(g, out_f32, st);
   if (aligned && g.K > 0 && g.K % 32 == 0) return gemm_dma<32>(g, out_f32, st);
+  if (extra) return hipErrorInvalidValue;  // the epilogue work needs the direct-load path
   // 128x128 tiles when N fills them and there are enough tiles for the chip
   // (two workgroups fit per CU); otherwise 64x64.
   const int64_t tiles128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch;

@@ -528,32 +528,54 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
   float *q_r = (float *)(ws + L.q_r);
   unsigned char *q_lat = ws + L.q_lat, *o_lat = ws + L.o_lat;
 
-  // c^Q = RMSNorm(W^Q_down x)  (Eq. 3, App. D.2)
-  MLA_TRY(run_gemm(c, gemm(x, c.d_model, 0, w.w_q_down, c.d_model, 0, u_q, c.d_q, 0, d.M, c.d_q,
-                           c.d_model, 1, 1.f),
-                   true, st, "query down-projection"));
-  MLA_HIP(mla::rmsnorm_rows(u_q, w.g_q, c_q, (int)d.M, c.d_q, c.rms_eps, bf, st), "query rmsnorm");
-  if (w.w_qlat) {
-    // every absorbed query row [q~_h | q^R_h] = W_qlat,h c^Q, scaled, in one GEMM:
-    // W_qlat,h = [(W^K_up,h)^T W^Q_up,h ; W^Q_R,h] prepared once (App. E Eq. 8-9)
-    MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qlat, c.d_q, 0, q_lat, (int64_t)nh * d.DK, 0, d.M,
-                             (int)(nh * d.DK), c.d_q, 1, scale),
-                     false, st, "absorbed query projection"));
+  if (w.w_qlat && bf) {
+    // c^Q = RMSNorm(W^Q_down x) * g_q (Eq. 3, App. D.2) taken apart over the two GEMMs:
+    // the first stores u * g_q (u = W^Q_down x) with the sums of squares of u per row in
+    // 64-column pieces; the second sums them and scales each row by 1 / RMS(u) on its
+    // way out.  Every absorbed query row [q~_h | q^R_h] = W_qlat,h c^Q, scaled, comes out
+    // of that one GEMM: W_qlat,h = [(W^K_up,h)^T W^Q_up,h ; W^Q_R,h] prepared once
+    // (App. E Eq. 8-9).
+    float *ssq = u_q;  // (d_q / 64 pieces) x M fp32
+    mla::GemmArgs g1 = gemm(x, c.d_model, 0, w.w_q_down, c.d_model, 0, c_q, c.d_q, 0, d.M, c.d_q,
+                            c.d_model, 1, 1.f);
+    g1.col_scale = w.g_q;
+    g1.ssq_out = ssq;
+    MLA_TRY(run_gemm(c, g1, false, st, "query down-projection"));
+    mla::GemmArgs g2 = gemm(c_q, c.d_q, 0, w.w_qlat, c.d_q, 0, q_lat, (int64_t)nh * d.DK, 0, d.M,
+                            (int)(nh * d.DK), c.d_q, 1, scale);
+    g2.ssq_in = ssq;
+    g2.ssq_parts = (c.d_q + 63) / 64;
+    g2.ssq_scale = 1.0f / (float)c.d_q;
+    g2.ssq_eps = c.rms_eps;
+    MLA_TRY(run_gemm(c, g2, false, st, "absorbed query projection"));
   } else {
-    // q^R = W^Q_R c^Q (Eq. 6); q^nope = W^Q_up c^Q (Eq. 4), then q~_h =
-    // (W^K_up,h)^T q^nope_h, scaled (App. E Eq. 8-9 applied to the query)
-    MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qr, c.d_q, 0, q_r, (int64_t)nh * c.d_rope, 0, d.M,
-                             nh * c.d_rope, c.d_q, 1, 1.f),
-                     true, st, "positional query projection"));
-    MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_q_up, c.d_q, 0, q_nope, (int64_t)nh * c.d_nope, 0,
-                             d.M, nh * c.d_nope, c.d_q, 1, 1.f),
-                     false, st, "query up-projection"));
-    MLA_HIP(mla::transpose_heads(w.w_k_up, w_t, nh, c.d_nope, c.d_c, (int)d.esz, st),
-            "key up transpose");
-    MLA_TRY(run_gemm(c, gemm(q_nope, (int64_t)nh * c.d_nope, c.d_nope, w_t, c.d_nope,
-                             (int64_t)c.d_c * c.d_nope, q_lat, (int64_t)nh * d.DK, d.DK, d.M, c.d_c,
-                             c.d_nope, nh, scale),
-                     false, st, "key absorption"));
+    // c^Q = RMSNorm(W^Q_down x)  (Eq. 3, App. D.2)
+    MLA_TRY(run_gemm(c, gemm(x, c.d_model, 0, w.w_q_down, c.d_model, 0, u_q, c.d_q, 0, d.M, c.d_q,
+                             c.d_model, 1, 1.f),
+                     true, st, "query down-projection"));
+    MLA_HIP(mla::rmsnorm_rows(u_q, w.g_q, c_q, (int)d.M, c.d_q, c.rms_eps, bf, st), "query rmsnorm");
+    if (w.w_qlat) {
+      // every absorbed query row [q~_h | q^R_h] = W_qlat,h c^Q, scaled, in one GEMM:
+      // W_qlat,h = [(W^K_up,h)^T W^Q_up,h ; W^Q_R,h] prepared once (App. E Eq. 8-9)
+      MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qlat, c.d_q, 0, q_lat, (int64_t)nh * d.DK, 0, d.M,
+                               (int)(nh * d.DK), c.d_q, 1, scale),
+                       false, st, "absorbed query projection"));
+    } else {
+      // q^R = W^Q_R c^Q (Eq. 6); q^nope = W^Q_up c^Q (Eq. 4), then q~_h =
+      // (W^K_up,h)^T q^nope_h, scaled (App. E Eq. 8-9 applied to the query)
+      MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_qr, c.d_q, 0, q_r, (int64_t)nh * c.d_rope, 0, d.M,
+                               nh * c.d_rope, c.d_q, 1, 1.f),
+                       true, st, "positional query projection"));
+      MLA_TRY(run_gemm(c, gemm(c_q, c.d_q, 0, w.w_q_up, c.d_q, 0, q_nope, (int64_t)nh * c.d_nope, 0,
+                               d.M, nh * c.d_nope, c.d_q, 1, 1.f),
+                       false, st, "query up-projection"));
+      MLA_HIP(mla::transpose_heads(w.w_k_up, w_t, nh, c.d_nope, c.d_c, (int)d.esz, st),
+              "key up transpose");
+      MLA_TRY(run_gemm(c, gemm(q_nope, (int64_t)nh * c.d_nope, c.d_nope, w_t, c.d_nope,
+                               (int64_t)c.d_c * c.d_nope, q_lat, (int64_t)nh * d.DK, d.DK, d.M, c.d_c,
+                               c.d_nope, nh, scale),
+                       false, st, "key absorption"));
+    }
   }
   // RoPE3D(q^R_h) into the last d_rope columns, same scale (Eq. 6, 12)
   mla::RopeQArgs rq;

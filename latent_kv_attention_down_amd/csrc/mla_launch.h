@@ -18,6 +18,17 @@ struct GemmArgs {
   int64_t ldc, sC;
   int M, N, K, batch;
   float alpha;
+  // Optional epilogue work (bf16 output, direct-load path, batch 1; null / 0 = none):
+  //  producer: ssq_out[(n / 64) * M + m] = sum over the 64-column piece of
+  //    (alpha * acc)^2, and the stored value is alpha * acc * col_scale[n] (bf16
+  //    vector, or ones when col_scale is null);
+  //  consumer: row m is multiplied by 1 / sqrt(ssq_scale * sum_{p < ssq_parts}
+  //    ssq_in[p * M + m] + ssq_eps) before rounding.
+  const void *col_scale = nullptr;
+  float *ssq_out = nullptr;
+  const float *ssq_in = nullptr;
+  int ssq_parts = 0;
+  float ssq_scale = 0.f, ssq_eps = 0.f;
 };
 hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st);
 hipError_t gemm_f32_nt(const GemmArgs &g, hipStream_t st);

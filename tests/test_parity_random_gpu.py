@@ -3,8 +3,8 @@ token per frame up, every latent width the bf16 path is built for, both RoPE
 placements, sink frames, partial windows, wrapped rings, causal blocks, batches of
 requests, both output epilogues, explicit RoPE frequency tables and all three ring
 layouts, each checked through the C ABI against the fp64 oracle at the usual
-tolerances.  Invalid draws (as the library's own validation
-judges them) are redrawn, so every case is one the ABI accepts."""
+tolerances.  Draws that the library's own validation refuses are redrawn, so
+every case is one the ABI accepts."""
 import os
 
 import numpy as np

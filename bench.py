@@ -195,7 +195,7 @@ def main():
                          "(30: the Wan-1.3B backbone's attention layers)")
     ap.add_argument("--batch", type=int, default=1,
                     help="independent requests per step, each with its own cache")
-    ap.add_argument("--epilogue", choices=("two-stage", "absorbed"), default="absorbed",
+    ap.add_argument("--epilogue", choices=("two-stage", "absorbed"), default="two-stage",
                     help="two-stage: per-head W^V_up then W_O; absorbed: y = sum_h B_h O_lat,h "
                          "with B_h = W_O,h W^V_up,h prepared once (FLOPs are counted as "
                          "two-stage either way)")

@@ -285,11 +285,12 @@ def sampled_full(shape, batch=1):
 
 @pytest.mark.timeout(600)
 def test_wan13b_layer_full_tensors():
-    """Wan-1.3B layer, 3-frame chunk over the 21-frame window, in the launch the
-    benchmark times (mla_step with both absorbed weight sets), compared in full:
-    every element of y (4680 x 1536), of out_heads from mla_chunk_attention
-    (4680 x 1536, the unabsorbed query route and per-head W^V_up) and of the ring
-    (21 slots x 1560 tokens x 224, one bf16 ulp) against the oracle -- no sampling."""
+    """Wan-1.3B layer, 3-frame chunk over the 21-frame window, compared in full against
+    the oracle -- no sampling: every element of out_heads from mla_chunk_attention
+    (4680 x 1536, the unabsorbed query route and per-head W^V_up), of y from mla_step in
+    the launch the benchmark times (absorbed query, W^V_up then W_O) and of y with the
+    value-absorbed epilogue as well (4680 x 1536 each), and every element of the ring
+    (21 slots x 1560 tokens x 224, one bf16 ulp)."""
     s = W.shape_by_name("wan1.3b-w21")
     run = Run(s)
     say(f"case {s.name} full tensors: prefill {len(run.window_ids) - s.chunk_frames} frames")
@@ -300,19 +301,20 @@ def test_wan13b_layer_full_tensors():
     out = run.L.chunk_attention(ch, x)
     torch.cuda.synchronize()
     out_h = to_host(out)[0]
-    run.L.absorb_value()
     run.L.absorb_query()
-    y = run.L.step(ch, x)  # writes the chunk's frames again (same values), then attends
+    y_two = to_host(run.L.step(ch, x))[0]  # writes the chunk's frames again (same values)
+    run.L.absorb_value()
+    y_abs = to_host(run.L.step(ch, x))[0]
     torch.cuda.synchronize()
-    y_h = to_host(y)[0]
     ring = to_host(run.L.ring())[0]
     say("  device done; oracle over all 4680 query tokens ...")
     ref = run.oracle()
     assert out_h.shape == ref["out"].shape == (4680, 1536)
     fro, mx = assert_close(out_h, ref["out"], TOL["bf16"], "out_heads (all elements)")
     say(f"  out_heads: frobenius {fro:.3e}, max {mx:.3e}")
-    fro, mx = assert_close(y_h, ref["y"], TOL["bf16"], "y (all elements)")
-    say(f"  y: frobenius {fro:.3e}, max {mx:.3e}")
+    for name, y_h in (("y, W^V_up then W_O", y_two), ("y, value-absorbed", y_abs)):
+        fro, mx = assert_close(y_h, ref["y"], TOL["bf16"], f"{name} (all elements)")
+        say(f"  {name}: frobenius {fro:.3e}, max {mx:.3e}")
     ref_ring = run.oracle_ring()
     assert ring.shape == ref_ring.shape == (21 * 1560, 224)
     assert_cache_rows(ring, ref_ring, "bf16", "ring (all 32760 rows)")

@@ -27,7 +27,6 @@ def test_thirty_layer_step():
     runs = []
     for l in range(N_LAYERS):
         run = Run(s, layer=l, pool=pool)
-        run.L.absorb_value()
         run.L.absorb_query()
         run.prefill()
         runs.append(run)

@@ -39,6 +39,11 @@
  *     environment variable MLA_ATTN_OVERFLOW_LIMIT=v (a number > 0, below 2^64)
  *     the bound is v instead, so that path can be exercised on ordinary data;
  *     results are exact either way.
+ *   - Score-MFMA check: the bf16 attention kernel issues its score MFMAs as
+ *     inline assembly, spacing their consumers by hand.  With the environment
+ *     variable MLA_ATTN_SCORE_MFMA=builtin it runs the same kernel with the
+ *     compiler's own MFMA form instead; the results are the same bits, which is
+ *     what the hook is for (it is slower).
  *   - Failure injection: with the environment variable MLA_FAULT_INJECT=launch,
  *     every entry point that would launch a kernel returns MLA_ERR_HIP after
  *     its argument checks and before anything reaches the HIP runtime, with

@@ -151,7 +151,7 @@ struct Cfg {
 
 // One wave per SIMD, QT x 32 query rows per wave, key tiles brought into an unpadded
 // swizzled four-stage LDS ring by buffer loads into LDS (k_latent_attn_w1).
-template <int DC_, int DR_, int QT_ = 2>
+template <int DC_, int DR_, int QT_ = 2, bool BUILTIN_ = false>
 struct CfgW {
   static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = 4, WPC = 1, NBUF = 4;
   static constexpr int NT = NW * 64;
@@ -170,8 +170,9 @@ struct CfgW {
   // LDS fragments read ahead of their MFMAs in the score and value contractions.
   static constexpr int DS = 3, DV = 3;
   // Score MFMAs issued so that S stays in architectural VGPRs (see TileW::scores),
-  // where q_lat takes at most 112 of them (more would spill).
-  static constexpr bool ASM_SCORES = DK * QT <= 448;
+  // where q_lat takes at most 112 of them (more would spill).  BUILTIN_ keeps the
+  // compiler's own MFMA form, against which the asm form is checked bit for bit.
+  static constexpr bool ASM_SCORES = !BUILTIN_ && DK * QT <= 448;
   static_assert(CPR % 4 == 0 && LOADS * NW * 64 == BN * CPR, "tile does not split into loads");
   static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
 };
@@ -180,6 +181,7 @@ struct CfgW {
 template <int DC, int DR>
 struct Choice {
   using Fast = CfgW<DC, DR>;
+  using FastBuiltin = CfgW<DC, DR, 2, true>;
   using Safe = Cfg<DC, DR, 1, 4>;
 };
 // At d_c = 256 the 64-row O^T alone needs all 256 accumulation registers, so the
@@ -187,6 +189,7 @@ struct Choice {
 template <>
 struct Choice<256, 32> {
   using Fast = CfgW<256, 32, 1>;
+  using FastBuiltin = CfgW<256, 32, 1, true>;
   using Safe = Cfg<256, 32, 1, 4>;
 };
 
@@ -1173,7 +1176,14 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
   using S = typename Choice<DC, DR>::Safe;
   Sched s = make_sched(a, F::RW, a.grid * F::WPC);
   if (s.T <= 0) return hipSuccess;
-  const auto fast = k_latent_attn_w1<F>;
+  auto fast = k_latent_attn_w1<F>;
+  if constexpr (F::ASM_SCORES) {
+    // the same kernel with the compiler's MFMA form for the scores (same layout,
+    // records and results), on request
+    using FB = typename Choice<DC, DR>::FastBuiltin;
+    static_assert(FB::RW == F::RW && FB::REC == F::REC && FB::LDS == F::LDS, "same layout");
+    if (a.builtin_scores) fast = k_latent_attn_w1<FB>;
+  }
   hipError_t e = allow_lds(fast, F::LDS);
   if (e == hipSuccess) e = allow_lds(k_latent_attn_safe<S>, S::LDS);
   if (e != hipSuccess) return e;

@@ -388,6 +388,13 @@ float overflow_limit() {
   return (end && *end == 0 && f > 0.f && std::isfinite(f)) ? f : 0.f;
 }
 
+// MLA_ATTN_SCORE_MFMA=builtin: the fast attention kernel issues its score MFMAs in
+// the compiler's form instead of inline asm (same results, bit for bit).
+bool builtin_scores() {
+  const char *v = std::getenv("MLA_ATTN_SCORE_MFMA");
+  return v && std::strcmp(v, "builtin") == 0;
+}
+
 // MLA_FAULT_INJECT=launch: refuse every launch before it reaches the HIP runtime.
 int launch_gate() {
   const char *v = std::getenv("MLA_FAULT_INJECT");
@@ -471,6 +478,7 @@ int run_latent_attention(const mla_config &c, const mla_chunk &k, const Dims &d,
   a.flags_zeroed = flags_zeroed;
   a.grid = attn_grid_cus();
   a.sum_limit = overflow_limit();
+  a.builtin_scores = builtin_scores();
   if (c.dtype == MLA_BF16)
     MLA_HIP(mla::latent_attention_bf16(a, g_ev_start, g_ev_stop, st), "latent attention");
   else

@@ -125,6 +125,9 @@ struct AttnArgs {
   // Row sums (weights relative to the first key tile's max) above this send the
   // row tile to the safe path: 2^64 (overflow guard), or lower to force it.
   float sum_limit;
+  // Score MFMAs in the compiler's own form instead of the inline-asm one (a check:
+  // both give the same bits).
+  bool builtin_scores;
 };
 // Row tiles (with causal blocks, a block's last tile may be partial) and
 // (row tile, key tile) steps of the bf16 kernel for these arguments.

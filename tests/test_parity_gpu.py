@@ -179,6 +179,49 @@ def test_cache_write_register_staged_path():
     full_step(Run(small_wan(d_model=96), random_gains=True))
 
 
+SCORE_FORM_CASES = {
+    "small": lambda: small_wan(),
+    "causal-blocks": lambda: small_wan(window_frames=6, chunk_frames=6, t0=0, n_valid_frames=6,
+                                       causal_frames=2),
+    "sink-read": lambda: small_wan(rope_at_read=True, sink_frames=1, window_frames=3,
+                                   chunk_frames=2, t0=12, n_valid_frames=3),
+    "dc128": lambda: small_wan(d_c=128, d_rope=32, d_nope=96, rope_pairs=(6, 5, 5)),
+    "dc256": lambda: small_wan(d_c=256, d_rope=32, d_nope=96, rope_pairs=(6, 5, 5)),
+    "wan1.3b-w21": lambda: W.shape_by_name("wan1.3b-w21"),
+}
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case", list(SCORE_FORM_CASES))
+def test_score_mfma_forms_agree_bitwise(case, monkeypatch):
+    """The fast attention kernel issues its score MFMAs as inline asm, and the waits
+    before their results are read were counted by hand.  The same kernel with the
+    compiler's own MFMA form (MLA_ATTN_SCORE_MFMA=builtin), on the same device inputs
+    and in the launch the benchmark times, must give the same bits of y.  A missing
+    wait would let a read of S see a stale value, and y would differ.  The cases cover
+    the first and the masked last key tile, causal blocks, a gathered window and
+    every latent width that uses the asm form.  Both runs are also checked against
+    the oracle (sampled query tokens at full size)."""
+    s = SCORE_FORM_CASES[case]()
+    run = Run(s)
+    say(f"case score MFMA forms {case}")
+    run.prefill()
+    ch, x = run.chunk(), run.chunk_tokens()
+    run.L.absorb_query()
+    y_asm = run.L.step(ch, x).clone()
+    monkeypatch.setenv("MLA_ATTN_SCORE_MFMA", "builtin")
+    y_builtin = run.L.step(ch, x).clone()
+    monkeypatch.delenv("MLA_ATTN_SCORE_MFMA")
+    y_again = run.L.step(ch, x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y_asm, y_again)
+    assert torch.equal(y_asm, y_builtin), "asm and builtin score MFMAs disagree"
+    rows = sample_rows(s) if s.tokens_per_frame > 1000 else None
+    ref = run.oracle(query_rows=rows)
+    y_h = to_host(y_asm)[0]
+    assert_close(y_h if rows is None else y_h[rows], ref["y"], TOL["bf16"], "y")
+
+
 def test_batch_of_two_requests():
     full_step(Run(small_wan(t0=6), batch=2))
 

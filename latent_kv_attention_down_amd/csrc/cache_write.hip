@@ -56,7 +56,7 @@ __device__ void finish_rows(float *tile, int ld, int rows, int m0, const CacheWr
   }
   if (!a.rotate) return;
   const int m = m0 + r, i = m % a.T_q, n = i % a.tpf;
-  const float pos[3] = {(float)(a.t0 + i / a.tpf), (float)(n / a.grid_w), (float)(n % a.grid_w)};
+  const double pos[3] = {(double)(a.t0 + i / a.tpf), (double)(n / a.grid_w), (double)(n % a.grid_w)};
   for (int p = sub; p < a.rope.n_pairs; p += 8) {
     float re = tile[r * ld + a.d_c + 2 * p], im = tile[r * ld + a.d_c + 2 * p + 1];
     rope_rotate(re, im, pos[a.rope.axis[p]], a.rope.omega[p]);
@@ -235,11 +235,11 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteAr
     // with wave-uniform table reads.
     const int p0 = (wave * 32 - a.d_c) / 2;
     int ax[2] = {0, 0};
-    float om[2] = {0.f, 0.f};
+    double om[2] = {0.0, 0.0};
     for (int q = 0; q < 16; ++q) {
       const int pq = p0 + q;
       const int axq = a.rope.axis[pq];
-      const float omq = a.rope.omega[pq];
+      const double omq = a.rope.omega[pq];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         if (j * 8 + (l16 >> 1) == q) {
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteAr
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = i * 16 + (lane >> 4) * 4 + r, m = m0 + t, ti = m % a.T_q, n = ti % a.tpf;
-        const float pos[3] = {(float)(a.t0 + ti / a.tpf), (float)(n / a.grid_w), (float)(n % a.grid_w)};
+        const double pos[3] = {(double)(a.t0 + ti / a.tpf), (double)(n / a.grid_w), (double)(n % a.grid_w)};
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const float v = acc[i][j][r], other = dpp_xor1(v);
@@ -359,18 +359,11 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArg
   // RoPE table of this workgroup's tokens (keys kept unrotated need none)
   for (int e = tid; a.rotate && e < kBM * np; e += NT) {
     const int t = e / np, p = e % np, m = m0 + t, ti = m % a.T_q, n = ti % a.tpf;
-    // unrolled over the table so its scalar loads are issued together
-    int ax = 0;
-    float om = 0.f;
-#pragma unroll
-    for (int q = 0; q < C::MAX_PAIRS; ++q)
-      if (q == p) {
-        ax = a.rope.axis[q];
-        om = a.rope.omega[q];
-      }
-    const float pos = ax == 0 ? (float)(a.t0 + ti / a.tpf) : (ax == 1 ? (float)(n / a.grid_w) : (float)(n % a.grid_w));
+    const int ax = a.rope.axis[p];
+    const double om = a.rope.omega[p];
+    const double pos = ax == 0 ? (double)(a.t0 + ti / a.tpf) : (ax == 1 ? (double)(n / a.grid_w) : (double)(n % a.grid_w));
     float sn, cs;
-    sincosf(pos * om, &sn, &cs);
+    rope_sincos(pos, om, sn, cs);
     rtab[e] = make_float2(cs, sn);
   }
 

@@ -241,8 +241,8 @@ mla::RopeTable rope_table(const mla_config &c) {
   for (int a = 0; a < 3; ++a)
     for (int k = 0; k < c.rope_pairs[a]; ++k, ++p) {
       t.axis[p] = a;
-      t.omega[p] = given ? c.rope_freq[p]
-                         : (float)std::pow((double)c.rope_theta, -2.0 * k / (double)width[a]);
+      t.omega[p] = given ? (double)c.rope_freq[p]
+                         : std::pow((double)c.rope_theta, -2.0 * k / (double)width[a]);
     }
   t.n_pairs = p;
   return t;

@@ -46,10 +46,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// sin and cos of the angle pos * omega.  The product is formed and reduced to
+// [-pi, pi] in fp64 (a frame index of a long rollout times a frequency near 1 is far
+// beyond what an fp32 product or argument resolves), and only the reduced angle goes
+// through the fp32 sincos.
+__device__ __forceinline__ void rope_sincos(double pos, double omega, float &s, float &c) {
+  const double two_pi = 6.283185307179586;
+  const double a = pos * omega;
+  const double r = fma(-two_pi, rint(a * (1.0 / two_pi)), a);
+  sincosf((float)r, &s, &c);
+}
+
 // Rotate pair (re, im) by angle pos * omega (counter-clockwise).
-__device__ __forceinline__ void rope_rotate(float &re, float &im, float pos, float omega) {
+__device__ __forceinline__ void rope_rotate(float &re, float &im, double pos, double omega) {
   float s, c;
-  sincosf(pos * omega, &s, &c);
+  rope_sincos(pos, omega, s, c);
   float r = re * c - im * s;
   float i = re * s + im * c;
   re = r;

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_rope_q(RopeQArgs a) {
   const int h = mh % a.n_h;
   const int m = mh / a.n_h;
   const int i = m % a.T_q, n = i % a.tpf;
-  const float pos[3] = {(float)(a.t0 + i / a.tpf), (float)(n / a.grid_w), (float)(n % a.grid_w)};
+  const double pos[3] = {(double)(a.t0 + i / a.tpf), (double)(n / a.grid_w), (double)(n % a.grid_w)};
   OutT *dst = (OutT *)a.q_lat + mh * (a.d_c + a.d_rope) + a.d_c + 2 * p0;
   float v[2 * PG];
   float scale = a.scale;

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_assemble_bf16(AssembleArgs a) {
   bf16x8 out = v;
   if (a.rotate && ch * 8 >= a.d_c) {
     const int64_t i = j / a.tpf, n = j % a.tpf;
-    const float pos[3] = {(float)i, (float)(n / a.grid_w), (float)(n % a.grid_w)};
+    const double pos[3] = {(double)i, (double)(n / a.grid_w), (double)(n % a.grid_w)};
     const int p0 = (ch * 8 - a.d_c) / 2;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void k_assemble_f32(AssembleArgs a) {
   if (a.rotate && c >= a.d_c) {
     const int p = (c - a.d_c) / 2, e = (c - a.d_c) % 2;
     const int64_t i = j / a.tpf, n = j % a.tpf;
-    const float pos[3] = {(float)i, (float)(n / a.grid_w), (float)(n % a.grid_w)};
+    const double pos[3] = {(double)i, (double)(n / a.grid_w), (double)(n % a.grid_w)};
     float re = *ring_src<float>(a, b, row, a.d_c + 2 * p);
     float im = *ring_src<float>(a, b, row, a.d_c + 2 * p + 1);
     rope_rotate(re, im, pos[a.rope.axis[p]], a.rope.omega[p]);

@@ -222,6 +222,19 @@ def test_score_mfma_forms_agree_bitwise(case, monkeypatch):
     assert_close(y_h if rows is None else y_h[rows], ref["y"], TOL["bf16"], "y")
 
 
+@pytest.mark.parametrize("t0,read", [(1_000_003, False), (3_000_000_001, False),
+                                     (3_000_000_001, True)])
+def test_large_absolute_positions(t0, read):
+    """A long rollout without the read-time re-indexing: write-time rotation at frame
+    indices far beyond what fp32 resolves (at t0 = 10^6 an fp32 product pos * omega is
+    off by up to ~0.03 rad, several bf16 steps of the rotated key).  The angle is
+    formed and reduced modulo 2 pi in fp64, so every ring element stays within one
+    bf16 ulp of the oracle's exact rotation and y within tolerance.  Past 2^31 the
+    frame index also exercises the 64-bit position and slot arithmetic; read-time
+    rotation there re-indexes to window-local positions."""
+    full_step(Run(small_wan(t0=t0, rope_at_read=read), random_gains=True))
+
+
 def test_batch_of_two_requests():
     full_step(Run(small_wan(t0=6), batch=2))
 

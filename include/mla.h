@@ -166,7 +166,10 @@ typedef struct {
 typedef struct {
   int32_t batch;          /* B >= 1 independent requests (separate caches)        */
   int32_t chunk_frames;   /* C: latent frames in the query chunk (3)              */
-  int64_t t0;             /* absolute index of the chunk's first latent frame     */
+  int64_t t0;             /* absolute index of the chunk's first latent frame,    */
+                          /* >= 0 and as large as a rollout gets: rotation angles */
+                          /* are formed and reduced mod 2 pi in fp64 from the     */
+                          /* exact index                                           */
   int32_t n_valid_frames; /* local frames attended after the chunk is written:    */
                           /* frames t0+C-n_valid .. t0+C-1, none of them a sink   */
                           /* frame, n_valid <= W and covering every chunk frame   */

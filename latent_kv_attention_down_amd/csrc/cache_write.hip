@@ -9,6 +9,7 @@
 //  * fp32: one token per workgroup, SIMT dot products.
 #include "mla_device.h"
 #include "mla_launch.h"
+#include "rope_q_item.h"
 
 namespace mla {
 namespace {
@@ -307,7 +308,7 @@ __device__ __forceinline__ void wait_stage(int after) {
 }
 
 template <int N>
-__global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArgs a) {
+__device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, int block) {
   using C = CwDma<N>;
   constexpr int NT = C::NT, KC = C::KC, NS = C::NS, NWAVE = C::NWAVE;
   constexpr int LDT = N + 8;
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kg = lane >> 4;
-  const int m0 = blockIdx.x * kBM;
+  const int m0 = block * kBM;
   const int nk = a.d / KC;
   const int np = a.d_rope / 2;
 
@@ -444,9 +445,10 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArg
         for (int r = 0; r < 4; ++r) {
           const int t = i * 16 + (lane >> 4) * 4 + r;
           const float v = acc[i][j][r], other = dpp_xor1(v);
-          const float re = even ? v : other, im = even ? other : v;
+          float re = even ? v : other, im = even ? other : v;
           const float2 cs = a.rotate ? rtab[t * np + p] : make_float2(1.f, 0.f);
-          tileo[t * LDT + col] = (bf16)(even ? re * cs.x - im * cs.y : re * cs.y + im * cs.x);
+          rotate_by(re, im, cs.y, cs.x);
+          tileo[t * LDT + col] = (bf16)(even ? re : im);
         }
     }
   }
@@ -455,6 +457,43 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArg
     const int r = id / (N / 8), c8 = (id % (N / 8)) * 8, m = m0 + r;
     if (m < a.M) *(bf16x8 *)ring_elem<bf16>(a, m, c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
   }
+}
+
+template <int N>
+__global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma(CacheWriteArgs a) {
+  cache_write_dma_block<N>(a, blockIdx.x);
+}
+
+// The same write with the chunk step's query RoPE riding along: the first cw_blocks
+// workgroups write the cache, the rest (on the CUs those leave idle: 147 of 256 at
+// the Wan-1.3B chunk) rotate the rope columns of the absorbed query rows in place and
+// clear the attention's overflow flags, work items strided over them.  The two jobs
+// share no data; one launch replaces two.
+template <int N>
+__global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_dma_rope(CacheWriteArgs a, RopeQArgs r,
+                                                                        int cw_blocks) {
+  if ((int)blockIdx.x < cw_blocks) {
+    cache_write_dma_block<N>(a, blockIdx.x);
+    return;
+  }
+  const int64_t items = rope_q_items(r, 4);
+  const int64_t stride = (int64_t)(gridDim.x - cw_blocks) * blockDim.x;
+  for (int64_t idx = (int64_t)(blockIdx.x - cw_blocks) * blockDim.x + threadIdx.x; idx < items;
+       idx += stride)
+    rope_q_item<bf16, 4>(r, idx);
+}
+
+template <int N>
+hipError_t launch_dma_rope(const CacheWriteArgs &a, const RopeQArgs &r, int rope_blocks,
+                           hipStream_t st) {
+  using C = CwDma<N>;
+  hipError_t e = hipFuncSetAttribute((const void *)k_cache_write_dma_rope<N>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+  if (e != hipSuccess) return e;
+  const int cw = (a.M + kBM - 1) / kBM;
+  hipLaunchKernelGGL(k_cache_write_dma_rope<N>, dim3(cw + rope_blocks), dim3(C::NT), C::LDS, st, a,
+                     r, cw);
+  return hipGetLastError();
 }
 
 template <int N>
@@ -522,6 +561,24 @@ hipError_t cache_write_bf16(const CacheWriteArgs &a, hipStream_t st) {
     case 224: return launch_bf16<224>(a, st);
     case 256: return launch_bf16<256>(a, st);
     case 288: return launch_bf16<288>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool cache_write_takes_rope(const CacheWriteArgs &a, const RopeQArgs &r) {
+  const int n = a.d_c + a.d_rope;
+  return a.M > 0 && a.d % CwDma<224>::KC == 0 && a.d_rope / 2 <= CwDma<224>::MAX_PAIRS &&
+         (n == 160 || n == 224 || n == 256 || n == 288) && r.in_place && (r.d_rope / 2) % 4 == 0;
+}
+
+hipError_t cache_write_bf16_rope(const CacheWriteArgs &a, const RopeQArgs &r, int rope_blocks,
+                                 hipStream_t st) {
+  if (!cache_write_takes_rope(a, r) || rope_blocks < 1) return hipErrorInvalidValue;
+  switch (a.d_c + a.d_rope) {
+    case 160: return launch_dma_rope<160>(a, r, rope_blocks, st);
+    case 224: return launch_dma_rope<224>(a, r, rope_blocks, st);
+    case 256: return launch_dma_rope<256>(a, r, rope_blocks, st);
+    case 288: return launch_dma_rope<288>(a, r, rope_blocks, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -403,8 +403,8 @@ int launch_gate() {
   return MLA_OK;
 }
 
-int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
-                    const mla_cache &cache, hipStream_t st) {
+mla::CacheWriteArgs cache_write_args(const mla_config &c, const mla_weights &w, const mla_chunk &k,
+                                     const void *x, const mla_cache &cache) {
   const Dims d = dims(c, k);
   mla::CacheWriteArgs a;
   a.x = x;
@@ -425,6 +425,12 @@ int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &
   a.t0 = k.t0;
   a.eps = c.rms_eps;
   a.rope = rope_table(c);
+  return a;
+}
+
+int run_cache_write(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
+                    const mla_cache &cache, hipStream_t st) {
+  const mla::CacheWriteArgs a = cache_write_args(c, w, k, x, cache);
   if (c.dtype == MLA_BF16)
     MLA_HIP(mla::cache_write_bf16(a, st), "cache write");
   else
@@ -521,12 +527,12 @@ int run_gemm(const mla_config &c, const mla::GemmArgs &g, bool out_f32, hipStrea
     if (s_ != MLA_OK) return s_; \
   } while (0)
 
-// Query preparation, latent attention and, when out_heads is given, the per-head
-// value up-projection.
-int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chunk &k,
-                        const void *x, const mla_cache &cache, void *out_heads, unsigned char *ws,
-                        hipStream_t st) {
-  const Dims d = dims(c, k, cache_in_place(c, k.batch, cache));
+// Query preparation (Eq. 3-4, 6; App. E Eq. 8-9): the absorbed query rows in the
+// workspace.  The RoPE pass (its arguments in *rq) is launched here unless the caller
+// takes it over (launch_rope false: the step runs it inside the cache write's launch).
+int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
+                    unsigned char *ws, hipStream_t st, bool launch_rope, mla::RopeQArgs *rq_out) {
+  const Dims d = dims(c, k);
   const Workspace L = carve(c, k);
   const bool bf = c.dtype == MLA_BF16;
   const int nh = c.n_heads;
@@ -603,7 +609,19 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
   rq.n_zero = (int)L.n_flags;
   rq.in_place = w.w_qlat != nullptr;
   if (rq.in_place) rq.q_r = nullptr;
-  MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
+  if (rq_out) *rq_out = rq;
+  if (launch_rope) MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
+  return MLA_OK;
+}
+
+// Latent attention over the window and, when out_heads is given, the per-head value
+// up-projection, on queries prepared by prepare_queries.
+int attend(const mla_config &c, const mla_weights &w, const mla_chunk &k, const mla_cache &cache,
+           void *out_heads, unsigned char *ws, hipStream_t st) {
+  const Dims d = dims(c, k, cache_in_place(c, k.batch, cache));
+  const Workspace L = carve(c, k);
+  const int nh = c.n_heads;
+  unsigned char *q_lat = ws + L.q_lat, *o_lat = ws + L.o_lat;
   const void *keys = nullptr;
   MLA_TRY(attended_keys(c, k, d, cache, ws, &keys, st));
   // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16)
@@ -615,6 +633,15 @@ int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chu
                            d.M, c.d_head, c.d_c, nh, 1.f),
                    false, st, "value up-projection"));
   return MLA_OK;
+}
+
+// Query preparation, latent attention and, when out_heads is given, the per-head
+// value up-projection.
+int run_chunk_attention(const mla_config &c, const mla_weights &w, const mla_chunk &k,
+                        const void *x, const mla_cache &cache, void *out_heads, unsigned char *ws,
+                        hipStream_t st) {
+  MLA_TRY(prepare_queries(c, w, k, x, ws, st, true, nullptr));
+  return attend(c, w, k, cache, out_heads, ws, st);
 }
 
 int check_ws(const mla_config &c, const mla_chunk &k, void *ws, size_t ws_bytes) {
@@ -638,14 +665,32 @@ int validate_step(const mla_config *cfg, const mla_weights *w, const mla_chunk *
 }
 
 // The chunk step on validated arguments: cache write, chunk attention, output
-// projection (§3.3), in `ws` laid out by carve().
+// projection (§3.3), in `ws` laid out by carve().  With the absorbed bf16 query the
+// query GEMMs run first and the query's in-place RoPE pass (with the flag clearing)
+// rides in the cache write's launch, on the CUs the write leaves idle; the write
+// still precedes the attention, which reads the chunk's own frames.
 int run_step(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
              const mla_cache &cache, void *y, unsigned char *ws, hipStream_t st) {
   const Workspace L = carve(c, k);
   const Dims d = dims(c, k);
-  MLA_TRY(run_cache_write(c, w, k, x, cache, st));
+  const mla::CacheWriteArgs cw = cache_write_args(c, w, k, x, cache);
+  mla::RopeQArgs rq_shape;
+  std::memset(&rq_shape, 0, sizeof(rq_shape));
+  rq_shape.in_place = w.w_qlat != nullptr;
+  rq_shape.d_rope = c.d_rope;
+  const bool fused = c.dtype == MLA_BF16 && mla::cache_write_takes_rope(cw, rq_shape);
+  if (fused) {
+    mla::RopeQArgs rq;
+    MLA_TRY(prepare_queries(c, w, k, x, ws, st, false, &rq));
+    const int cw_blocks = (int)((d.M + 31) / 32), cus = attn_grid_cus();
+    const int rope_blocks = cus - cw_blocks > 16 ? cus - cw_blocks : 16;
+    MLA_HIP(mla::cache_write_bf16_rope(cw, rq, rope_blocks, st), "cache write with query rope");
+  } else {
+    MLA_TRY(run_cache_write(c, w, k, x, cache, st));
+    MLA_TRY(prepare_queries(c, w, k, x, ws, st, true, nullptr));
+  }
   if (w.w_b) {
-    MLA_TRY(run_chunk_attention(c, w, k, x, cache, nullptr, ws, st));
+    MLA_TRY(attend(c, w, k, cache, nullptr, ws, st));
     // y = sum_h B_h O_lat,h  (App. E Eq. 10-11): row (token) of O_lat is n_h * d_c wide
     const int64_t kb = (int64_t)c.n_heads * c.d_c;
     MLA_TRY(run_gemm(c, gemm(ws + L.o_lat, kb, 0, w.w_b, kb, 0, y, c.d_model, 0, d.M, c.d_model,
@@ -653,7 +698,7 @@ int run_step(const mla_config &c, const mla_weights &w, const mla_chunk &k, cons
                      false, st, "value-absorbed output projection"));
     return MLA_OK;
   }
-  MLA_TRY(run_chunk_attention(c, w, k, x, cache, ws + L.out_heads, ws, st));
+  MLA_TRY(attend(c, w, k, cache, ws + L.out_heads, ws, st));
   // y = W_O out  (§3.3)
   MLA_TRY(run_gemm(c, gemm(ws + L.out_heads, (int64_t)c.n_heads * c.d_head, 0, w.w_o,
                            (int64_t)c.n_heads * c.d_head, 0, y, c.d_model, 0, d.M, c.d_model,

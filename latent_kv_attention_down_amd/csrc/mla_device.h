@@ -57,14 +57,21 @@ __device__ __forceinline__ void rope_sincos(double pos, double omega, float &s, 
   sincosf((float)r, &s, &c);
 }
 
+// (re, im) turned by the angle whose sine and cosine are s and c, with the fused
+// multiply-adds spelled out, so that every kernel that rotates (whatever code the
+// compiler inlines this into) gives the same bits.
+__device__ __forceinline__ void rotate_by(float &re, float &im, float s, float c) {
+  const float r = fmaf(re, c, -(im * s));
+  const float i = fmaf(re, s, im * c);
+  re = r;
+  im = i;
+}
+
 // Rotate pair (re, im) by angle pos * omega (counter-clockwise).
 __device__ __forceinline__ void rope_rotate(float &re, float &im, double pos, double omega) {
   float s, c;
   rope_sincos(pos, omega, s, c);
-  float r = re * c - im * s;
-  float i = re * s + im * c;
-  re = r;
-  im = i;
+  rotate_by(re, im, s, c);
 }
 
 }  // namespace mla

@@ -75,6 +75,12 @@ struct RopeQArgs {
   bool in_place;  // q_r is null: rotate the (already scaled) RoPE columns of q_lat in place
 };
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st);
+// The bf16 cache write with the in-place query RoPE of the same step in one launch:
+// rope_blocks workgroups beside the cache write's own (bf16, in-place, pair count a
+// multiple of 4, a shape the direct-load cache write covers: cache_write_takes_rope).
+bool cache_write_takes_rope(const CacheWriteArgs &a, const RopeQArgs &r);
+hipError_t cache_write_bf16_rope(const CacheWriteArgs &a, const RopeQArgs &r, int rope_blocks,
+                                 hipStream_t st);
 
 // Window assembly: context frame i (the n_sink sink frames, then frames
 // first_local, first_local+1, ...) is copied from its ring slot to rows i*tpf .. of

@@ -8,6 +8,7 @@
 //    q~_h = (W^K_up,h)^T q^nope_h.
 #include "mla_device.h"
 #include "mla_launch.h"
+#include "rope_q_item.h"
 
 namespace mla {
 namespace {
@@ -55,40 +56,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *in, const GT 
 // PG pairs per thread (4 when the pair count allows: 32-byte reads of q^R).
 template <typename OutT, int PG>
 __global__ __launch_bounds__(256) void k_rope_q(RopeQArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx < a.n_zero) a.zero[idx] = 0;
-  const int P = a.d_rope / 2, NG = P / PG;
-  const int64_t total = (int64_t)a.M * a.n_h * NG;
-  if (idx >= total) return;
-  const int p0 = (int)(idx % NG) * PG;
-  const int64_t mh = idx / NG;
-  const int h = mh % a.n_h;
-  const int m = mh / a.n_h;
-  const int i = m % a.T_q, n = i % a.tpf;
-  const double pos[3] = {(double)(a.t0 + i / a.tpf), (double)(n / a.grid_w), (double)(n % a.grid_w)};
-  OutT *dst = (OutT *)a.q_lat + mh * (a.d_c + a.d_rope) + a.d_c + 2 * p0;
-  float v[2 * PG];
-  float scale = a.scale;
-  if (a.in_place) {  // the GEMM already wrote scale * q^R here
-#pragma unroll
-    for (int e = 0; e < 2 * PG; ++e) v[e] = to_f32(dst[e]);
-    scale = 1.f;
-  } else if (PG == 4) {
-    const float *src = a.q_r + (int64_t)m * a.n_h * a.d_rope + h * a.d_rope + 2 * p0;
-    const float4 lo = *(const float4 *)src, hi = *(const float4 *)(src + 4);
-    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-  } else {
-    const float *src = a.q_r + (int64_t)m * a.n_h * a.d_rope + h * a.d_rope + 2 * p0;
-#pragma unroll
-    for (int e = 0; e < 2 * PG; ++e) v[e] = src[e];
-  }
-#pragma unroll
-  for (int q = 0; q < PG; ++q) {
-    rope_rotate(v[2 * q], v[2 * q + 1], pos[a.rope.axis[p0 + q]], a.rope.omega[p0 + q]);
-    dst[2 * q] = from_f32<OutT>(v[2 * q] * scale);
-    dst[2 * q + 1] = from_f32<OutT>(v[2 * q + 1] * scale);
-  }
+  rope_q_item<OutT, PG>(a, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 template <typename T>
@@ -121,8 +89,7 @@ hipError_t rmsnorm_rows(const float *in, const void *g, void *out, int rows, int
 hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st) {
   const int P = a.d_rope / 2;
   const bool by4 = P % 4 == 0;  // q^R rows are 16-byte aligned when d_rope % 8 == 0
-  int64_t total = (int64_t)a.M * a.n_h * (by4 ? P / 4 : P);
-  if (a.n_zero > total) total = a.n_zero;
+  const int64_t total = rope_q_items(a, by4 ? 4 : 1);
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
   if (bf16_out && by4)

@@ -540,7 +540,7 @@ int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &
   float *u_q = (float *)(ws + L.u_q);
   void *c_q = ws + L.c_q, *q_nope = ws + L.q_nope, *w_t = ws + L.w_t;
   float *q_r = (float *)(ws + L.q_r);
-  unsigned char *q_lat = ws + L.q_lat, *o_lat = ws + L.o_lat;
+  unsigned char *q_lat = ws + L.q_lat;
 
   if (w.w_qlat && bf) {
     // c^Q = RMSNorm(W^Q_down x) * g_q (Eq. 3, App. D.2) taken apart over the two GEMMs:

@@ -678,13 +678,19 @@ int run_step(const mla_config &c, const mla_weights &w, const mla_chunk &k, cons
   std::memset(&rq_shape, 0, sizeof(rq_shape));
   rq_shape.in_place = w.w_qlat != nullptr;
   rq_shape.d_rope = c.d_rope;
-  const bool fused = c.dtype == MLA_BF16 && mla::cache_write_takes_rope(cw, rq_shape);
+  // Fused only where the CUs the write leaves idle can take the RoPE items at no more
+  // than 8 per thread (each item is a dependent read-modify-write, so a thread's
+  // items run one after another): the single-request chunk, not batches or clips.
+  const int cw_blocks = (int)((d.M + 31) / 32), cus = attn_grid_cus();
+  const int64_t rope_items = d.M * c.n_heads * (c.d_rope / 8);
+  const int64_t wg_threads = 2 * (c.d_c + c.d_rope);  // the cache write's workgroup: 64 * N / 32
+  const int64_t rope_needed = (rope_items + 8 * wg_threads - 1) / (8 * wg_threads);
+  const bool fused = c.dtype == MLA_BF16 && mla::cache_write_takes_rope(cw, rq_shape) &&
+                     cw_blocks + rope_needed <= cus;
   if (fused) {
     mla::RopeQArgs rq;
     MLA_TRY(prepare_queries(c, w, k, x, ws, st, false, &rq));
-    const int cw_blocks = (int)((d.M + 31) / 32), cus = attn_grid_cus();
-    const int rope_blocks = cus - cw_blocks > 16 ? cus - cw_blocks : 16;
-    MLA_HIP(mla::cache_write_bf16_rope(cw, rq, rope_blocks, st), "cache write with query rope");
+    MLA_HIP(mla::cache_write_bf16_rope(cw, rq, cus - cw_blocks, st), "cache write with query rope");
   } else {
     MLA_TRY(run_cache_write(c, w, k, x, cache, st));
     MLA_TRY(prepare_queries(c, w, k, x, ws, st, true, nullptr));

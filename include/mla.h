@@ -252,8 +252,9 @@ int mla_chunk_attention(const mla_config *cfg, const mla_weights *w, const mla_c
  * One layer's chunk step: the work of mla_cache_write, then mla_chunk_attention,
  * then the output projection y = W_O out_heads (§3.3).  Parts that do not depend on
  * each other may run in another order or share a launch (with the absorbed bf16
- * query, the query GEMMs run first and the query's RoPE pass rides in the cache
- * write's launch); the cache write always precedes the attention.  With w->w_b set, the value
+ * query, the query GEMMs run first and the cache write shares a launch with the
+ * query GEMM or with the query's RoPE pass); the cache write always precedes the
+ * attention.  With w->w_b set, the value
  * up-projection and W_O are replaced by y = sum_h B_h O_lat,h (App. E Eq. 10-11),
  * one GEMM over the n_h * d_c latent outputs; the result is the same up to
  * rounding.

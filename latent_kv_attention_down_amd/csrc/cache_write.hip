@@ -10,6 +10,7 @@
 #include "mla_device.h"
 #include "mla_launch.h"
 #include "rope_q_item.h"
+#include "gemm_tile.h"
 
 namespace mla {
 namespace {
@@ -280,17 +281,26 @@ __global__ __launch_bounds__(64 * (N / 32)) void k_cache_write_bf16(CacheWriteAr
 // conflicts; the swizzle is applied on the global side of each load.  The RoPE
 // cos/sin of the workgroup's (token, pair)s are computed by all threads while the
 // first stages are in flight.  The finish is that of k_cache_write_bf16.
-template <int N>
+template <int N, int BM = kBM>
 struct CwDma {
   static constexpr int NWAVE = N / 32, NT = 64 * NWAVE;
   static constexpr int KC = 64;                         // k per stage
-  static constexpr int NS = N <= 256 ? 4 : 3;           // stages
-  static constexpr int XB = kBM * KC * 2;               // x bytes per stage
+  static constexpr int XB = BM * KC * 2;                // x bytes per stage
   static constexpr int WB = N * KC * 2;                 // weight bytes per stage
   static constexpr int SB = XB + WB;
   static constexpr int MAX_PAIRS = 32;
-  static constexpr size_t LDS = (size_t)SB * NS + (size_t)kBM * MAX_PAIRS * 8;
-  static_assert(NWAVE >= 4, "waves 0-3 load the x rows");
+  static constexpr int RTAB = BM * MAX_PAIRS * 8;       // (cos, sin) of the tile's pairs
+  static constexpr int NS_MAX = N <= 256 ? 4 : 3;
+  static constexpr int NS = SB * NS_MAX + RTAB <= 163840 ? NS_MAX
+                          : SB * (NS_MAX - 1) + RTAB <= 163840 ? NS_MAX - 1 : 2;  // stages
+  static constexpr size_t LDS = (size_t)SB * NS + RTAB;
+  static constexpr int RT = BM / 16;                    // 16-row MFMA tiles
+  static constexpr int XR = BM / 8;                     // x load instructions per stage
+  static constexpr int XW = XR <= NWAVE ? XR : (XR % NWAVE == 0 ? NWAVE : XR / 2);  // loading waves
+  static constexpr int XQ = XR / XW;                    // ... and instructions each
+  static_assert(BM % 16 == 0 && XW * XQ == XR && XW <= NWAVE, "x rows split evenly over waves");
+  static_assert(LDS <= 163840, "LDS");
+  static_assert(NWAVE >= 4, "at least four waves");
 };
 
 __device__ __forceinline__ int cw_swz(int row) { return (row >> 1) & 7; }
@@ -307,27 +317,30 @@ __device__ __forceinline__ void wait_stage(int after) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int N>
+// One workgroup's tile: BM tokens, all N columns (32 by default; taller tiles let
+// fewer workgroups cover the chunk, for a launch beside other work).
+template <int N, int BM = kBM>
 __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, int block) {
-  using C = CwDma<N>;
-  constexpr int NT = C::NT, KC = C::KC, NS = C::NS, NWAVE = C::NWAVE;
+  using C = CwDma<N, BM>;
+  constexpr int NT = C::NT, KC = C::KC, NS = C::NS, NWAVE = C::NWAVE, RT = C::RT, XQ = C::XQ;
   constexpr int LDT = N + 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   typedef __attribute__((address_space(3))) void lds_void;
-  float2 *rtab = (float2 *)(smem + (size_t)C::SB * NS);  // [kBM][n_pairs]: (cos, sin)
+  float2 *rtab = (float2 *)(smem + (size_t)C::SB * NS);  // [BM][n_pairs]: (cos, sin)
   bf16 *tileo = (bf16 *)smem;                             // after the k loop
-  float *ssum = (float *)(smem + kBM * LDT * 2);          // [NWAVE][kBM]
-  float *sinv = ssum + NWAVE * kBM;                       // [kBM]
+  float *ssum = (float *)(smem + BM * LDT * 2);           // [NWAVE][BM]
+  float *sinv = ssum + NWAVE * BM;                        // [BM]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kg = lane >> 4;
-  const int m0 = block * kBM;
+  const int m0 = block * BM;
   const int nk = a.d / KC;
   const int np = a.d_rope / 2;
 
   // sources of this lane's loads: load i of wave w fills stage rows 8i + lane/8 of
-  // the wave's weight rows (and, for waves 0-3, x rows 8w + lane/8), slot lane%8
+  // the wave's weight rows (and, for waves below XW, x rows 8(w XQ + q) + lane/8),
+  // slot lane%8
   const int slot = lane & 7, rsub = lane >> 3;
   const bf16 *wsrc[4];
 #pragma unroll
@@ -337,17 +350,21 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
                                  : (const bf16 *)a.w_kr + (int64_t)(n - a.d_c) * a.d;
     wsrc[i] = base + (slot ^ cw_swz(row)) * 8;
   }
-  const bool xload = wave < 4;
-  const bf16 *xsrc = (const bf16 *)a.x;
-  if (xload) {
-    const int row = 8 * wave + rsub, gm = min(m0 + row, a.M - 1);  // rows past M: any valid row
-    xsrc += (int64_t)gm * a.d + (slot ^ cw_swz(row)) * 8;
+  const bool xload = wave < C::XW;
+  const bf16 *xsrc[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int row = 8 * (wave * XQ + q) + rsub, gm = min(m0 + row, a.M - 1);  // past M: any valid row
+    xsrc[q] = (const bf16 *)a.x + (int64_t)gm * a.d + (slot ^ cw_swz(row)) * 8;
   }
   auto issue = [&](int kc) {
     unsigned char *st = smem + (size_t)(kc % NS) * C::SB;
     const int k0 = kc * KC;
     if (xload)
-      __builtin_amdgcn_global_load_lds((const void *)(xsrc + k0), (lds_void *)(st + wave * 1024), 16, 0, 0);
+#pragma unroll
+      for (int q = 0; q < XQ; ++q)
+        __builtin_amdgcn_global_load_lds((const void *)(xsrc[q] + k0),
+                                         (lds_void *)(st + (wave * XQ + q) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_global_load_lds((const void *)(wsrc[i] + k0),
@@ -358,7 +375,7 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
     if (kc < nk) issue(kc);
 
   // RoPE table of this workgroup's tokens (keys kept unrotated need none)
-  for (int e = tid; a.rotate && e < kBM * np; e += NT) {
+  for (int e = tid; a.rotate && e < BM * np; e += NT) {
     const int t = e / np, p = e % np, m = m0 + t, ti = m % a.T_q, n = ti % a.tpf;
     const int ax = a.rope.axis[p];
     const double om = a.rope.omega[p];
@@ -368,15 +385,15 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
     rtab[e] = make_float2(cs, sn);
   }
 
-  f32x4 acc[2][2];
+  f32x4 acc[RT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int kc = 0; kc < nk; ++kc) {
     const int after = min(NS - 2, nk - 1 - kc);
     if (xload)
-      wait_stage<5>(after);
+      wait_stage<4 + XQ>(after);
     else
       wait_stage<4>(after);
     __syncthreads();
@@ -385,17 +402,18 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
     const unsigned char *sw = st + C::XB + wave * 4096;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 xa[2], wb[2];
+      bf16x8 wb[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = 16 * h + l16, ch = (4 * s + kg) ^ cw_swz(row);
-        xa[h] = *(const bf16x8 *)(st + row * 128 + ch * 16);
         wb[h] = *(const bf16x8 *)(sw + row * 128 + ch * 16);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[0][j] = mfma16(xa[0], wb[j], acc[0][j]);
-        acc[1][j] = mfma16(xa[1], wb[j], acc[1][j]);
+      for (int i = 0; i < RT; ++i) {
+        const int row = 16 * i + l16, ch = (4 * s + kg) ^ cw_swz(row);
+        const bf16x8 xa = *(const bf16x8 *)(st + row * 128 + ch * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(xa, wb[j], acc[i][j]);
       }
     }
   }
@@ -405,17 +423,17 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
   __syncthreads();  // stages no longer read
   if (latent) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float q = row16_sum(acc[i][0][r] * acc[i][0][r] + acc[i][1][r] * acc[i][1][r]);
-        if (l16 == 0) ssum[wave * kBM + i * 16 + (lane >> 4) * 4 + r] = q;
+        if (l16 == 0) ssum[wave * BM + i * 16 + (lane >> 4) * 4 + r] = q;
       }
   }
   __syncthreads();
-  if (tid < kBM) {
+  if (tid < BM) {
     float q = 0.f;
-    for (int w = 0; w < a.d_c / 32; ++w) q += ssum[w * kBM + tid];
+    for (int w = 0; w < a.d_c / 32; ++w) q += ssum[w * BM + tid];
     sinv[tid] = 1.0f / sqrtf(q / (float)a.d_c + a.eps);
   }
   __syncthreads();
@@ -426,7 +444,7 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
       const int col = wave * 32 + j * 16 + l16;
       const float gain = gk ? to_f32(gk[col]) : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = i * 16 + (lane >> 4) * 4 + r;
@@ -440,7 +458,7 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
     for (int j = 0; j < 2; ++j) {
       const int col = wave * 32 + j * 16 + l16, p = (col - a.d_c) >> 1;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = i * 16 + (lane >> 4) * 4 + r;
@@ -453,7 +471,7 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
     }
   }
   __syncthreads();
-  for (int id = tid; id < kBM * (N / 8); id += NT) {
+  for (int id = tid; id < BM * (N / 8); id += NT) {
     const int r = id / (N / 8), c8 = (id % (N / 8)) * 8, m = m0 + r;
     if (m < a.M) *(bf16x8 *)ring_elem<bf16>(a, m, c8) = *(const bf16x8 *)(tileo + r * LDT + c8);
   }
@@ -494,6 +512,28 @@ hipError_t launch_dma_rope(const CacheWriteArgs &a, const RopeQArgs &r, int rope
   hipLaunchKernelGGL(k_cache_write_dma_rope<N>, dim3(cw + rope_blocks), dim3(C::NT), C::LDS, st, a,
                      r, cw);
   return hipGetLastError();
+}
+
+// The step's absorbed query GEMM (256x256 tiles whose rows are scaled by their RMS)
+// with the cache write of the same step in one launch: the GEMM's 209 tiles leave 47
+// of 256 CUs idle for its ~32 us, and the write, in tiles of kBMQ tokens (42 at the
+// Wan-1.3B chunk, each ~1 MB of weights and x), fits beside it.  Workgroups below
+// g_tiles run GEMM tiles with the numbering of the GEMM's own launch (so the same
+// XCD-aware tile order); the rest write the cache with the first N/32 of their waves
+// (the others end at once; barriers wait only for waves still running).  The jobs
+// share no data.
+constexpr int kBMQ = 112;
+using QueryTile = GemmDma<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS>;
+
+template <int N>
+__global__ __launch_bounds__(QueryTile::NT) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void k_query_gemm_cache_write(GemmArgs g, int g_nbx, int g_tiles, CacheWriteArgs a) {
+  if ((int)blockIdx.x < g_tiles) {
+    gemm_dma_tile<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS>(g, blockIdx.x, g_nbx, g_tiles, 0);
+    return;
+  }
+  if ((int)threadIdx.x >= CwDma<N, kBMQ>::NT) return;
+  cache_write_dma_block<N, kBMQ>(a, blockIdx.x - g_tiles);
 }
 
 template <int N>
@@ -563,6 +603,29 @@ hipError_t cache_write_bf16(const CacheWriteArgs &a, hipStream_t st) {
     case 288: return launch_bf16<288>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+int query_gemm_cache_write_blocks(const GemmArgs &g, const CacheWriteArgs &a) {
+  if (a.M <= 0 || a.d_c + a.d_rope != 224 || a.d % CwDma<224>::KC != 0 ||
+      a.d_rope / 2 > CwDma<224>::MAX_PAIRS)
+    return 0;
+  if (g.batch != 1 || !g.ssq_in || g.ssq_out || g.N < 512 || g.K % 64 != 0) return 0;
+  const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  if (tiles < 200) return 0;  // the GEMM would not take 256x256 tiles
+  return tiles + (a.M + kBMQ - 1) / kBMQ;
+}
+
+hipError_t query_gemm_cache_write(const GemmArgs &g, const CacheWriteArgs &a, hipStream_t st) {
+  const int total = query_gemm_cache_write_blocks(g, a);
+  if (total <= 0) return hipErrorInvalidValue;
+  const int nbx = (g.N + 255) / 256, tiles = nbx * ((g.M + 255) / 256);
+  const size_t lds = QueryTile::LDS > CwDma<224, kBMQ>::LDS ? QueryTile::LDS : CwDma<224, kBMQ>::LDS;
+  hipError_t e = hipFuncSetAttribute((const void *)k_query_gemm_cache_write<224>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_query_gemm_cache_write<224>, dim3(total), dim3(QueryTile::NT), lds, st, g, nbx,
+                     tiles, a);
+  return hipGetLastError();
 }
 
 bool cache_write_takes_rope(const CacheWriteArgs &a, const RopeQArgs &r) {

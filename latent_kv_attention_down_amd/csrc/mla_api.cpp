@@ -528,10 +528,14 @@ int run_gemm(const mla_config &c, const mla::GemmArgs &g, bool out_f32, hipStrea
   } while (0)
 
 // Query preparation (Eq. 3-4, 6; App. E Eq. 8-9): the absorbed query rows in the
-// workspace.  The RoPE pass (its arguments in *rq) is launched here unless the caller
-// takes it over (launch_rope false: the step runs it inside the cache write's launch).
+// workspace.  The RoPE pass (its arguments in *rq_out) is launched here unless the
+// caller takes it over (launch_rope false).  With `ride` (a cache write of the same
+// step), the absorbed query GEMM and that write share one launch where they fit
+// (*rode then says so).
 int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
-                    unsigned char *ws, hipStream_t st, bool launch_rope, mla::RopeQArgs *rq_out) {
+                    unsigned char *ws, hipStream_t st, bool launch_rope, mla::RopeQArgs *rq_out,
+                    const mla::CacheWriteArgs *ride = nullptr, bool *rode = nullptr) {
+  if (rode) *rode = false;
   const Dims d = dims(c, k);
   const Workspace L = carve(c, k);
   const bool bf = c.dtype == MLA_BF16;
@@ -561,7 +565,13 @@ int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &
     g2.ssq_parts = (c.d_q + 63) / 64;
     g2.ssq_scale = 1.0f / (float)c.d_q;
     g2.ssq_eps = c.rms_eps;
-    MLA_TRY(run_gemm(c, g2, false, st, "absorbed query projection"));
+    const int both = ride ? mla::query_gemm_cache_write_blocks(g2, *ride) : 0;
+    if (both > 0 && both <= attn_grid_cus()) {
+      MLA_HIP(mla::query_gemm_cache_write(g2, *ride, st), "absorbed query projection with cache write");
+      if (rode) *rode = true;
+    } else {
+      MLA_TRY(run_gemm(c, g2, false, st, "absorbed query projection"));
+    }
   } else {
     // c^Q = RMSNorm(W^Q_down x)  (Eq. 3, App. D.2)
     MLA_TRY(run_gemm(c, gemm(x, c.d_model, 0, w.w_q_down, c.d_model, 0, u_q, c.d_q, 0, d.M, c.d_q,
@@ -674,23 +684,29 @@ int run_step(const mla_config &c, const mla_weights &w, const mla_chunk &k, cons
   const Workspace L = carve(c, k);
   const Dims d = dims(c, k);
   const mla::CacheWriteArgs cw = cache_write_args(c, w, k, x, cache);
-  mla::RopeQArgs rq_shape;
-  std::memset(&rq_shape, 0, sizeof(rq_shape));
-  rq_shape.in_place = w.w_qlat != nullptr;
-  rq_shape.d_rope = c.d_rope;
-  // Fused only where the CUs the write leaves idle can take the RoPE items at no more
-  // than 8 per thread (each item is a dependent read-modify-write, so a thread's
-  // items run one after another): the single-request chunk, not batches or clips.
+  // Where they fit, the cache write shares the absorbed query GEMM's launch (the GEMM
+  // leaves 47 of 256 CUs idle at the Wan-1.3B chunk); otherwise the query's RoPE pass
+  // shares the cache write's launch, fused only where the CUs the write leaves idle can
+  // take the RoPE items at no more than 8 per thread (each item is a dependent
+  // read-modify-write, so a thread's items run one after another): the single-request
+  // chunk, not batches or clips.
   const int cw_blocks = (int)((d.M + 31) / 32), cus = attn_grid_cus();
   const int64_t rope_items = d.M * c.n_heads * (c.d_rope / 8);
   const int64_t wg_threads = 2 * (c.d_c + c.d_rope);  // the cache write's workgroup: 64 * N / 32
   const int64_t rope_needed = (rope_items + 8 * wg_threads - 1) / (8 * wg_threads);
-  const bool fused = c.dtype == MLA_BF16 && mla::cache_write_takes_rope(cw, rq_shape) &&
-                     cw_blocks + rope_needed <= cus;
-  if (fused) {
+  const bool absorbed_bf16 = c.dtype == MLA_BF16 && w.w_qlat;
+  if (absorbed_bf16) {
     mla::RopeQArgs rq;
-    MLA_TRY(prepare_queries(c, w, k, x, ws, st, false, &rq));
-    MLA_HIP(mla::cache_write_bf16_rope(cw, rq, cus - cw_blocks, st), "cache write with query rope");
+    bool rode = false;
+    MLA_TRY(prepare_queries(c, w, k, x, ws, st, false, &rq, &cw, &rode));
+    if (rode) {
+      MLA_HIP(mla::rope_q(rq, true, st), "query rope");
+    } else if (mla::cache_write_takes_rope(cw, rq) && cw_blocks + rope_needed <= cus) {
+      MLA_HIP(mla::cache_write_bf16_rope(cw, rq, cus - cw_blocks, st), "cache write with query rope");
+    } else {
+      MLA_TRY(run_cache_write(c, w, k, x, cache, st));
+      MLA_HIP(mla::rope_q(rq, true, st), "query rope");
+    }
   } else {
     MLA_TRY(run_cache_write(c, w, k, x, cache, st));
     MLA_TRY(prepare_queries(c, w, k, x, ws, st, true, nullptr));

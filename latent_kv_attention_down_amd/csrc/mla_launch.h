@@ -81,11 +81,13 @@ hipError_t rope_q(const RopeQArgs &a, bool bf16_out, hipStream_t st);
 bool cache_write_takes_rope(const CacheWriteArgs &a, const RopeQArgs &r);
 hipError_t cache_write_bf16_rope(const CacheWriteArgs &a, const RopeQArgs &r, int rope_blocks,
                                  hipStream_t st);
-// The absorbed query GEMM g (bf16, rows scaled by ssq_in, 256x256 tiles) and the
-// bf16 cache write a in one launch.  query_gemm_cache_write_blocks: the launch's
+// The absorbed query GEMM g (bf16, rows scaled by ssq_in, 256x256 tiles) with the
+// in-place query RoPE r done in its tiles, and the bf16 cache write a, in one launch
+// (r's flags are cleared on the way).  query_gemm_cache_write_blocks: the launch's
 // workgroups, or 0 where the pair does not apply (then run them apart).
 int query_gemm_cache_write_blocks(const GemmArgs &g, const CacheWriteArgs &a);
-hipError_t query_gemm_cache_write(const GemmArgs &g, const CacheWriteArgs &a, hipStream_t st);
+hipError_t query_gemm_cache_write(const GemmArgs &g, const CacheWriteArgs &a, const RopeQArgs &r,
+                                  hipStream_t st);
 
 // Window assembly: context frame i (the n_sink sink frames, then frames
 // first_local, first_local+1, ...) is copied from its ring slot to rows i*tpf .. of

@@ -337,9 +337,10 @@ int mla_attention_grid(const mla_config *cfg, const mla_chunk *chunk);
 
 /* Where the bf16 attention leaves its overflow flags in the workspace: *offset
  * (bytes from the workspace start) and *count int32 flags, one per row tile of
- * the fast kernel.  After a call, a nonzero flag means that row tile's scores
- * rose more than 64 (base 2) above its first key tile's maximum, so the safe
- * path recomputed it (exact either way).  Host-only; MLA_OK, or INVALID_ARG for
+ * the fast kernel.  After a call, a nonzero flag means that some of that row
+ * tile's scores rose more than 64 (base 2) above the maximum of the first key
+ * tile a workgroup saw for it, so the attention kernel recomputed that
+ * workgroup's part of the row tile against the exact maximum (exact either way).  Host-only; MLA_OK, or INVALID_ARG for
  * an invalid cfg/chunk or NULL outputs; *count = 0 on the fp32 path. */
 int mla_overflow_flags(const mla_config *cfg, const mla_chunk *chunk, size_t *offset,
                        int64_t *count);

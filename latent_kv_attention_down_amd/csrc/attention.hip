@@ -33,11 +33,11 @@
 //  * fast path: each row's softmax reference is the max of the first key tile the
 //    workgroup sees for it and is never moved, so O is never rescaled inside the
 //    loop (a rescale would drag the AGPR-resident accumulators through VGPRs).
-//    Any row whose later scores exceed the reference by more than 64 (base 2) has
-//    its row tile flagged (a lower bound can be set to exercise this on ordinary
-//    data), and the safe kernel (reference raised lazily, O rescaled) recomputes
-//    exactly those row tiles.  Below that bound every weight
-//    is at most 2^64, far inside fp32 and bf16 range;
+//    If a row's later scores exceed the reference by more than 64 (base 2), the
+//    workgroup recomputes that piece at once with the classic online softmax
+//    (reference following the running max, O rescaled) and flags the row tile (a
+//    lower bound can be set to exercise this on ordinary data).  Below that bound
+//    every weight is at most 2^64, far inside fp32 and bf16 range;
 //  * the fast grid is persistent: workgroup g takes the flat range
 //    [gT/G, (g+1)T/G) of T = (row tiles) x (key tiles) tile steps, so every CU gets
 //    the same work.  A row tile finished by one workgroup is written directly; one
@@ -58,7 +58,6 @@ constexpr float kFastSumLimit = 1.8446744e19f;  // 2^64: weights above it fall b
 // Word 3 of a gfx9 buffer descriptor for raw byte-addressed loads (no format
 // conversion, stride 0).
 constexpr int kBufferConfig = 0x00020000;
-constexpr float kSafeThreshold = 8.f;  // lazy rescale threshold of the safe kernel
 
 // Work of one launch.  The rows of a request form nblk blocks of blk_rows rows
 // (one block, all R rows, without a causal mask); block k attends the first
@@ -126,29 +125,6 @@ __host__ __device__ __forceinline__ int rt_of(const Sched &s, int64_t f) {
   return b * s.RTb + k * s.blk_rt + (int)(r / blk_kt(s, k));
 }
 
-// Configuration of the safe kernel: DC/DR latent and RoPE widths, QT 32-row query
-// tiles per wave, NW waves per workgroup, one padded LDS stage of one key tile
-// (rows padded by PAD_ elements), filled through registers.
-template <int DC_, int DR_, int QT_, int NW_, int PAD_ = 8>
-struct Cfg {
-  static constexpr int DC = DC_, DR = DR_, QT = QT_, NW = NW_;
-  static constexpr int NBUF = 1;
-  static constexpr int NT = NW * 64;
-  static constexpr int DK = DC + DR;
-  static constexpr int KB = DK / 16;
-  static constexpr int FT = DC / 32;
-  static constexpr int RW = NW * QT * 32;
-  static constexpr int KS = DK + PAD_;        // LDS row stride (elements) of the key tile
-  static_assert(PAD_ % 8 == 0, "rows must stay 16-byte aligned");
-  static constexpr int CPR = DK / 8;          // 16-byte chunks per ring row
-  static constexpr int CHUNKS = BN * CPR;     // chunks per key tile
-  static constexpr int CH_PER_T = (CHUNKS + NT - 1) / NT;
-  static constexpr int STAGE = BN * KS;       // elements per LDS stage
-  static constexpr size_t LDS = (size_t)STAGE * 2 * NBUF;
-  static_assert(NW % 4 == 0, "whole waves per SIMD");
-  static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
-};
-
 // One wave per SIMD, QT x 32 query rows per wave, key tiles brought into an unpadded
 // swizzled four-stage LDS ring by buffer loads into LDS (k_latent_attn_w1).
 template <int DC_, int DR_, int QT_ = 2, bool BUILTIN_ = false>
@@ -177,12 +153,11 @@ struct CfgW {
   static_assert(DK % 16 == 0 && DC % 32 == 0, "bad widths");
 };
 
-// Production configuration per (d_c, d_rope), and the safe-path configuration.
+// Production configuration per (d_c, d_rope).
 template <int DC, int DR>
 struct Choice {
   using Fast = CfgW<DC, DR>;
   using FastBuiltin = CfgW<DC, DR, 2, true>;
-  using Safe = Cfg<DC, DR, 1, 4>;
 };
 // At d_c = 256 the 64-row O^T alone needs all 256 accumulation registers, so the
 // one-wave kernel takes 32 rows per wave there.
@@ -190,183 +165,7 @@ template <>
 struct Choice<256, 32> {
   using Fast = CfgW<256, 32, 1>;
   using FastBuiltin = CfgW<256, 32, 1, true>;
-  using Safe = Cfg<256, 32, 1, 4>;
 };
-
-// One workgroup's view of the ring: global -> registers -> LDS (one key-major tile
-// of BN ring rows), and the two MFMA contractions of a key tile.  The score
-// contraction reads 16-byte K fragments (lane: key l32, features 8g..8g+7); the
-// value contraction reads V^T fragments from the same tile with the gfx950 LDS
-// transpose load ds_read_b64_tr_b16, which hands each lane one feature of four
-// consecutive keys, so no transposed copy of the latent is ever written.
-template <class C>
-struct Tile {
-  static constexpr int DC = C::DC, DR = C::DR, QT = C::QT, NT = C::NT;
-  static constexpr int DK = C::DK, KB = C::KB, FT = C::FT, KS = C::KS, CPR = C::CPR;
-  bf16 *base;      // LDS stage(s)
-  const bf16 *cb;  // this request's ring
-  int nk, start0, len0;
-  uint4 reg[C::CH_PER_T];
-
-  __device__ __forceinline__ bf16 *Ks(int buf) const { return base + buf * C::STAGE; }
-
-  __device__ __forceinline__ int64_t key_row(int kk) const {
-    return kk < len0 ? (int64_t)(start0 + kk) : (int64_t)(kk - len0);
-  }
-
-  // Global loads of tile kt into registers: chunk c = tid + NT*i is 16 bytes of
-  // key c / CPR at feature 8 * (c % CPR); consecutive lanes read consecutive bytes.
-  __device__ __forceinline__ void load(int kt, int tid) {
-    const int k0 = kt * BN;
-    const bool contiguous = (k0 + BN <= nk) && (k0 + BN <= len0 || k0 >= len0);
-    if (contiguous) {
-      const bf16 *tb = cb + key_row(k0) * DK;
-#pragma unroll
-      for (int i = 0; i < C::CH_PER_T; ++i) {
-        const int c = tid + NT * i;
-        if (C::CHUNKS % NT == 0 || c < C::CHUNKS) reg[i] = *(const uint4 *)(tb + c * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::CH_PER_T; ++i) {
-        const int c = tid + NT * i;
-        if (C::CHUNKS % NT == 0 || c < C::CHUNKS) {
-          const int kk = k0 + c / CPR;
-          reg[i] = kk < nk ? *(const uint4 *)(cb + key_row(kk) * DK + (c % CPR) * 8)
-                           : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(int tid, int buf) {
-    bf16 *ks = Ks(buf);
-#pragma unroll
-    for (int i = 0; i < C::CH_PER_T; ++i) {
-      const int c = tid + NT * i;
-      if (C::CHUNKS % NT == 0 || c < C::CHUNKS)
-        *(uint4 *)(ks + (c / CPR) * KS + (c % CPR) * 8) = reg[i];
-    }
-  }
-
-  // S^T (keys x queries) for the 64 keys of tile kt; masked keys get -inf.
-  __device__ __forceinline__ void scores(f32x16 (&S)[2][QT], const bf16x8 (&Qr)[QT][KB], int kt,
-                                         int buf, int l32, int g) const {
-    const bf16 *ks = Ks(buf);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[t][qt][r] = 0.f;
-    // Fragments of k-block kb+1 are read before the MFMAs of k-block kb, so each
-    // LDS read has a k-block of MFMA work to hide behind.
-    const bf16 *kr = ks + l32 * KS + g * 8;
-    bf16x8 fr[2][2];  // [k-block parity][key half]
-#pragma unroll
-    for (int t = 0; t < 2; ++t) fr[0][t] = *(const bf16x8 *)(kr + t * 32 * KS);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (kb + 1 < KB) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          fr[(kb + 1) & 1][t] = *(const bf16x8 *)(kr + t * 32 * KS + (kb + 1) * 16);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) S[t][qt] = mfma32(fr[kb & 1][t], Qr[qt][kb], S[t][qt]);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * QT, 0);
-    }
-    if ((kt + 1) * BN > nk) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * BN + t * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          if (key >= nk)
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) S[t][qt][r] = -INFINITY;
-        }
-    }
-  }
-
-  // O^T (features x queries) += V^T P^T over the tile's four 16-key blocks.  For
-  // block kb the A operand of lane l (16-lane group G = l/16, r = l%16) must hold
-  // feature ft*32 + l%32 of keys kb*16 + 4g + j (slots 0-3) and kb*16 + 8 + 4g + j
-  // (slots 4-7).  ds_read_b64_tr_b16 gives lane r of a 16-lane group element r%4 of
-  // the 8-byte chunks addressed by lanes r/4 + 4j, so lane r addresses key
-  // kb*16 + 8h + 4g + r/4 at feature ft*32 + 16*(G%2) + 4*(r%4).
-  __device__ __forceinline__ void values(f32x16 (&O)[FT][QT], const bf16x8 (&P)[BN / 16][QT],
-                                         int buf, int lane) const {
-    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-    const int G = lane >> 4, r = lane & 15, g = lane >> 5;
-    const bf16 *vt = Ks(buf) + (4 * g + (r >> 2)) * KS + 16 * (G & 1) + 4 * (r & 3);
-    auto frag = [&](int i) {  // block i = ft * (BN/16) + kb
-      const bf16 *p0 = vt + ((i % (BN / 16)) * 16) * KS + (i / (BN / 16)) * 32;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)p0);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(__attribute__((address_space(3))) bf16 *)(p0 + 8 * KS));
-      return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    constexpr int NB = FT * (BN / 16);
-    bf16x8 fr[2];  // ping-pong: the next fragment is read before this MFMA
-    fr[0] = frag(0);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (i + 1 < NB) fr[(i + 1) & 1] = frag(i + 1);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        O[i / (BN / 16)][qt] = mfma32(fr[i & 1], P[i % (BN / 16)][qt], O[i / (BN / 16)][qt]);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
-    }
-  }
-};
-
-// Probabilities of one query tile as bf16 B operands: slot e of block 2t+h holds
-// key t*32 + 16h + 4g + e, slot 4+e key t*32 + 16h + 8 + 4g + e (the MFMA output
-// rows of S^T), matching the V^T fragments read in Tile::values.
-template <int QT>
-__device__ __forceinline__ float exp_and_pack(f32x16 (&S)[2][QT], bf16x8 (&P)[BN / 16][QT], int qt,
-                                              float m) {
-  float ls = 0.f;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(S[t][qt][r] - m);
-      S[t][qt][r] = p;
-      ls += p;
-    }
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pv[e] = (bf16)S[t][qt][(2 * h) * 4 + e];
-        pv[4 + e] = (bf16)S[t][qt][(2 * h + 1) * 4 + e];
-      }
-      P[2 * t + h][qt] = pv;
-    }
-  return ls;
-}
-
-template <int QT>
-__device__ __forceinline__ float tile_max(const f32x16 (&S)[2][QT], int qt) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[t][qt][r]);
-  return fmaxf(mx, __shfl_xor(mx, 32, 64));
-}
 
 template <int DK, int QT, int KB>
 __device__ __forceinline__ void load_queries(bf16x8 (&Qr)[QT][KB], const bf16 *q, const Sched &s,
@@ -385,21 +184,6 @@ __device__ __forceinline__ void load_queries(bf16x8 (&Qr)[QT][KB], const bf16 *q
       }
     }
   }
-}
-
-// Normalise and store 32 rows x DC: lane holds row l32, features ft*32 + 8i + 4g + j.
-template <int FT, int QT>
-__device__ __forceinline__ void store_rows(bf16 *dst, const f32x16 (&O)[FT][QT], int qt, float inv,
-                                           int g) {
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16 v4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v4[j] = (bf16)(O[ft][qt][4 * i + j] * inv);
-      *(uint2 *)(dst + ft * 32 + i * 8 + g * 4) = *(const uint2 *)v4;
-    }
 }
 
 // The same values into an LDS image of the wave's rows (row-major, DC wide), 16-byte
@@ -727,6 +511,65 @@ __device__ __forceinline__ void wait_loads() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Exact recomputation of one piece (key tiles kt0 .. kt1-1 of a row tile) for the
+// workgroup's rows, taken only when the fast pass over that piece overflowed.  Two
+// passes, one key tile at a time through stage 0: the first takes each row's true
+// maximum score over the piece, the second the softmax against it, so every weight
+// is at most 1 and O is never rescaled.  Leaves O, m and l as the fast pass would
+// (O unnormalised, l the lane's partial row sum).  Every wave of the workgroup
+// takes it together (it has barriers); on entry every wave is done with the LDS
+// stages.
+template <class C>
+__device__ __forceinline__ void safe_piece(const TileW<C> &tl, __amdgpu_buffer_rsrc_t rs,
+                                           const bf16x8 (&Qr)[C::QT][C::KB],
+                                           f32x16 (&O)[C::FT][C::QT], float (&m)[C::QT],
+                                           float (&l)[C::QT], int kt0, int kt1, int last_kt,
+                                           int nk, int lane, int l32, int g) {
+  constexpr int QT = C::QT, FT = C::FT;
+  f32x16 S0[QT], S1[QT];
+  const f32x16 zero[QT] = {};
+  // scores of tile kt, both halves, keys past nk at -inf
+  auto tile_scores = [&](int kt) {
+    tl.load(rs, kt, 0);
+    wait_loads<0>();
+    __syncthreads();
+    tl.template scores<0, true>(S0, Qr, zero, 0, l32, g, [](int) {});
+    tl.template scores<1, true>(S1, Qr, zero, 0, l32, g, [](int) {});
+    if (kt == last_kt) {
+      mask_half<QT>(S0, kt * BN, nk, g);
+      mask_half<QT>(S1, kt * BN + 32, nk, g);
+    }
+  };
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) m[qt] = -INFINITY;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    tile_scores(kt);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m[qt] = fmaxf(m[qt], fmaxf(S0[qt][r], S1[qt][r]));
+    // every wave is done with stage 0 before the next tile goes there
+    __syncthreads();
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = fmaxf(m[qt], __shfl_xor(m[qt], 32, 64));
+    l[qt] = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[ft][qt][r] = 0.f;
+  }
+  u32x4 P[BN / 16][QT];
+  for (int kt = kt0; kt < kt1; ++kt) {
+    tile_scores(kt);
+    exp_half<0, QT, true>(S0, P, m, l);
+    exp_half<1, QT, true>(S1, P, m, l);
+    values_part<C, 0, BN / 16>(tl, O, P, 0, lane, [](int) {});
+    __syncthreads();
+  }
+}
+
 // Fast latent attention, one wave per SIMD.  Each wave owns QT x 32 query rows
 // (64 at d_c <= 192, 32 at d_c = 256) whose q_lat stays in registers; O^T lives in
 // the accumulation registers.  Key tile kt is handled in three steps:
@@ -908,19 +751,44 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
     constexpr int WR = QT * 32, CPR = DC / 8;
     static_assert(CPR % 8 == 0 && (size_t)C::NW * WR * DC * 2 <= C::LDS, "row image");
     bf16 *img = tl.base + wave * WR * DC;
+    // The reference key of the first tile has weight 1, so a row sum is >= 1.  Any
+    // weight above 2^64 (a score more than 64 above the reference) makes it exceed
+    // 2^64, as does inf or NaN: then the whole workgroup recomputes this piece
+    // exactly, and the row tile's flag records it.  Sums above 2^64 made only of
+    // smaller weights take that path too (harmless).
+    float lt[QT];
+    int bad = 0;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
-      // The reference key of the first tile has weight 1, so lt >= 1.  Any weight
-      // above 2^64 (a score more than 64 above the reference) makes lt exceed 2^64,
-      // as does inf or NaN: such a row tile is recomputed by the safe kernel.
-      // Sums above 2^64 made only of smaller weights are flagged too (harmless).
-      if (!(lt <= s.sum_limit)) flags[rt] = 1;
-      stage_rows<FT, QT, DC>(img, O, qt, qt * 32 + l32, 1.0f / lt, g);
+      lt[qt] = l[qt] + __shfl_xor(l[qt], 32, 64);
+      bad |= !(lt[qt] <= s.sum_limit);
+    }
+    if (__builtin_expect(__syncthreads_or(bad), 0)) {
+      if (tid == 0) flags[rt] = 1;
+      // the piece's bounds and ring are derived again here rather than kept live
+      // through the tile loop
+      int rt2 = rt;
+      asm volatile("" : "+s"(rt2));
+      const RowTile t2 = row_tile(s, rt2);
+      const int k0 = (int)((begin > t2.f0 ? begin : t2.f0) - t2.f0);
+      const int k1 = (int)((end < t2.f0 + t2.KT ? end : t2.f0 + t2.KT) - t2.f0);
+      tl.nk = t2.nk;
+      tl.cb = cache + (int64_t)t2.b * s.cache_rows * C::DK;
+      const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)tl.cb, (short)0, (int)(s.cache_rows * C::DK * 2), kBufferConfig);
+      // the queries too: their registers are free after the tile loop
+      load_queries<C::DK, QT, KB>(Qr, q, s, t2.b, t2.row0 + wave * QT * 32, l32, g);
+      safe_piece<C>(tl, rs2, Qr, O, m, l, k0, k1, t2.KT - 1, t2.nk, lane, l32, g);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) lt[qt] = l[qt] + __shfl_xor(l[qt], 32, 64);
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      stage_rows<FT, QT, DC>(img, O, qt, qt * 32 + l32, 1.0f / lt[qt], g);
       const int lrow = wave * WR + qt * 32 + l32;
       if (!whole && g == 0 && row0 + lrow < t.row_end) {
         rec_m[lrow] = m[qt];
-        rec_l[lrow] = lt;
+        rec_l[lrow] = lt[qt];
       }
     }
     // LDS operations of one wave complete in order; this keeps the compiler from
@@ -1002,79 +870,6 @@ __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
 #pragma unroll
   for (int e = 0; e < 8; ++e) out[e] = (bf16)(acc[e] * inv);
   *(bf16x8 *)(o + ((int64_t)b * s.R + row) * DC + c8) = out;
-}
-
-// Safe recomputation of the row tiles the fast kernel flagged: the whole window per
-// workgroup, reference max raised lazily (by more than kSafeThreshold) with O
-// rescaled, result written directly.  Workgroups of unflagged tiles exit at once.
-template <class C>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_latent_attn_safe(const bf16 *__restrict__ q, const bf16 *__restrict__ cache,
-                        bf16 *__restrict__ o, const int *__restrict__ flags, Sched s) {
-  constexpr int QT = C::QT, KB = C::KB, FT = C::FT, RW = C::RW;
-  // workgroup: one RW-row piece of a fast row tile (s.RW rows)
-  const int per = (s.RW + RW - 1) / RW;
-  const int rt = blockIdx.x / per;
-  if (!flags[rt]) return;
-  const RowTile t = row_tile(s, rt);
-  const int b = t.b, row0 = t.row0 + (blockIdx.x % per) * RW;
-  if (row0 >= t.row_end) return;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  Tile<C> tl;
-  tl.base = (bf16 *)lds;
-  tl.nk = t.nk;
-  tl.start0 = s.start0;
-  tl.len0 = s.len0;
-  tl.cb = cache + (int64_t)b * s.cache_rows * C::DK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-
-  bf16x8 Qr[QT][KB];
-  f32x16 O[FT][QT];
-  bf16x8 P[BN / 16][QT];
-  float m[QT], l[QT];
-  load_queries<C::DK, QT, KB>(Qr, q, s, b, row0 + wave * QT * 32, l32, g);
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m[qt] = -1e30f;
-    l[qt] = 0.f;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) O[ft][qt][r] = 0.f;
-  }
-  tl.load(0, tid);
-  for (int kt = 0; kt < t.KT; ++kt) {
-    __syncthreads();
-    tl.store(tid, 0);
-    __syncthreads();
-    if (kt + 1 < t.KT) tl.load(kt + 1, tid);
-    f32x16 S[2][QT];
-    tl.scores(S, Qr, kt, 0, l32, g);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mx = tile_max<QT>(S, qt);
-      if (__any(mx > m[qt] + kSafeThreshold)) {
-        const float mn = fmaxf(m[qt], mx);
-        const float al = fast_exp2(m[qt] - mn);
-        m[qt] = mn;
-        l[qt] *= al;
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[ft][qt][r] *= al;
-      }
-      l[qt] += exp_and_pack<QT>(S, P, qt, m[qt]);
-    }
-    tl.values(O, P, 0, lane);
-  }
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
-    const int row = row0 + wave * QT * 32 + qt * 32 + l32;
-    if (row < t.row_end)
-      store_rows<FT, QT>(o + ((int64_t)b * s.R + row) * C::DC, O, qt, 1.0f / lt, g);
-  }
 }
 
 __global__ void k_fill_i32(int *p, int n, int v) {
@@ -1173,7 +968,6 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 template <int DC, int DR>
 hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   using F = typename Choice<DC, DR>::Fast;
-  using S = typename Choice<DC, DR>::Safe;
   Sched s = make_sched(a, F::RW, a.grid * F::WPC);
   if (s.T <= 0) return hipSuccess;
   auto fast = k_latent_attn_w1<F>;
@@ -1185,7 +979,6 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
     if (a.builtin_scores) fast = k_latent_attn_w1<FB>;
   }
   hipError_t e = allow_lds(fast, F::LDS);
-  if (e == hipSuccess) e = allow_lds(k_latent_attn_safe<S>, S::LDS);
   if (e != hipSuccess) return e;
   if (!a.flags_zeroed) {
     hipLaunchKernelGGL(k_fill_i32, dim3((s.RT + 255) / 256), dim3(256), 0, st, a.flags, s.RT, 0);
@@ -1200,11 +993,6 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
   const int by_boundary = s.RT > s.G;
   hipLaunchKernelGGL(k_attn_merge<F>, dim3((by_boundary ? s.G : s.RT) * merge_blocks), dim3(256), 0,
                      st, (bf16 *)a.o, (const unsigned char *)a.part, s, merge_blocks, by_boundary);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int safe_wgs = s.RT * ((F::RW + S::RW - 1) / S::RW);
-  hipLaunchKernelGGL(k_latent_attn_safe<S>, dim3(safe_wgs), dim3(S::NT), S::LDS, st,
-                     (const bf16 *)a.q, (const bf16 *)a.cache, (bf16 *)a.o,
-                     (const int *)a.flags, s);
   return hipGetLastError();
 }
 

@@ -377,9 +377,9 @@ bool cache_in_place(const mla_config &c, int32_t batch, const mla_cache &r) {
   return true;
 }
 
-// MLA_ATTN_OVERFLOW_LIMIT=v (a number > 0): the fast attention kernel flags row
-// tiles whose row sums exceed v instead of 2^64, so the safe path can be exercised
-// on ordinary data; unset or invalid: 2^64.
+// MLA_ATTN_OVERFLOW_LIMIT=v (a number > 0): the fast attention kernel recomputes
+// (and flags) the pieces whose row sums exceed v instead of 2^64, so its exact
+// path can be exercised on ordinary data; unset or invalid: 2^64.
 float overflow_limit() {
   const char *v = std::getenv("MLA_ATTN_OVERFLOW_LIMIT");
   if (!v || !*v) return 0.f;

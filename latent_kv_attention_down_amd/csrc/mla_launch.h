@@ -135,8 +135,8 @@ struct AttnArgs {
   // attends the first min(nk0 + (k + 1) * blk_keys, nk) keys.  No mask: nblk = 1,
   // blk_rows = R, blk_keys = nk, nk0 = 0.
   int nblk, blk_rows, blk_keys, nk0;
-  // Row sums (weights relative to the first key tile's max) above this send the
-  // row tile to the safe path: 2^64 (overflow guard), or lower to force it.
+  // Row sums (weights relative to the first key tile's max) above this make the
+  // kernel recompute that piece exactly: 2^64 (overflow guard), or lower to force it.
   float sum_limit;
   // Score MFMAs in the compiler's own form instead of the inline-asm one (a check:
   // both give the same bits).

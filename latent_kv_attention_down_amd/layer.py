@@ -123,7 +123,7 @@ class DeviceLayer:
 
     def overflow_flags(self, chunk):
         """The attention's overflow flags left in the workspace by the last call
-        (one per row tile; nonzero: recomputed by the safe path), as a host array."""
+        (one per row tile; nonzero: recomputed against the exact maximum), as a host array."""
         off, n = _lib.overflow_flags(self.cfg, chunk)
         ws = self.workspace(chunk)
         return ws[off:off + 4 * n].view(torch.int32).cpu().numpy()

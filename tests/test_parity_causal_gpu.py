@@ -53,15 +53,26 @@ def test_blocks_fp32():
 
 
 def test_blocks_sharp_softmax():
-    full_step(Run(small_wan(window_frames=6, chunk_frames=6, t0=0, n_valid_frames=6,
-                            causal_frames=3), scale={"w_q_down": 8.0}), check_cache=False)
+    """RMSNorm gain of c^Q x8 (a scale on W^Q_down would be cancelled by the
+    normalisation): logits of standard deviation ~8 nats, inside the fast kernel's
+    range, so nothing is flagged."""
+    run = Run(small_wan(window_frames=6, chunk_frames=6, t0=0, n_valid_frames=6,
+                        causal_frames=3), scale={"g_q": 8.0})
+    full_step(run, check_cache=False)
+    flags = run.L.overflow_flags(run.chunk())
+    assert len(flags) > 0 and not flags.any(), flags
 
 
-def test_blocks_very_sharp_softmax_takes_the_safe_path():
-    """Row tiles the fast kernel flags are recomputed per block with that block's
-    key count."""
-    full_step(Run(small_wan(window_frames=6, chunk_frames=6, t0=0, n_valid_frames=6,
-                            causal_frames=2), scale={"w_q_down": 40.0}), check_cache=False)
+def test_blocks_exact_path(monkeypatch):
+    """The fast kernel's bound forced down to 2 (MLA_ATTN_OVERFLOW_LIMIT): every piece
+    of every block's row tiles is recomputed against its exact maximum, each over its
+    own block's key count."""
+    monkeypatch.setenv("MLA_ATTN_OVERFLOW_LIMIT", "2")
+    run = Run(small_wan(window_frames=6, chunk_frames=6, t0=0, n_valid_frames=6,
+                        causal_frames=2), random_gains=True)
+    full_step(run, check_cache=False)
+    flags = run.L.overflow_flags(run.chunk())
+    assert flags.all(), f"{int((flags == 0).sum())} of {len(flags)} row tiles not flagged"
 
 
 def test_clip21_full_size_sampled():

@@ -125,10 +125,11 @@ def long_window(**kw):
 
 
 @pytest.mark.parametrize("case", ["small", "long", "batch-causal", "sink-read", "dc256"])
-def test_safe_path_recomputes_flagged_row_tiles(case, monkeypatch):
+def test_exact_path_recomputes_flagged_pieces(case, monkeypatch):
     """The bound of the fast kernel forced down to 2 (MLA_ATTN_OVERFLOW_LIMIT): every
-    row sum exceeds it, every row tile is flagged and recomputed by the safe kernel
-    (lazy rescaling), on ordinary data and at the usual
+    row sum exceeds it, so every piece of every row tile is recomputed inside the
+    attention kernel (a pass for the exact maximum, then the softmax against it) and
+    every row tile is flagged, on ordinary data and at the usual
     tolerance, with causal blocks, two requests, a sink with read-time rotation and
     the 32-rows-per-wave d_c = 256 build."""
     monkeypatch.setenv("MLA_ATTN_OVERFLOW_LIMIT", "2")
@@ -152,12 +153,12 @@ def test_needle_key_overflows_the_fast_kernel():
     so its positional key k^R = W^K_R x, which RMSNorm does not touch, is 64 times
     larger and its scores reach far above the rest.  Pieces that start before its
     key tile see scores more than 64 (base 2) above their reference, so the fast
-    kernel flags their row tiles by itself and the safe path recomputes them.
+    kernel recomputes those pieces and flags their row tiles by itself.
     Parity here is the Frobenius relative error alone: with scores this sharp
     (tens of units, base 2), the bf16 rounding of the absorbed query and the keys
     by itself moves single rows by about 1.4e-2 of max|y| in fp64 (computed on the
     CPU for this case), so the max-abs criterion measures the inputs' precision,
-    not the path; the safe path itself is held to both criteria on ordinary data
+    not the path; the exact path itself is held to both criteria on ordinary data
     by the forced-bound test above."""
     run = Run(long_window())
     tpf = run.s.tokens_per_frame

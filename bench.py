@@ -297,8 +297,8 @@ def main():
     for L, x, y in layers:
         assert torch.isfinite(y.float()).all(), "non-finite output"
 
-    # the chunk attention on its own (a2-a4: query preparation, latent attention with
-    # its merge and fallback, per-head value up-projection), layer 0, back to back
+    # the chunk attention on its own (a2-a4: query preparation, latent attention,
+    # per-head value up-projection with the merge of split row tiles), layer 0, back to back
     out_heads = L0.new_out(chunk, s.n_heads * s.d_head)
     for _ in range(3):
         mla.chunk_attention(L0.cfg, L0.weights, chunk, x0, L0.cache_desc, out_heads, ws, stream)
@@ -382,8 +382,8 @@ def main():
         "chunk_attention_tflops": round(ca_tflops, 2),
         "chunk_attention_ms": spread(ca_ms),
         "chunk_attention_note": "mla_chunk_attention timed whole (query preparation, latent "
-                                "attention with its merge and fallback, per-head W^V_up), "
-                                "attention FLOPs only",
+                                "attention, per-head W^V_up with the merge of split row "
+                                "tiles), attention FLOPs only",
         "fast_kernel_tflops": round(kernel_tflops, 2),
         "cache_write_gbs": round(write_gbs, 1),
         "cache_write_us": round(write_ms * 1e3, 2),
@@ -396,7 +396,7 @@ def main():
                      "frac": round(kernel_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic,
                      "kernel": "k_latent_attn_w1 (the dominant kernel: latent attention, "
-                               "fast path, without its merge)",
+                               "without the merge of split row tiles)",
                      "kernel_ms": round(attn_avg, 4)},
         "cache_write_roofline": {"bound": "hbm", "achieved": round(write_gbs, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",

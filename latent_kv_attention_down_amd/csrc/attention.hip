@@ -872,6 +872,209 @@ __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
   *(bf16x8 *)(o + ((int64_t)b * s.R + row) * DC + c8) = out;
 }
 
+// The per-head value up-projection of the chunk step (Eq. 2) with the merge of split
+// row tiles folded into the loading of its A operand: one workgroup computes a
+// 128-token x 128-column tile of out_heads for one head h,
+//   out_heads[m][h*d_head + n] = sum_c W^V_up[h*d_head + n][c] O_lat[(m, h)][c].
+// Row (m, h) of O_lat is read from o when its row tile was finished by one workgroup,
+// else combined from the records of the pieces, in the same order and arithmetic as
+// k_attn_merge (so the rows are the same bits), and never written back.  A and the
+// head's W^V_up rows sit whole in LDS (K = d_c), 16-byte chunk c of row r at
+// c ^ (r & 7); W^V_up arrives by direct loads while the rows are combined.  Four
+// waves of 64 x 64, 32x32x16 MFMAs in k order, as the projections' GEMM tile.
+struct VupArgs {
+  const bf16 *w;  // W^V_up, (n_h * d_head) x d_c
+  bf16 *out;      // out_heads, (B * T_q) x (n_h * d_head)
+  int M, T_q, n_h, N, nbn;
+};
+
+template <class C>
+struct VupTile {
+  static constexpr int DC = C::DC, BM = 64, BN = 128, NT = 256, CH = DC / 8;
+  static constexpr int TPR = NT / BM;  // threads per A row
+  static constexpr int CPT = CH / TPR; // 16-byte chunks per thread
+  static constexpr int NP = 3;         // pieces of a row whose loads are issued together
+  static constexpr size_t A_B = (size_t)BM * DC * 2, B_B = (size_t)BN * DC * 2;
+  static constexpr size_t LDS = A_B + B_B;
+  static constexpr int B_LOADS = BN * CH / 64;  // 1 KB direct loads of the W^V_up tile
+  static_assert(CH % 8 == 0 && CH % TPR == 0 && B_LOADS % (NT / 64) == 0, "tile shape");
+  static_assert((size_t)BM * (BN + 8) * 2 <= LDS, "epilogue tile");
+};
+
+// Row (r, h)'s combined latent, chunks c0 .. c0+CPT-1, into acc: the fixed-order
+// combination of k_attn_merge (largest m first, weights l_p 2^(m_p - max m), sums in
+// piece order, rounded to bf16), or the row itself when one workgroup finished its
+// row tile.  Up to NP pieces have every load issued before the first use.
+template <class C>
+__device__ __forceinline__ void vup_row(float (&acc)[VupTile<C>::CPT][8], const bf16 *o,
+                                        const unsigned char *part, const Sched &s, int b, int row,
+                                        int c0) {
+  using V = VupTile<C>;
+  constexpr int DC = C::DC, RW = C::RW, CPT = V::CPT, NP = V::NP;
+  const int k = row / s.blk_rows, j = row - k * s.blk_rows, i = j / s.RW;
+  const int rt = b * s.RTb + k * s.blk_rt + i, lrow = j - i * s.RW;
+  const RowTile t = row_tile(s, rt);
+  const int g0 = wg_of(s, t.f0), g1 = wg_of(s, t.f0 + t.KT - 1);
+  if (g0 == g1) {
+    const bf16 *src = o + ((int64_t)b * s.R + row) * DC + c0 * 8;
+    bf16x8 x[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) x[c] = *(const bf16x8 *)(src + c * 8);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[c][e] = (float)x[c][e];
+    return;
+  }
+  auto rec = [&](int gg) { return part + (size_t)(gg + rt) * C::REC; };
+  auto mrec = [&](int gg) { return (const float *)(rec(gg) + (size_t)RW * DC * 2); };
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+  float wsum = 0.f;
+  if (g1 - g0 < NP) {
+    float mp[NP], lp[NP];
+    bf16x8 x[NP][CPT];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int gg = min(g0 + p, g1);
+      mp[p] = mrec(gg)[lrow];
+      lp[p] = mrec(gg)[RW + lrow];
+      const bf16 *src = (const bf16 *)rec(gg) + (int64_t)lrow * DC + c0 * 8;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) x[p][c] = *(const bf16x8 *)(src + c * 8);
+    }
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (g0 + p <= g1) mmax = fmaxf(mmax, mp[p]);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (g0 + p > g1) break;
+      const float w = lp[p] * fast_exp2(mp[p] - mmax);
+      wsum += w;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)x[p][c][e];
+    }
+  } else {
+    float mmax = -INFINITY;
+    for (int gg = g0; gg <= g1; ++gg) mmax = fmaxf(mmax, mrec(gg)[lrow]);
+    for (int gg = g0; gg <= g1; ++gg) {
+      const bf16 *src = (const bf16 *)rec(gg) + (int64_t)lrow * DC + c0 * 8;
+      bf16x8 x[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) x[c] = *(const bf16x8 *)(src + c * 8);
+      const float w = mrec(gg)[RW + lrow] * fast_exp2(mrec(gg)[lrow] - mmax);
+      wsum += w;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)x[c][e];
+    }
+  }
+  const float inv = 1.0f / wsum;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[c][e] = (float)(bf16)(acc[c][e] * inv);
+}
+
+template <class C>
+__global__ __launch_bounds__(VupTile<C>::NT) void k_merge_vup(const bf16 *__restrict__ o,
+                                                   const unsigned char *__restrict__ part, Sched s,
+                                                   VupArgs v) {
+  using V = VupTile<C>;
+  constexpr int DC = C::DC, CH = V::CH, CPT = V::CPT, BM = V::BM, BN = V::BN, NT = V::NT;
+  typedef __attribute__((address_space(3))) void lds_void;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  bf16 *As = (bf16 *)lds, *Bs = (bf16 *)(lds + V::A_B);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y, mt = blockIdx.x / v.nbn, nt = blockIdx.x % v.nbn;
+  const int m0 = mt * BM, n0 = nt * BN;
+
+  // W^V_up rows n0.. of head h (rows past N repeat row N-1; their columns are not
+  // stored): lane p of load L fetches the chunk that belongs at position L*64 + p.
+  {
+    constexpr int LPW = V::B_LOADS / (NT / 64);
+    const bf16 *wb = v.w + (int64_t)h * v.N * DC;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int L = wave * LPW + i, p = L * 64 + lane;
+      const int r = p / CH, c = (p % CH) ^ (r & 7);
+      __builtin_amdgcn_global_load_lds((const void *)(wb + (int64_t)min(n0 + r, v.N - 1) * DC + c * 8),
+                                       (lds_void *)((unsigned char *)Bs + L * 1024), 16, 0, 0);
+    }
+  }
+  // A: thread (r, part) combines chunks part*CPT .. of row (m0 + r, h)
+  {
+    const int r = tid / V::TPR, c0 = (tid % V::TPR) * CPT, m = m0 + r;
+    float acc[CPT][8];
+    if (m < v.M) {
+      const int b = m / v.T_q;
+      vup_row<C>(acc, o, part, s, b, (m - b * v.T_q) * v.n_h + h, c0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      bf16x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (bf16)acc[c][e];
+      *(bf16x8 *)(As + r * DC + ((c0 + c) ^ (r & 7)) * 8) = x;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // waves of 32 x 64
+  static_assert(NT / 64 == (BM / 32) * (BN / 64), "one 32 x 64 block per wave");
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g8 = lane >> 5;
+  f32x16 acc[2];
+#pragma unroll
+  for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[jn][q] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < DC / 16; ++ks) {
+    const int ra = wm * 32 + l32;
+    const bf16x8 af = *(const bf16x8 *)(As + ra * DC + ((2 * ks + g8) ^ (ra & 7)) * 8);
+    bf16x8 bfr[2];
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+      const int rb = wn * 64 + jn * 32 + l32;
+      bfr[jn] = *(const bf16x8 *)(Bs + rb * DC + ((2 * ks + g8) ^ (rb & 7)) * 8);
+    }
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) acc[jn] = mfma32(af, bfr[jn], acc[jn]);
+  }
+  // results through LDS for 16-byte stores (acc[j][4q + e]: row 8q + 4*g8 + e,
+  // column l32 of the 32x32 tile)
+  constexpr int LDC = BN + 8;
+  bf16 *tile = (bf16 *)lds;
+  __syncthreads();
+#pragma unroll
+  for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = wm * 32 + (q >> 2) * 8 + g8 * 4 + (q & 3);
+      tile[row * LDC + wn * 64 + jn * 32 + l32] = (bf16)acc[jn][q];
+    }
+  __syncthreads();
+  const int ldo = v.n_h * v.N;
+  for (int id = tid; id < BM * (BN / 8); id += NT) {
+    const int r = id / (BN / 8), c = (id % (BN / 8)) * 8;
+    if (m0 + r < v.M && n0 + c < v.N)
+      *(uint4 *)(v.out + (int64_t)(m0 + r) * ldo + h * v.N + n0 + c) = *(const uint4 *)(tile + r * LDC + c);
+  }
+}
+
 __global__ void k_fill_i32(int *p, int n, int v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -989,6 +1192,15 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
                      (const bf16 *)a.cache, (bf16 *)a.o, (unsigned char *)a.part, a.flags, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
+  if (a.out_heads) {
+    using V = VupTile<F>;
+    VupArgs v{(const bf16 *)a.w_v_up, (bf16 *)a.out_heads, a.B * a.T_q, a.T_q, a.n_h, a.d_head,
+              (a.d_head + V::BN - 1) / V::BN};
+    if ((e = allow_lds(k_merge_vup<F>, V::LDS)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_merge_vup<F>, dim3(((v.M + V::BM - 1) / V::BM) * v.nbn, a.n_h), dim3(V::NT),
+                       V::LDS, st, (const bf16 *)a.o, (const unsigned char *)a.part, s, v);
+    return hipGetLastError();
+  }
   const int merge_blocks = (F::RW * (DC / 8) + 255) / 256;
   const int by_boundary = s.RT > s.G;
   hipLaunchKernelGGL(k_attn_merge<F>, dim3((by_boundary ? s.G : s.RT) * merge_blocks), dim3(256), 0,

@@ -473,9 +473,16 @@ int attended_keys(const mla_config &c, const mla_chunk &k, const Dims &d, const 
 // order in the workspace.
 int run_latent_attention(const mla_config &c, const mla_chunk &k, const Dims &d, const void *q_lat,
                          const void *keys, void *o_lat, unsigned char *ws, bool flags_zeroed,
-                         hipStream_t st) {
+                         hipStream_t st, const void *w_v_up = nullptr, void *out_heads = nullptr) {
   const Workspace L = carve(c, k);
   mla::AttnArgs a = attn_shape(c, k, d);
+  if (out_heads) {  // bf16: the value up-projection takes the place of the merge pass
+    a.w_v_up = w_v_up;
+    a.out_heads = out_heads;
+    a.n_h = c.n_heads;
+    a.d_head = c.d_head;
+    a.T_q = (int)d.T_q;
+  }
   a.q = q_lat;
   a.cache = keys;
   a.o = o_lat;
@@ -636,7 +643,13 @@ int attend(const mla_config &c, const mla_weights &w, const mla_chunk &k, const 
   unsigned char *q_lat = ws + L.q_lat, *o_lat = ws + L.o_lat;
   const void *keys = nullptr;
   MLA_TRY(attended_keys(c, k, d, cache, ws, &keys, st));
-  // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16)
+  // softmax over the window, latent value sum (Eq. 7 absorbed, Eq. 12, 16).  In bf16
+  // the value up-projection (Eq. 2) combines the split row tiles as it loads them
+  // where they are a large share (at most four row tiles per attention workgroup:
+  // the single chunk, small batches); otherwise a merge pass completes O_lat first.
+  if (out_heads && c.dtype == MLA_BF16 &&
+      mla::latent_attention_counts(attn_shape(c, k, d)).row_tiles <= 4 * (int64_t)attn_grid_cus())
+    return run_latent_attention(c, k, d, q_lat, keys, o_lat, ws, true, st, w.w_v_up, out_heads);
   MLA_TRY(run_latent_attention(c, k, d, q_lat, keys, o_lat, ws, true, st));
   if (!out_heads) return MLA_OK;  // O_lat stays in the workspace
   // o_h = W^V_up,h O_lat,h  (Eq. 2)

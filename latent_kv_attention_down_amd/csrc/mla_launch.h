@@ -141,6 +141,14 @@ struct AttnArgs {
   // Score MFMAs in the compiler's own form instead of the inline-asm one (a check:
   // both give the same bits).
   bool builtin_scores;
+  // Optional (bf16 path): the per-head value up-projection out_heads[m][h*d_head + n]
+  // = sum_c W^V_up[h*d_head + n][c] O_lat[m*n_h + h][c] for the M = B*T_q tokens,
+  // with the rows of split row tiles combined from their records while they are
+  // loaded, instead of a merge pass into o.  Rows of split row tiles are then not
+  // written to o.  out_heads null: the merge pass, o complete.
+  const void *w_v_up = nullptr;
+  void *out_heads = nullptr;
+  int n_h = 0, d_head = 0, T_q = 0;
 };
 // Row tiles (with causal blocks, a block's last tile may be partial) and
 // (row tile, key tile) steps of the bf16 kernel for these arguments.

@@ -74,6 +74,22 @@ def test_small_bf16_out_heads():
     assert_close(to_host(out)[0], run.oracle()["out"], TOL["bf16"], "out_heads")
 
 
+@pytest.mark.parametrize("d_nope", [32, 128, 224])
+def test_head_widths(d_nope):
+    """d_head = 64, 160 and 256 (32 RoPE columns each): the per-head value
+    up-projection's 128-wide column tiles come out short, ragged (128 + 32) and
+    doubled, with the split row tiles combined as they load; out_heads and y."""
+    run = Run(small_wan(d_nope=d_nope, d_head=d_nope + 32), random_gains=True)
+    run.prefill()
+    ch = run.chunk()
+    x = run.chunk_tokens()
+    run.L.cache_write(ch, x)
+    out = run.L.chunk_attention(ch, x)
+    torch.cuda.synchronize()
+    assert_close(to_host(out)[0], run.oracle()["out"], TOL["bf16"], "out_heads")
+    full_step(run, check_cache=False)
+
+
 def test_ring_wraps_around():
     """Window frames 6..10 in a 5-slot ring: slots 1,2,3,4,0 (FIFO, App. D.4)."""
     full_step(Run(small_wan(t0=9)))

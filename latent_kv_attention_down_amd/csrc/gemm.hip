@@ -208,6 +208,19 @@ hipError_t launch_bf16(const GemmArgs &g, bool out_f32, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The absorbed query GEMM alone (256x256 tiles, rows scaled by their RMS) with the
+// query's RoPE columns rotated in its tiles, exactly as the separate RoPE pass rotates
+// them; the first tile also clears the attention's overflow flags, the other duty of
+// that pass.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void k_query_gemm_rope(GemmArgs g, RopeQArgs r) {
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  if (lin == 0)
+    for (int i = threadIdx.x; i < r.n_zero; i += blockDim.x) r.zero[i] = 0;
+  gemm_dma_tile<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS, true>(g, lin, gridDim.x,
+                                                                   gridDim.x * gridDim.y, 0, &r);
+}
+
 }  // namespace
 
 hipError_t gemm_bf16_nt(const GemmArgs &g, bool out_f32, hipStream_t st) {
@@ -237,6 +250,27 @@ hipError_t gemm_f32_nt(const GemmArgs &g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   dim3 grid((g.N + 15) / 16, (g.M + 15) / 16, g.batch);
   hipLaunchKernelGGL(k_gemm_f32_nt, grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+bool query_gemm_rope_applies(const GemmArgs &g, const RopeQArgs &r) {
+  const int64_t tiles = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const int dk = r.d_c + r.d_rope;
+  return g.batch == 1 && g.ssq_in && !g.ssq_out && g.N >= 512 && g.K > 0 && g.K % 64 == 0 &&
+         tiles >= 200 && r.in_place && r.d_c % 8 == 0 && dk % 8 == 0 && dk >= 64 &&
+         (int64_t)r.n_h * dk == g.N && r.M == g.M && (uintptr_t)g.A % 16 == 0 &&
+         (uintptr_t)g.B % 16 == 0 && (uintptr_t)g.C % 16 == 0 && g.lda % 8 == 0 &&
+         g.ldb % 8 == 0 && g.ldc % 8 == 0;
+}
+
+hipError_t query_gemm_rope(const GemmArgs &g, const RopeQArgs &r, hipStream_t st) {
+  if (!query_gemm_rope_applies(g, r)) return hipErrorInvalidValue;
+  using D = GemmDma<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS>;
+  hipError_t e = hipFuncSetAttribute((const void *)k_query_gemm_rope,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)D::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_query_gemm_rope, dim3((g.N + 255) / 256, (g.M + 255) / 256), dim3(D::NT),
+                     D::LDS, st, g, r);
   return hipGetLastError();
 }
 

@@ -535,15 +535,17 @@ int run_gemm(const mla_config &c, const mla::GemmArgs &g, bool out_f32, hipStrea
   } while (0)
 
 // Query preparation (Eq. 3-4, 6; App. E Eq. 8-9): the absorbed query rows in the
-// workspace.  The RoPE pass (its arguments in *rq_out) is launched here unless the
-// caller takes it over (launch_rope false).  With `ride` (a cache write of the same
-// step), the absorbed query GEMM, rotating the rope columns in its tiles, and that
-// write share one launch where they fit (*rode then says so: the RoPE pass and the
-// flag clearing are done).
+// workspace.  Where the absorbed query GEMM takes 256x256 tiles it rotates the rope
+// columns in its tiles and clears the attention's flags (*rotated then says so);
+// otherwise the RoPE pass (its arguments in *rq_out) does that, launched here unless
+// the caller takes it over (launch_rope false).  With `ride` (a cache write of the
+// same step) the GEMM and that write share one launch where they fit (*wrote).
 int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &k, const void *x,
                     unsigned char *ws, hipStream_t st, bool launch_rope, mla::RopeQArgs *rq_out,
-                    const mla::CacheWriteArgs *ride = nullptr, bool *rode = nullptr) {
-  if (rode) *rode = false;
+                    const mla::CacheWriteArgs *ride = nullptr, bool *wrote = nullptr,
+                    bool *rotated = nullptr) {
+  bool rot = false;
+  if (wrote) *wrote = false;
   const Dims d = dims(c, k);
   const Workspace L = carve(c, k);
   const bool bf = c.dtype == MLA_BF16;
@@ -591,11 +593,18 @@ int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &
     g2.ssq_parts = (c.d_q + 63) / 64;
     g2.ssq_scale = 1.0f / (float)c.d_q;
     g2.ssq_eps = c.rms_eps;
+    // The query's RoPE columns are rotated in the GEMM's tiles (and the attention's flags
+    // cleared) where the GEMM takes 256x256 tiles; in mla_step the cache write shares
+    // that launch where it fits beside it.
     const int both = ride ? mla::query_gemm_cache_write_blocks(g2, *ride) : 0;
     if (both > 0 && both <= attn_grid_cus()) {
       MLA_HIP(mla::query_gemm_cache_write(g2, *ride, rq, st),
               "absorbed query projection with query rope and cache write");
-      if (rode) *rode = true;
+      if (wrote) *wrote = true;
+      rot = true;
+    } else if (mla::query_gemm_rope_applies(g2, rq)) {
+      MLA_HIP(mla::query_gemm_rope(g2, rq, st), "absorbed query projection with query rope");
+      rot = true;
     } else {
       MLA_TRY(run_gemm(c, g2, false, st, "absorbed query projection"));
     }
@@ -629,7 +638,8 @@ int prepare_queries(const mla_config &c, const mla_weights &w, const mla_chunk &
     }
   }
   if (rq_out) *rq_out = rq;
-  if (launch_rope && !(rode && *rode)) MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
+  if (rotated) *rotated = rot;
+  if (launch_rope && !rot) MLA_HIP(mla::rope_q(rq, bf, st), "query rope");
   return MLA_OK;
 }
 
@@ -712,10 +722,12 @@ int run_step(const mla_config &c, const mla_weights &w, const mla_chunk &k, cons
   const bool absorbed_bf16 = c.dtype == MLA_BF16 && w.w_qlat;
   if (absorbed_bf16) {
     mla::RopeQArgs rq;
-    bool rode = false;
-    MLA_TRY(prepare_queries(c, w, k, x, ws, st, false, &rq, &cw, &rode));
-    if (rode) {
+    bool wrote = false, rotated = false;
+    MLA_TRY(prepare_queries(c, w, k, x, ws, st, false, &rq, &cw, &wrote, &rotated));
+    if (wrote) {
       // the cache write, the query's RoPE and the flags are done
+    } else if (rotated) {
+      MLA_TRY(run_cache_write(c, w, k, x, cache, st));  // the RoPE and the flags are done
     } else if (mla::cache_write_takes_rope(cw, rq) && cw_blocks + rope_needed <= cus) {
       MLA_HIP(mla::cache_write_bf16_rope(cw, rq, cus - cw_blocks, st), "cache write with query rope");
     } else {

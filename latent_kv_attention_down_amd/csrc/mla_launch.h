@@ -88,6 +88,10 @@ hipError_t cache_write_bf16_rope(const CacheWriteArgs &a, const RopeQArgs &r, in
 int query_gemm_cache_write_blocks(const GemmArgs &g, const CacheWriteArgs &a);
 hipError_t query_gemm_cache_write(const GemmArgs &g, const CacheWriteArgs &a, const RopeQArgs &r,
                                   hipStream_t st);
+// The same absorbed query GEMM alone, with the in-place query RoPE r done in its tiles
+// and r's flags cleared, in one launch; query_gemm_rope_applies: where it can run.
+bool query_gemm_rope_applies(const GemmArgs &g, const RopeQArgs &r);
+hipError_t query_gemm_rope(const GemmArgs &g, const RopeQArgs &r, hipStream_t st);
 
 // Window assembly: context frame i (the n_sink sink frames, then frames
 // first_local, first_local+1, ...) is copied from its ring slot to rows i*tpf .. of

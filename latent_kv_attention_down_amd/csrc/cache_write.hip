@@ -396,7 +396,13 @@ __device__ __forceinline__ void cache_write_dma_block(const CacheWriteArgs &a, i
       wait_stage<4 + XQ>(after);
     else
       wait_stage<4>(after);
-    __syncthreads();
+    // A bare barrier: __syncthreads() would also wait for the later stages' loads,
+    // which are meant to stay in flight.  Before it this wave's reads of the stage
+    // refilled next (read in the previous chunk) are complete; the clobbers keep the
+    // compiler from moving LDS accesses across it.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if (kc + NS - 1 < nk) issue(kc + NS - 1);
     const unsigned char *st = smem + (size_t)(kc % NS) * C::SB;
     const unsigned char *sw = st + C::XB + wave * 4096;

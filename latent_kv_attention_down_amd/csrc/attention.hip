@@ -894,11 +894,14 @@ struct VupTile {
   static constexpr int TPR = NT / BM;  // threads per A row
   static constexpr int CPT = CH / TPR; // 16-byte chunks per thread
   static constexpr int NP = 3;         // pieces of a row whose loads are issued together
+  static constexpr int MPW = 2;        // token tiles per workgroup (one W^V_up tile load)
   static constexpr size_t A_B = (size_t)BM * DC * 2, B_B = (size_t)BN * DC * 2;
-  static constexpr size_t LDS = A_B + B_B;
+  // the bf16 output tile (rows padded by 8) over the A tile where it fits, else past B
+  static constexpr size_t T_B = (size_t)BM * (BN + 8) * 2;
+  static constexpr size_t T_OFF = T_B <= A_B ? 0 : A_B + B_B;
+  static constexpr size_t LDS = T_OFF + T_B > A_B + B_B ? T_OFF + T_B : A_B + B_B;
   static constexpr int B_LOADS = BN * CH / 64;  // 1 KB direct loads of the W^V_up tile
   static_assert(CH % 8 == 0 && CH % TPR == 0 && B_LOADS % (NT / 64) == 0, "tile shape");
-  static_assert((size_t)BM * (BN + 8) * 2 <= LDS, "epilogue tile");
 };
 
 // Row (r, h)'s combined latent, chunks c0 .. c0+CPT-1, into acc: the fixed-order
@@ -994,10 +997,11 @@ __global__ __launch_bounds__(VupTile<C>::NT) void k_merge_vup(const bf16 *__rest
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y, mt = blockIdx.x / v.nbn, nt = blockIdx.x % v.nbn;
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int n0 = nt * BN;
 
   // W^V_up rows n0.. of head h (rows past N repeat row N-1; their columns are not
-  // stored): lane p of load L fetches the chunk that belongs at position L*64 + p.
+  // stored), once for the workgroup's MPW token tiles: lane p of load L fetches the
+  // chunk that belongs at position L*64 + p.
   {
     constexpr int LPW = V::B_LOADS / (NT / 64);
     const bf16 *wb = v.w + (int64_t)h * v.N * DC;
@@ -1009,69 +1013,74 @@ __global__ __launch_bounds__(VupTile<C>::NT) void k_merge_vup(const bf16 *__rest
                                        (lds_void *)((unsigned char *)Bs + L * 1024), 16, 0, 0);
     }
   }
-  // A: thread (r, part) combines chunks part*CPT .. of row (m0 + r, h)
-  {
-    const int r = tid / V::TPR, c0 = (tid % V::TPR) * CPT, m = m0 + r;
-    float acc[CPT][8];
-    if (m < v.M) {
-      const int b = m / v.T_q;
-      vup_row<C>(acc, o, part, s, b, (m - b * v.T_q) * v.n_h + h, c0);
-    } else {
+  for (int t = 0; t < V::MPW; ++t) {
+    const int m0 = (mt * V::MPW + t) * BM;
+    if (m0 >= v.M) break;
+    // A: thread (r, part) combines chunks part*CPT .. of row (m0 + r, h)
+    {
+      const int r = tid / V::TPR, c0 = (tid % V::TPR) * CPT, m = m0 + r;
+      float acc[CPT][8];
+      if (m < v.M) {
+        const int b = m / v.T_q;
+        vup_row<C>(acc, o, part, s, b, (m - b * v.T_q) * v.n_h + h, c0);
+      } else {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c)
+        for (int c = 0; c < CPT; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+          for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (bf16)acc[c][e];
+        *(bf16x8 *)(As + r * DC + ((c0 + c) ^ (r & 7)) * 8) = x;
+      }
     }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      bf16x8 x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (bf16)acc[c][e];
-      *(bf16x8 *)(As + r * DC + ((c0 + c) ^ (r & 7)) * 8) = x;
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the W^V_up tile too, the first time
+    __syncthreads();
 
-  // waves of 32 x 64
-  static_assert(NT / 64 == (BM / 32) * (BN / 64), "one 32 x 64 block per wave");
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g8 = lane >> 5;
-  f32x16 acc[2];
+    // waves of 32 x 64
+    static_assert(NT / 64 == (BM / 32) * (BN / 64), "one 32 x 64 block per wave");
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g8 = lane >> 5;
+    f32x16 acc[2];
 #pragma unroll
-  for (int jn = 0; jn < 2; ++jn)
+    for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[jn][q] = 0.f;
+      for (int q = 0; q < 16; ++q) acc[jn][q] = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < DC / 16; ++ks) {
-    const int ra = wm * 32 + l32;
-    const bf16x8 af = *(const bf16x8 *)(As + ra * DC + ((2 * ks + g8) ^ (ra & 7)) * 8);
-    bf16x8 bfr[2];
+    for (int ks = 0; ks < DC / 16; ++ks) {
+      const int ra = wm * 32 + l32;
+      const bf16x8 af = *(const bf16x8 *)(As + ra * DC + ((2 * ks + g8) ^ (ra & 7)) * 8);
+      bf16x8 bfr[2];
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
-      const int rb = wn * 64 + jn * 32 + l32;
-      bfr[jn] = *(const bf16x8 *)(Bs + rb * DC + ((2 * ks + g8) ^ (rb & 7)) * 8);
+      for (int jn = 0; jn < 2; ++jn) {
+        const int rb = wn * 64 + jn * 32 + l32;
+        bfr[jn] = *(const bf16x8 *)(Bs + rb * DC + ((2 * ks + g8) ^ (rb & 7)) * 8);
+      }
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn) acc[jn] = mfma32(af, bfr[jn], acc[jn]);
     }
+    // results through LDS (clear of the W^V_up rows) for 16-byte stores
+    // (acc[j][4q + e]: row 8q + 4*g8 + e, column l32 of the 32x32 tile)
+    constexpr int LDC = BN + 8;
+    bf16 *tile = (bf16 *)(lds + V::T_OFF);
+    __syncthreads();
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) acc[jn] = mfma32(af, bfr[jn], acc[jn]);
-  }
-  // results through LDS for 16-byte stores (acc[j][4q + e]: row 8q + 4*g8 + e,
-  // column l32 of the 32x32 tile)
-  constexpr int LDC = BN + 8;
-  bf16 *tile = (bf16 *)lds;
-  __syncthreads();
+    for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-  for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = wm * 32 + (q >> 2) * 8 + g8 * 4 + (q & 3);
-      tile[row * LDC + wn * 64 + jn * 32 + l32] = (bf16)acc[jn][q];
+      for (int q = 0; q < 16; ++q) {
+        const int row = wm * 32 + (q >> 2) * 8 + g8 * 4 + (q & 3);
+        tile[row * LDC + wn * 64 + jn * 32 + l32] = (bf16)acc[jn][q];
+      }
+    __syncthreads();
+    const int ldo = v.n_h * v.N;
+    for (int id = tid; id < BM * (BN / 8); id += NT) {
+      const int r = id / (BN / 8), c = (id % (BN / 8)) * 8;
+      if (m0 + r < v.M && n0 + c < v.N)
+        *(uint4 *)(v.out + (int64_t)(m0 + r) * ldo + h * v.N + n0 + c) = *(const uint4 *)(tile + r * LDC + c);
     }
-  __syncthreads();
-  const int ldo = v.n_h * v.N;
-  for (int id = tid; id < BM * (BN / 8); id += NT) {
-    const int r = id / (BN / 8), c = (id % (BN / 8)) * 8;
-    if (m0 + r < v.M && n0 + c < v.N)
-      *(uint4 *)(v.out + (int64_t)(m0 + r) * ldo + h * v.N + n0 + c) = *(const uint4 *)(tile + r * LDC + c);
+    __syncthreads();  // the next token tile's rows go where this output tile was
   }
 }
 
@@ -1197,7 +1206,8 @@ hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t
     VupArgs v{(const bf16 *)a.w_v_up, (bf16 *)a.out_heads, a.B * a.T_q, a.T_q, a.n_h, a.d_head,
               (a.d_head + V::BN - 1) / V::BN};
     if ((e = allow_lds(k_merge_vup<F>, V::LDS)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_merge_vup<F>, dim3(((v.M + V::BM - 1) / V::BM) * v.nbn, a.n_h), dim3(V::NT),
+    const int mtiles = (v.M + V::BM * V::MPW - 1) / (V::BM * V::MPW);
+    hipLaunchKernelGGL(k_merge_vup<F>, dim3(mtiles * v.nbn, a.n_h), dim3(V::NT),
                        V::LDS, st, (const bf16 *)a.o, (const unsigned char *)a.part, s, v);
     return hipGetLastError();
   }

@@ -34,15 +34,16 @@
 //    workgroup sees for it and is never moved, so O is never rescaled inside the
 //    loop (a rescale would drag the AGPR-resident accumulators through VGPRs).
 //    If a row's later scores exceed the reference by more than 64 (base 2), the
-//    workgroup recomputes that piece at once with the classic online softmax
-//    (reference following the running max, O rescaled) and flags the row tile (a
-//    lower bound can be set to exercise this on ordinary data).  Below that bound
-//    every weight is at most 2^64, far inside fp32 and bf16 range;
+//    workgroup recomputes that piece at once against each row's exact maximum (a
+//    pass for the maximum, then the softmax) and flags the row tile (a lower bound
+//    can be set to exercise this on ordinary data).  Below that bound every weight
+//    is at most 2^64, far inside fp32 and bf16 range;
 //  * the fast grid is persistent: workgroup g takes the flat range
 //    [gT/G, (g+1)T/G) of T = (row tiles) x (key tiles) tile steps, so every CU gets
 //    the same work.  A row tile finished by one workgroup is written directly; one
 //    split across workgroups leaves normalised bf16 partials plus (m, l) per row,
-//    merged by k_attn_merge in a fixed order (deterministic, no atomics).
+//    merged in a fixed order (deterministic, no atomics): by k_attn_merge, or by
+//    k_merge_vup while it loads the rows for the per-head value up-projection.
 #include <type_traits>
 
 #include "mla_device.h"
@@ -353,7 +354,13 @@ struct TileW {
 };
 
 // V^T fragment i of key blocks KB0 .. KB0+NKB-1 of stage buf (fragment i: key block
-// KB0 + i % NKB, features 32 (i / NKB) .. +31).
+// KB0 + i % NKB, features 32 (i / NKB) .. +31).  For key block kb the A operand of
+// lane l (16-lane group G = l/16, r = l%16, g = l/32) must hold feature
+// 32 (i / NKB) + l%32 of keys 16kb + 4g + j (slots 0-3) and 16kb + 8 + 4g + j (slots
+// 4-7).  ds_read_b64_tr_b16 hands lane r of a 16-lane group element r%4 of the
+// 8-byte pieces addressed by lanes r/4 + 4j, so lane r addresses key
+// 16kb + 8h + 4g + r/4 at feature 32 (i / NKB) + 16 (G%2) + 4 (r%4) (through the chunk
+// swizzle), and no transposed copy of the latent is ever written.
 template <class C, int KB0, int NKB>
 __device__ __forceinline__ bf16x8 vfrag_at(const TileW<C> &tl, int buf, int lane, int i) {
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -376,7 +383,7 @@ __device__ __forceinline__ bf16x8 vfrag_at(const TileW<C> &tl, int buf, int lane
 }
 
 // O^T += V^T P^T over key blocks KB0 .. KB0+NKB-1 (16 keys each) of the tile, V^T
-// fragments read with ds_read_b64_tr_b16 as in Tile::values (addresses through the
+// fragments read with ds_read_b64_tr_b16 as in vfrag_at (addresses through the
 // swizzle) C::DV ahead of their MFMAs in the ring fr (fragment i in slot i % (DV + 1);
 // with PRE the first DV are already there); P holds packed bf16 pairs.  The caller's
 // work(i) follows the MFMA of (fragment i / QT, query tile i % QT), each group fenced;

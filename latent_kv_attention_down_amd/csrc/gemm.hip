@@ -125,8 +125,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_nt(GemmArgs g) {
 }
 
 template <int BM, int BN, int WTM, int WTN, int KC, int NS, bool OUT_F32, int EP>
+// Up to 256 registers per wave: the fragments of four k-steps are in flight at once.
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64)
-__attribute__((amdgpu_waves_per_eu(WTM * WTN >= 128 * 64 ? 2 : 4, 8)))
+__attribute__((amdgpu_waves_per_eu(2, 8)))
 void k_gemm_dma(GemmArgs g) {
   gemm_dma_tile<BM, BN, WTM, WTN, KC, NS, OUT_F32, EP>(g, blockIdx.y * gridDim.x + blockIdx.x,
                                                        gridDim.x, gridDim.x * gridDim.y, blockIdx.z);

@@ -135,7 +135,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nb
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  bf16x8 af[2][TM], bfr[2][TN];
+  constexpr int NB = KS >= 3 ? KS : 2;  // fragment buffers
+  bf16x8 af[NB][TM], bfr[NB][TN];
   auto frags = [&](int kc, int s, int p) {
     const unsigned char *sa = smem + (size_t)(kc % NS) * D::SB;
     const unsigned char *sb = sa + BM * D::ROWB;
@@ -150,27 +151,65 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nb
       bfr[p][j] = *(const bf16x8 *)(sb + row * D::ROWB + ((2 * s + g8) ^ gswz<KC>(row)) * 16);
     }
   };
-  // Fragments run one k-step ahead.  At a chunk's last k-step the next stage is
-  // awaited first: once every wave has passed that barrier it has read all of the
-  // current stage into registers, so the stage can be refilled (chunk kc + NS).
   arrive(0);
   if (NS - 1 < nk) issue(NS - 1);
-  frags(0, 0, 0);
-  for (int kc = 0; kc < nk; ++kc) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int p = (kc * KS + s) & 1;
-      if (s + 1 < KS) {
-        frags(kc, s + 1, p ^ 1);
-      } else if (kc + 1 < nk) {
-        arrive(kc + 1);
-        if (kc + NS < nk) issue(kc + NS);
-        frags(kc + 1, 0, p ^ 1);
-      }
+  if constexpr (KS >= 3) {
+    // Fragments two k-steps ahead (buffer s for k-step s), each read slotted between
+    // two MFMAs of the step.  Two steps before a chunk ends the next stage is awaited:
+    // by then every wave holds the current stage's last fragments (or has them in
+    // flight, drained by the wait), so the stage can be refilled.  The last chunk is
+    // peeled so that no branch splits the steps.
+    auto step = [&](int s) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[p][i], bfr[p][j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[s][i], bfr[s][j], acc[i][j]);
+#pragma unroll
+      for (int q = 0; q < TM * TN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    frags(0, 0, 0);
+    frags(0, 1, 1);
+    for (int kc = 0; kc + 1 < nk; ++kc) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 2 < KS) {
+          frags(kc, s + 2, s + 2);
+        } else {
+          if (s + 2 == KS) {
+            arrive(kc + 1);
+            if (kc + NS < nk) issue(kc + NS);
+          }
+          frags(kc + 1, s + 2 - KS, s + 2 - KS);
+        }
+        step(s);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 2 < KS) frags(nk - 1, s + 2, s + 2);
+      step(s);
+    }
+  } else {
+    frags(0, 0, 0);
+    for (int kc = 0; kc < nk; ++kc) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int p = (kc * KS + s) & 1;
+        if (s + 1 < KS) {
+          frags(kc, s + 1, p ^ 1);
+        } else if (kc + 1 < nk) {
+          arrive(kc + 1);
+          if (kc + NS < nk) issue(kc + NS);
+          frags(kc + 1, 0, p ^ 1);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[p][i], bfr[p][j], acc[i][j]);
+      }
     }
   }
 

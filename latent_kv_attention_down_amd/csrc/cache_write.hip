@@ -632,7 +632,10 @@ hipError_t query_gemm_cache_write(const GemmArgs &g, const CacheWriteArgs &a, co
       (int64_t)r.n_h * (r.d_c + r.d_rope) != g.N || r.M != g.M)
     return hipErrorInvalidValue;
   const int nbx = (g.N + 255) / 256, tiles = nbx * ((g.M + 255) / 256);
-  const size_t lds = QueryTile::LDS > CwDma<224, kBMQ>::LDS ? QueryTile::LDS : CwDma<224, kBMQ>::LDS;
+  // the GEMM tile with its rotation table, or the write's tile
+  constexpr size_t lds_g = QueryTile::LDS + RopeLds<256>::BYTES;
+  static_assert(lds_g <= 163840, "LDS");
+  const size_t lds = lds_g > CwDma<224, kBMQ>::LDS ? lds_g : CwDma<224, kBMQ>::LDS;
   hipError_t e = hipFuncSetAttribute((const void *)k_query_gemm_cache_write<224>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -174,9 +174,14 @@ hipError_t gemm_dma(const GemmArgs &g, bool out_f32, hipStream_t st) {
   // 128x128 tiles with two 64-wide stages (64 KB of LDS, 68 KB with an fp32 output
   // tile) leave room for a second workgroup on the CU: the per-head W^V_up GEMM
   // (K = 192, three k chunks, 444 tiles) then runs in one round, 9.4 us against
-  // 13.4 us with four stages, and W^Q_down is no slower (20.8 against 21.6 us).
-  if (g.N % 128 == 0 && mt128 * (g.N / 128) * g.batch >= 200)
+  // 13.4 us with four stages.  Where the tiles fit on the CUs in one round anyway
+  // (W^Q_down of the 3-frame chunk: 222 tiles) a third stage keeps two in flight:
+  // 19.1 against 21.0 us.
+  const int64_t t128 = mt128 * (g.N / 128) * g.batch;
+  if (g.N % 128 == 0 && t128 >= 200) {
+    if (KC == 64 && t128 <= 256) return launch_dma<128, 128, 64, 64, KC, 3>(g, out_f32, st);
     return launch_dma<128, 128, 64, 64, KC, KC == 64 ? 2 : 4>(g, out_f32, st);
+  }
   return launch_dma<128, 64, 64, 32, KC, 4>(g, out_f32, st);
 }
 
@@ -267,11 +272,13 @@ bool query_gemm_rope_applies(const GemmArgs &g, const RopeQArgs &r) {
 hipError_t query_gemm_rope(const GemmArgs &g, const RopeQArgs &r, hipStream_t st) {
   if (!query_gemm_rope_applies(g, r)) return hipErrorInvalidValue;
   using D = GemmDma<256, 256, 128, 64, 64, 2, false, EP_ROW_RMS>;
+  constexpr size_t lds = D::LDS + RopeLds<256>::BYTES;  // the tile, then its rotation table
+  static_assert(lds <= 163840, "LDS");
   hipError_t e = hipFuncSetAttribute((const void *)k_query_gemm_rope,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)D::LDS);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_query_gemm_rope, dim3((g.N + 255) / 256, (g.M + 255) / 256), dim3(D::NT),
-                     D::LDS, st, g, r);
+                     lds, st, g, r);
   return hipGetLastError();
 }
 

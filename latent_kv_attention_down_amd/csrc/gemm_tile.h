@@ -40,6 +40,55 @@ struct GemmDma {
 template <int KC>
 __device__ __forceinline__ int gswz(int row) { return (row >> 1) & (KC / 8 - 1); }
 
+// LDS a rotating tile keeps past its own: the cos and sin of every rope pair at each
+// position its axis takes in the chunk (frame within the chunk, row and column of the
+// token grid; pair p's run starts at entry p * S, S the longest of the three spans),
+// the axis of each pair, and each tile row's three axis positions.  A tile whose
+// pairs would need more entries rotates without it.
+template <int BM>
+struct RopeLds {
+  static constexpr int ENTRIES = 2048, MAX_PAIRS = 64;
+  static constexpr size_t AX = (size_t)ENTRIES * 8, ROWS = AX + MAX_PAIRS * 4;
+  static constexpr size_t BYTES = (ROWS + (size_t)BM * 3 * 4 + 15) / 16 * 16;
+};
+
+// Fills the table at `base` for the tile rows m0 .. m0 + BM - 1 (rows past M take
+// row M - 1's positions) and returns S, or 0 (nothing written) when it does not fit.
+// Each entry is what rope_sincos gives for that pair and position, as in the separate
+// RoPE pass.  A wave takes whole pairs, so that a pair's axis and frequency are
+// wave-uniform scalar reads of the kernel arguments.
+template <int BM, int NT>
+__device__ __forceinline__ int rope_lds_build(const RopeQArgs &r, unsigned char *base, int m0,
+                                              int M) {
+  using T = RopeLds<BM>;
+  const int np = r.d_rope / 2;
+  const int n_t = (r.T_q + r.tpf - 1) / r.tpf, n_y = (r.tpf + r.grid_w - 1) / r.grid_w,
+            n_x = r.grid_w;
+  const int S = max(n_t, max(n_y, n_x));
+  if (np > T::MAX_PAIRS || np * S > T::ENTRIES) return 0;
+  float2 *ct = (float2 *)base;
+  int *ax = (int *)(base + T::AX), *rp = (int *)(base + T::ROWS);
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int p = __builtin_amdgcn_readfirstlane(tid >> 6); p < np; p += NT / 64) {
+    const int a = r.rope.axis[p], n = a == 0 ? n_t : a == 1 ? n_y : n_x;
+    const double om = r.rope.omega[p];
+    for (int idx = lane; idx < n; idx += 64) {
+      const double pos = a == 0 ? (double)(r.t0 + idx) : (double)idx;
+      float s, c;
+      rope_sincos(pos, om, s, c);
+      ct[p * S + idx] = make_float2(c, s);
+    }
+    if (lane == 0) ax[p] = a;
+  }
+  for (int rr = tid; rr < BM; rr += NT) {
+    const int m = min(m0 + rr, M - 1), i = m % r.T_q, nn = i % r.tpf;
+    rp[3 * rr] = i / r.tpf;
+    rp[3 * rr + 1] = nn / r.grid_w;
+    rp[3 * rr + 2] = nn % r.grid_w;
+  }
+  return S;
+}
+
 // One output tile; lin is the workgroup's linear index among the total tiles of the
 // launch (nbx tiles across N), b its batch.  With ROPE (the absorbed query GEMM, bf16
 // output), the tile's columns that are a head's rope columns of q_lat (column n is
@@ -111,6 +160,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nb
       for (int p = 0; p < g.ssq_parts; ++p) ss += g.ssq_in[(int64_t)p * g.M + row];
       xs[r] = 1.0f / sqrtf(ss * g.ssq_scale + g.ssq_eps);
     }
+  // A rotating tile's cos and sin table, built in the same shadow (LDS past D::LDS).
+  int tab = 0;
+  if constexpr (ROPE) tab = rope_lds_build<BM, D::NT>(*rq, smem + D::LDS, m0, g.M);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -133,7 +185,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nb
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPW) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
+    // a bare barrier: __syncthreads would also wait for the later stages' loads
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
   constexpr int NB = KS >= 3 ? KS : 2;  // fragment buffers
   bf16x8 af[NB][TM], bfr[NB][TN];
@@ -266,17 +320,32 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, int lin, int nb
       }
       if (m >= g.M) continue;
       const int p0 = ((n0 + c8) % dk - rq->d_c) / 2;  // four pairs from here
-      const int i = m % rq->T_q, nn = i % rq->tpf;
-      const double pos[3] = {(double)(rq->t0 + i / rq->tpf), (double)(nn / rq->grid_w),
-                             (double)(nn % rq->grid_w)};
       bf16x8 *t = (bf16x8 *)((bf16 *)tile + r * LDC + c8);
       bf16x8 v = *t;
+      if (tab) {
+        using T = RopeLds<BM>;
+        const float2 *ct = (const float2 *)(smem + D::LDS);
+        const int *ax = (const int *)(smem + D::LDS + T::AX);
+        const int *rp = (const int *)(smem + D::LDS + T::ROWS) + 3 * r;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float re = to_f32(v[2 * q]), im = to_f32(v[2 * q + 1]);
-        rope_rotate(re, im, pos[rq->rope.axis[p0 + q]], rq->rope.omega[p0 + q]);
-        v[2 * q] = (bf16)re;
-        v[2 * q + 1] = (bf16)im;
+        for (int q = 0; q < 4; ++q) {
+          float re = to_f32(v[2 * q]), im = to_f32(v[2 * q + 1]);
+          const float2 cs = ct[(p0 + q) * tab + rp[ax[p0 + q]]];
+          rotate_by(re, im, cs.y, cs.x);
+          v[2 * q] = (bf16)re;
+          v[2 * q + 1] = (bf16)im;
+        }
+      } else {
+        const int i = m % rq->T_q, nn = i % rq->tpf;
+        const double pos[3] = {(double)(rq->t0 + i / rq->tpf), (double)(nn / rq->grid_w),
+                               (double)(nn % rq->grid_w)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float re = to_f32(v[2 * q]), im = to_f32(v[2 * q + 1]);
+          rope_rotate(re, im, pos[rq->rope.axis[p0 + q]], rq->rope.omega[p0 + q]);
+          v[2 * q] = (bf16)re;
+          v[2 * q + 1] = (bf16)im;
+        }
       }
       *t = v;
     }

@@ -120,3 +120,28 @@ def test_absorbed_and_two_stage_steps_agree():
     y1 = run.L.step(ch, x)
     torch.cuda.synchronize()
     assert_close(to_host(y1)[0], to_host(y2)[0], TOL["bf16"], "absorbed vs two-stage")
+
+
+@pytest.mark.parametrize("grid", [(30, 52), (1, 1560)])
+def test_absorbed_query_full_size_sampled(grid):
+    """Full Wan-1.3B size with the absorbed query (App. E Eq. 8-9): y of mla_step (the
+    query GEMM rotates its RoPE columns in its tiles and shares its launch with the
+    cache write) and out_heads of mla_chunk_attention (the query GEMM alone), sampled
+    query tokens against the oracle.  On the 30 x 52 grid the tiles take the RoPE cos/sin
+    from a per-tile table; on a 1 x 1560 grid a pair spans more positions than that table
+    holds, so the tiles rotate position by position."""
+    s = W.shape_by_name("wan1.3b-w21").with_(grid_h=grid[0], grid_w=grid[1])
+    run = query_absorbed(Run(s))
+    rows = sample_rows(s)
+    full_step(run, check_cache=False, sample=rows)
+    out = run.L.chunk_attention(run.chunk(), run.chunk_tokens())
+    torch.cuda.synchronize()
+    ref = run.oracle(query_rows=rows)
+    assert_close(to_host(out)[0][rows], ref["out"], TOL["bf16"], "out_heads")
+
+
+def test_absorbed_query_two_requests_full_size_sampled():
+    """Two requests at full Wan-1.3B size with the absorbed query: the query GEMM (407
+    tiles) runs alone, rotating its RoPE columns in its tiles, before the cache write."""
+    s = W.shape_by_name("wan1.3b-w21")
+    full_step(query_absorbed(Run(s, batch=2)), check_cache=False, sample=sample_rows(s))

@@ -422,3 +422,4 @@ def test_latent_width_variants_full_size_sampled(name):
     """The (d_c, d_rope) variants at full Wan-1.3B size, in the launch the sweep times
     (d_c = 256 runs the attention kernel with 32 query rows per wave)."""
     sampled_full(W.shape_by_name(name))
+

@@ -122,15 +122,19 @@ def test_absorbed_and_two_stage_steps_agree():
     assert_close(to_host(y1)[0], to_host(y2)[0], TOL["bf16"], "absorbed vs two-stage")
 
 
-@pytest.mark.parametrize("grid", [(30, 52), (1, 1560)])
-def test_absorbed_query_full_size_sampled(grid):
+@pytest.mark.parametrize("grid,t0", [((30, 52), None), ((1, 1560), None),
+                                     ((30, 52), 3_000_000_018)])
+def test_absorbed_query_full_size_sampled(grid, t0):
     """Full Wan-1.3B size with the absorbed query (App. E Eq. 8-9): y of mla_step (the
     query GEMM rotates its RoPE columns in its tiles and shares its launch with the
     cache write) and out_heads of mla_chunk_attention (the query GEMM alone), sampled
     query tokens against the oracle.  On the 30 x 52 grid the tiles take the RoPE cos/sin
     from a per-tile table; on a 1 x 1560 grid a pair spans more positions than that table
-    holds, so the tiles rotate position by position."""
+    holds, so the tiles rotate position by position.  At frame 3e9 the table's angles
+    (frame index times frequency, reduced in fp64) are checked far past fp32 and 2^31."""
     s = W.shape_by_name("wan1.3b-w21").with_(grid_h=grid[0], grid_w=grid[1])
+    if t0 is not None:
+        s = s.with_(t0=t0)
     run = query_absorbed(Run(s))
     rows = sample_rows(s)
     full_step(run, check_cache=False, sample=rows)

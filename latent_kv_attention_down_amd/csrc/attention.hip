@@ -64,8 +64,11 @@ constexpr int kBufferConfig = 0x00020000;
 // (one block, all R rows, without a causal mask); block k attends the first
 // min(nk0 + (k+1) blk_keys, nk) keys.  Each block is cut into blk_rt row tiles of
 // RW rows (its last tile may be partial), and row tile rt has one step per key
-// tile it attends.  Steps are numbered request by request, block by block, row
-// tile by row tile: T in all, Tb per request.
+// tile it attends, after ov steps that stand for its fixed cost (query load, first
+// tile, output and record stores) and hold no key tile: the flat split then gives
+// every workgroup the same time, not the same number of key tiles, where row tiles
+// differ in length (causal blocks).  Steps are numbered request by request, block by
+// block, row tile by row tile: T in all, Tb per request.
 struct Sched {
   int B, R, RTb, RT;
   int nk, KT;
@@ -75,6 +78,7 @@ struct Sched {
   int G;
   int RW;
   int nblk, blk_rows, blk_rt, blk_keys, nk0;
+  int ov;
   float sum_limit;  // row sums above it flag the row tile (at most kFastSumLimit)
 };
 
@@ -92,7 +96,7 @@ __host__ __device__ __forceinline__ int blk_kt(const Sched &s, int k) {
 }
 
 // One row tile: its request, rows [row0, row_end), keys attended, key tiles and
-// the number of its first step.
+// the number of the step of its first key tile (its ov cost steps come before).
 struct RowTile {
   int b, row0, row_end, nk, KT;
   int64_t f0;
@@ -103,27 +107,36 @@ __host__ __device__ __forceinline__ RowTile row_tile(const Sched &s, int rt) {
   t.b = rt / s.RTb;
   const int j = rt - t.b * s.RTb, k = j / s.blk_rt, i = j - k * s.blk_rt;
   int64_t f = (int64_t)t.b * s.Tb;
-  for (int q = 0; q < k; ++q) f += (int64_t)s.blk_rt * blk_kt(s, q);
+  for (int q = 0; q < k; ++q) f += (int64_t)s.blk_rt * (blk_kt(s, q) + s.ov);
   t.nk = blk_nk(s, k);
   t.KT = (t.nk + BN - 1) / BN;
-  t.f0 = f + (int64_t)i * t.KT;
+  t.f0 = f + (int64_t)i * (t.KT + s.ov) + s.ov;
   t.row0 = k * s.blk_rows + i * s.RW;
   const int lim = min((k + 1) * s.blk_rows, s.R);
   t.row_end = min(t.row0 + s.RW, lim);
   return t;
 }
 
-// The row tile that step f belongs to.
+// The row tile that step f belongs to (one of its cost steps or a key tile).
 __host__ __device__ __forceinline__ int rt_of(const Sched &s, int64_t f) {
   const int b = (int)(f / s.Tb);
   int64_t r = f - (int64_t)b * s.Tb;
   int k = 0;
   for (; k + 1 < s.nblk; ++k) {
-    const int64_t wk = (int64_t)s.blk_rt * blk_kt(s, k);
+    const int64_t wk = (int64_t)s.blk_rt * (blk_kt(s, k) + s.ov);
     if (r < wk) break;
     r -= wk;
   }
-  return b * s.RTb + k * s.blk_rt + (int)(r / blk_kt(s, k));
+  return b * s.RTb + k * s.blk_rt + (int)(r / (blk_kt(s, k) + s.ov));
+}
+
+// The key tiles [kt0, kt1) of row tile t that the steps [begin, end) hold (empty
+// where they hold only its cost steps).
+__host__ __device__ __forceinline__ void piece_of(const RowTile &t, int64_t begin, int64_t end,
+                                                  int &kt0, int &kt1) {
+  const int64_t a = begin - t.f0, e = end - t.f0;
+  kt0 = (int)(a < 0 ? 0 : a > t.KT ? t.KT : a);
+  kt1 = (int)(e < 0 ? 0 : e > t.KT ? t.KT : e);
 }
 
 // One wave per SIMD, QT x 32 query rows per wave, key tiles brought into an unpadded
@@ -616,8 +629,9 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
   const int rt_first = rt_of(s, begin), rt_last = rt_of(s, end - 1);
   for (int rt = rt_last; rt >= rt_first; --rt) {
     const RowTile t = row_tile(s, rt);
-    const int kt0 = (int)((begin > t.f0 ? begin : t.f0) - t.f0);
-    const int kt1 = (int)((end < t.f0 + t.KT ? end : t.f0 + t.KT) - t.f0);
+    int kt0, kt1;
+    piece_of(t, begin, end, kt0, kt1);
+    if (kt0 >= kt1) continue;  // only cost steps of this row tile fall in the range
     const int last_kt = t.KT - 1, nk = t.nk;
     const int b = t.b, row0 = t.row0;
     tl.nk = nk;
@@ -777,8 +791,8 @@ void k_latent_attn_w1(const bf16 *__restrict__ q, const bf16 *__restrict__ cache
       int rt2 = rt;
       asm volatile("" : "+s"(rt2));
       const RowTile t2 = row_tile(s, rt2);
-      const int k0 = (int)((begin > t2.f0 ? begin : t2.f0) - t2.f0);
-      const int k1 = (int)((end < t2.f0 + t2.KT ? end : t2.f0 + t2.KT) - t2.f0);
+      int k0, k1;
+      piece_of(t2, begin, end, k0, k1);
       tl.nk = t2.nk;
       tl.cb = cache + (int64_t)t2.b * s.cache_rows * C::DK;
       const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc(
@@ -845,7 +859,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(bf16 *__restrict__ o,
   }
   const RowTile t = row_tile(s, rt);
   if (by_boundary) {
-    if ((int64_t)unit * s.T / s.G == t.f0 || wg_of(s, t.f0) != g0) return;
+    // a boundary among the row tile's key tiles, the first one (the workgroup before
+    // it took the first key tile)
+    if ((int64_t)unit * s.T / s.G <= t.f0 || wg_of(s, t.f0) != g0) return;
   } else {
     g0 = wg_of(s, t.f0);
   }
@@ -1144,8 +1160,15 @@ __global__ __launch_bounds__(256) void k_latent_attn_f32(const float *__restrict
   }
 }
 
-Sched make_sched(const AttnArgs &a, int rows_per_wg, int grid) {
+// Cost steps per row tile in the bf16 kernel's split where row tiles differ in length
+// (causal blocks): a row tile's fixed cost (query load, first tile and its maximum,
+// output and record stores) is about six key tiles' time.  Without blocks every row
+// tile has the same length and the split counts key tiles only.
+constexpr int kRowTileCostSteps = 6;
+
+Sched make_sched(const AttnArgs &a, int rows_per_wg, int grid, int ov = 0) {
   Sched s;
+  s.ov = ov;
   s.B = a.B;
   s.R = a.R;
   s.RW = rows_per_wg;
@@ -1169,7 +1192,7 @@ Sched make_sched(const AttnArgs &a, int rows_per_wg, int grid) {
   s.RTb = s.nblk * s.blk_rt;
   s.RT = s.B * s.RTb;
   s.Tb = 0;
-  for (int k = 0; k < s.nblk; ++k) s.Tb += (int64_t)s.blk_rt * blk_kt(s, k);
+  for (int k = 0; k < s.nblk; ++k) s.Tb += (int64_t)s.blk_rt * (blk_kt(s, k) + s.ov);
   s.T = (int64_t)s.B * s.Tb;
   s.G = (int)((int64_t)grid < s.T ? (int64_t)grid : s.T);
   if (s.G < 1) s.G = 1;
@@ -1187,7 +1210,7 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 template <int DC, int DR>
 hipError_t launch(const AttnArgs &a, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   using F = typename Choice<DC, DR>::Fast;
-  Sched s = make_sched(a, F::RW, a.grid * F::WPC);
+  Sched s = make_sched(a, F::RW, a.grid * F::WPC, a.nblk > 1 ? kRowTileCostSteps : 0);
   if (s.T <= 0) return hipSuccess;
   auto fast = k_latent_attn_w1<F>;
   if constexpr (F::ASM_SCORES) {
@@ -1241,7 +1264,7 @@ bool latent_attention_bf16_supported(int dc, int dr) {
 AttnCounts latent_attention_counts(const AttnArgs &a) {
   const AttnLayout al = latent_attention_layout(a.DC, a.DR);
   if (al.rows_per_wg <= 0) return AttnCounts{0, 0};
-  const Sched s = make_sched(a, al.rows_per_wg, 1);
+  const Sched s = make_sched(a, al.rows_per_wg, 1, a.nblk > 1 ? kRowTileCostSteps : 0);
   return AttnCounts{s.RT, s.T};
 }
 

@@ -40,10 +40,13 @@
 //    is at most 2^64, far inside fp32 and bf16 range;
 //  * the fast grid is persistent: workgroup g takes the flat range
 //    [gT/G, (g+1)T/G) of T = (row tiles) x (key tiles) tile steps, so every CU gets
-//    the same work.  A row tile finished by one workgroup is written directly; one
-//    split across workgroups leaves normalised bf16 partials plus (m, l) per row,
-//    merged in a fixed order (deterministic, no atomics): by k_attn_merge, or by
-//    k_merge_vup while it loads the rows for the per-head value up-projection.
+//    the same work (with causal blocks, whose row tiles differ in length, each row
+//    tile also counts a few steps for its fixed cost, so that a workgroup on many
+//    short row tiles gets fewer key tiles).  A row tile finished by one workgroup is
+//    written directly; one split across workgroups leaves normalised bf16 partials
+//    plus (m, l) per row, merged in a fixed order (deterministic, no atomics): by
+//    k_attn_merge, or by k_merge_vup while it loads the rows for the per-head value
+//    up-projection.
 #include <type_traits>
 
 #include "mla_device.h"
